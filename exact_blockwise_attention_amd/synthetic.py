@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs and the workload table.
+
+This module is shared by the GPU path's tests/bench and by the CPU oracle's
+tests. It holds no attention arithmetic: it draws i.i.d. N(0, 1) float32
+samples from a counter-free, seeded numpy generator, rounds them to bfloat16
+bit patterns when a workload is bf16, and widens bit patterns back to floats
+so that both sides see exactly the same values.
+
+Seeding: ``numpy.random.Generator(PCG64(SeedSequence([workload_id,
+tensor_id])))`` with tensor ids Q=0, K=1, V=2, dO=3; values are drawn with
+``standard_normal(dtype=float32)`` in the [B, L, H, d] (original token order)
+layout.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention problem: shapes, ring size, layout and precision.
+
+    ``ring_size`` P splits the sequence of ``seq_len`` tokens into P equal
+    blocks of ``block_len`` tokens (the ring of P devices). ``q_ranks`` is the
+    half-open range of ranks whose query blocks are computed: the whole ring
+    for the whole-sequence workloads, a single rank for one device's share.
+    """
+
+    wid: int
+    name: str
+    batch: int
+    heads: int
+    seq_len: int
+    head_dim: int
+    ring_size: int
+    causal: bool
+    layouts: tuple
+    dtype: str  # "f32" or "bf16"
+    passes: tuple  # ("fwd",) or ("fwd", "bwd")
+    q_ranks: tuple | None = None  # None: all ranks
+    prefetch: bool = False
+
+    @property
+    def block_len(self) -> int:
+        return self.seq_len // self.ring_size
+
+
+# The five workloads: a tiny fp32 correctness case, a non-causal bf16 forward,
+# a causal forward in both layouts, one device's share of a 262,144-token
+# 7B-shaped layer (H=32, d=128) with a prefetched side-stream KV receive, and
+# a causal striped forward+backward at 32,768 tokens.
+WORKLOADS = {
+    1: Workload(1, "noncausal_f32_L1024_d64_P4", 1, 1, 1024, 64, 4, False,
+                ("contiguous",), "f32", ("fwd",)),
+    2: Workload(2, "noncausal_bf16_H8_L16384_d128_P8", 1, 8, 16384, 128, 8,
+                False, ("contiguous",), "bf16", ("fwd",)),
+    3: Workload(3, "causal_bf16_H32_L65536_d128_P16", 1, 32, 65536, 128, 16,
+                True, ("contiguous", "striped"), "bf16", ("fwd",)),
+    4: Workload(4, "share_causal_striped_bf16_H32_L262144_d128_P8_rank7", 1, 32,
+                262144, 128, 8, True, ("striped",), "bf16", ("fwd",),
+                q_ranks=(7, 8), prefetch=True),
+    5: Workload(5, "causal_striped_bf16_H32_L32768_d128_P8_fwdbwd", 1, 32,
+                32768, 128, 8, True, ("striped",), "bf16", ("fwd", "bwd")),
+}
+
+
+def rng_for(workload_id: int, tensor_id: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload_id, tensor_id])))
+
+
+def normal_f32(workload_id: int, tensor: str, shape) -> np.ndarray:
+    """i.i.d. N(0,1) float32 array of ``shape`` for (workload, tensor)."""
+    g = rng_for(workload_id, TENSOR_IDS[tensor])
+    return g.standard_normal(size=tuple(shape), dtype=np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even) -> uint16 bits.
+
+    NaN inputs map to a quiet NaN; the synthetic data never holds one.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    out = rounded.astype(np.uint16)
+    out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def make_tensor(workload_id: int, tensor: str, shape, dtype: str):
+    """Return (device_payload, exact_f64) for one input tensor.
+
+    ``device_payload`` is a float32 array (dtype "f32") or the uint16 bf16 bit
+    pattern array (dtype "bf16"); ``exact_f64`` is the same values widened to
+    float64, for the oracle.
+    """
+    x = normal_f32(workload_id, tensor, shape)
+    if dtype == "f32":
+        return x, x.astype(np.float64)
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return bits, bf16_bits_to_f32(bits).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def workload_shape(w: Workload):
+    return (w.batch, w.seq_len, w.heads, w.head_dim)
