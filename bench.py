@@ -1,0 +1,267 @@
+"""Benchmark: causal striped blockwise ring attention, forward + backward, d=128.
+
+Default workload (one GPU): B=1, H=32, L=32768, d=128, bf16, ring of P=8
+blocks of 4096 tokens, causal, striped layout. One step = the forward over
+all 8 ranks (every KV block visited in ring order, O and lse out) followed by
+the backward (D = rowsum(dO*O), the ring walk recomputing P from lse with
+dV/dP/dS/dQ/dK, dQ cast). Inputs are seeded synthetic N(0,1) tensors already
+resident in HBM. Throughput is algorithmic: 4*d flop per visible
+(query, key) pair forward and 10*d backward (masked pairs not counted).
+
+Prints one JSON line. --workload picks one of the other workloads (for
+profiling); the default is the forward+backward one.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["exact_blockwise_attention_amd/csrc/" + f for f in
+                  ("ra_fwd.hip", "ra_bwd.hip", "ra_misc.hip", "ra_api.cpp", "ra_schedule.h", "ra_internal.h")]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--layout", default=None, help="workload 3: contiguous or striped")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def pair_count(layout, causal, P, Bb, ranks):
+    """Visible (query, key) pairs of the given ranks' query blocks, per head:
+    a striped block pair (i, j) sees b <= a - [j > i], a contiguous one all
+    (j < i), the lower triangle (j == i) or nothing (j > i)."""
+    total = 0
+    for i in ranks:
+        for kstep in range(P):
+            j = (i - kstep) % P
+            if not causal:
+                total += Bb * Bb
+            elif layout == "striped":
+                total += Bb * (Bb + 1) // 2 if j <= i else Bb * (Bb - 1) // 2
+            elif j < i:
+                total += Bb * Bb
+            elif j == i:
+                total += Bb * (Bb + 1) // 2
+    return total
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w):
+    """Oracle (float64 numpy) on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    from exact_blockwise_attention_amd import synthetic as syn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count() or 1
+    d = w.head_dim
+    if 5 == w.wid:
+        # heads 0 and H-1 of the full 32768-token sequence (the workload's own
+        # tensors), forward + backward; about 10 s on 16 host cores
+        heads = [0, w.heads - 1]
+        shape = syn.workload_shape(w)
+        t = {}
+        for n in ("q", "k", "v", "do"):
+            pay = syn.make_payload(w.wid, n, shape, w.dtype)
+            t[n] = syn.to_f64(np.ascontiguousarray(pay[:, :, heads]))
+            del pay
+        L = w.seq_len
+        t0 = time.perf_counter()
+        oracle.attention_bwd(t["q"], t["k"], t["v"], t["do"], True)  # runs the forward inside
+        dt = time.perf_counter() - t0
+        flops = len(heads) * L * (L + 1) // 2 * (4 + 10) * d
+        sample = f"heads 0 and {w.heads - 1} of {w.heads}, all {L} tokens, forward+backward (causal, " \
+                 "contiguous order: the oracle's mask is on token positions, so the layout does not change it)"
+    else:
+        Ls = 4096 if w.causal else 2048
+        shape = (1, Ls, 1, d)
+        t = {n: syn.to_f64(syn.make_payload(w.wid, n, shape, w.dtype)) for n in ("q", "k", "v")}
+        t0 = time.perf_counter()
+        oracle.attention_fwd(t["q"], t["k"], t["v"], w.causal)
+        dt = time.perf_counter() - t0
+        pairs = Ls * (Ls + 1) // 2 if w.causal else Ls * Ls
+        flops = pairs * 4 * d
+        sample = f"one head, first {Ls} tokens, forward"
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not part of "
+              "this build", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import exact_blockwise_attention_amd as ra
+    from exact_blockwise_attention_amd import synthetic as syn
+
+    ra.library()
+    w = syn.WORKLOADS[args.workload]
+    layout = args.layout or w.layouts[-1]
+    P, Bb, d = w.ring_size, w.block_len, w.head_dim
+    ranks = list(range(*w.q_ranks)) if w.q_ranks else list(range(P))
+    rb, re_ = ranks[0], ranks[-1] + 1
+    shape = syn.workload_shape(w)
+    names = ("q", "k", "v", "do") if "bwd" in w.passes else ("q", "k", "v")
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(x).to("cuda")
+
+    t = {}
+    for n in names:
+        pay = syn.make_payload(w.wid, n, shape, w.dtype)
+        if n == "q" and w.q_ranks:
+            # one device's share: only its query block is resident, in local row order
+            x = np.arange(Bb)
+            pos = x * P + rb if layout == "striped" else rb * Bb + x
+            pay = np.ascontiguousarray(pay[:, pos])
+        t[n] = dev(pay)
+        del pay
+    torch.cuda.synchronize()
+
+    code = ra.BF16 if w.dtype == "bf16" else ra.F32
+    pb = ra.make_problem(w.batch, w.heads, d, P, Bb, layout, w.causal, code)
+    stream = torch.cuda.current_stream()
+    sh = ra._stream_handle(stream)
+    copy_stream = torch.cuda.Stream() if w.prefetch else None
+    ch = ra._stream_handle(copy_stream) if copy_stream is not None else None
+    if w.q_ranks:
+        so = lambda x: ra._seq_rank_rows(x, re_ - rb, layout, P)  # noqa: E731
+    else:
+        so = lambda x: ra.seq_original(x, P, layout, block_offset=rb)  # noqa: E731
+    sk = lambda x: ra.seq_original(x, P, layout)  # noqa: E731
+    o = torch.empty_like(t["q"])
+    nr = re_ - rb
+    lse = torch.empty((nr, w.batch, w.heads, Bb), dtype=torch.float32, device="cuda")
+    fws = ra.workspace_bytes(pb, rb, re_, w.prefetch, False)
+    fwd_ws = torch.empty(max(fws, 256), dtype=torch.uint8, device="cuda")
+    bwd = "bwd" in w.passes
+    if bwd:
+        dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+        bws = ra.workspace_bytes(pb, rb, re_, False, True)
+        bwd_ws = torch.empty(bws, dtype=torch.uint8, device="cuda")
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(timing=None):
+        if timing is not None:
+            timing["f0"].append(ev())
+            timing["f0"][-1].record(stream)
+        ra.forward_raw(pb, rb, re_, so(t["q"]), sk(t["k"]), sk(t["v"]), so(o), lse.data_ptr(),
+                       fwd_ws.data_ptr() if fws else None, fws, sh, ch)
+        if timing is not None:
+            timing["f1"].append(ev())
+            timing["f1"][-1].record(stream)
+        if bwd:
+            args_ = (pb, rb, re_, so(t["q"]), sk(t["k"]), sk(t["v"]), so(o), so(t["do"]), lse.data_ptr(), so(dq),
+                     sk(dk), sk(dv), bwd_ws.data_ptr(), bws, sh)
+            ra.backward_stage_raw(0, *args_)
+            if timing is not None:
+                timing["b0"].append(ev())
+                timing["b0"][-1].record(stream)
+            ra.backward_stage_raw(1, *args_)
+            if timing is not None:
+                timing["b1"].append(ev())
+                timing["b1"][-1].record(stream)
+            ra.backward_stage_raw(2, *args_)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timing = {"f0": [], "f1": [], "b0": [], "b1": []}
+    start, stop = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step(timing)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+
+    pairs = pair_count(layout, w.causal, P, Bb, ranks) * w.batch * w.heads
+    fwd_flops = 4 * d * pairs
+    bwd_flops = 10 * d * pairs if bwd else 0
+    fwd_ms = sum(a.elapsed_time(b) for a, b in zip(timing["f0"], timing["f1"])) / args.steps
+    details = {"pairs": pairs, "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_flops / fwd_ms / 1e9, 2)}
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    if bwd:
+        bwd_main_ms = sum(a.elapsed_time(b) for a, b in zip(timing["b0"], timing["b1"])) / args.steps
+        details.update({"bwd_main_ms": round(bwd_main_ms, 4), "bwd_main_tflops": round(bwd_flops / bwd_main_ms / 1e9, 2),
+                        "bwd_other_ms": round(ms - fwd_ms - bwd_main_ms, 4)})
+        dom_ms, dom_flops, tag = bwd_main_ms, bwd_flops, "bwd_bf16_kernel"
+    else:
+        dom_ms, dom_flops, tag = fwd_ms, fwd_flops, "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel"
+    achieved = dom_flops / dom_ms / 1e9
+    value = (fwd_flops + bwd_flops) / ms / 1e9
+    roof = {"bound": "mfma", "kernel": tag, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": read_traffic(tag), "launch_ms": round(dom_ms, 4)}
+    if w.prefetch:
+        roof["note"] = "one call of 8 step launches plus the side-stream copies, timed as a whole"
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    out = {
+        "metric": "attention TFLOP/s fwd+bwd (causal striped, d=128) and % of bf16 MFMA peak" if bwd else
+                  f"attention forward TFLOP/s ({w.name})",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "head_dim": d,
+                   "ring_size": P, "block_len": Bb, "layout": layout, "causal": w.causal,
+                   "ranks": [rb, re_], "passes": list(w.passes), "prefetch": w.prefetch},
+        "frac_of_peak": round(value / peak, 4),
+        "roofline": roof, "cpu_baseline": cpu, "details": details,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

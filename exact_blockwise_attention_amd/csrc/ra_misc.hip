@@ -1,0 +1,209 @@
+// ra_misc.hip — memory-bound kernels: log-sum-exp merge of partial results,
+// the KV block receive copy, layout gathers, and the backward's row sums and
+// dQ finalisation.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ra_internal.h"
+#include "ra_schedule.h"
+
+namespace ra {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One wave per row: every lane reads the row's two lse values before lane 0
+// writes the merged one, so lse_out may alias an input (a wave executes in
+// lockstep). Merge rule ("Ring Attention 論文分析" (blog), section "ブロック
+// 単位の分割戦略", the online-softmax correction in log-sum-exp form):
+// lse = M + ln(e^(la-M) + e^(lb-M)), O = e^(la-lse) Oa + e^(lb-lse) Ob.
+__global__ __launch_bounds__(256) void merge_lse_kernel(int64_t rows, int32_t d, const float* oa,
+                                                        const float* la, const float* ob,
+                                                        const float* lb, float* oo, float* lo) {
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  if (row >= rows) return;
+  const float xa = la[row], xb = lb[row];
+  const float m = fmaxf(xa, xb);
+  const float ms = (m == -INFINITY) ? 0.0f : m;
+  const float wa = expf(xa - ms), wb = expf(xb - ms);
+  const float tot = wa + wb;
+  const float ca = (tot > 0.0f) ? wa / tot : 0.0f;
+  const float cb = (tot > 0.0f) ? wb / tot : 0.0f;
+  const int64_t base = row * d;
+  if ((d & 3) == 0) {
+    for (int e = 4 * lane; e < d; e += 256) {
+      const float4 u = *reinterpret_cast<const float4*>(oa + base + e);
+      const float4 w = *reinterpret_cast<const float4*>(ob + base + e);
+      float4 r;
+      r.x = ca * u.x + cb * w.x;
+      r.y = ca * u.y + cb * w.y;
+      r.z = ca * u.z + cb * w.z;
+      r.w = ca * u.w + cb * w.w;
+      *reinterpret_cast<float4*>(oo + base + e) = r;
+    }
+  } else {
+    for (int e = lane; e < d; e += 64) oo[base + e] = ca * oa[base + e] + cb * ob[base + e];
+  }
+  if (lane == 0) lo[row] = (tot > 0.0f) ? ms + logf(tot) : -INFINITY;
+}
+
+// Copies 16-byte chunks of one ring block of a strided sequence tensor into
+// a dense [B][Bb][H][D] buffer (the stand-in for a ring receive).
+__global__ __launch_bounds__(256) void gather_block_kernel(const char* src, int64_t s_blk,
+                                                           int64_t s_batch, int64_t s_tok,
+                                                           int64_t s_head, int32_t blk, char* dst,
+                                                           int32_t B, int32_t H, int64_t Bb,
+                                                           int32_t chunks, int32_t es) {
+  const int64_t total = (int64_t)B * Bb * H * chunks;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t c = (int32_t)(idx % chunks);
+    int64_t r = idx / chunks;
+    const int32_t h = (int32_t)(r % H);
+    r /= H;
+    const int64_t x = r % Bb;
+    const int32_t b = (int32_t)(r / Bb);
+    const int64_t off = ((int64_t)blk * s_blk + (int64_t)b * s_batch + x * s_tok + (int64_t)h * s_head) * es;
+    *reinterpret_cast<u32x4*>(dst + idx * 16) = *reinterpret_cast<const u32x4*>(src + off + 16 * c);
+  }
+}
+
+// Original order [B][L][H][D] <-> blocked [P][B][Bb][H][D] (pure data movement).
+__global__ __launch_bounds__(256) void layout_copy_kernel(const char* src, char* dst, int32_t B,
+                                                          int32_t H, int32_t P, int64_t Bb,
+                                                          int32_t layout, int32_t inverse,
+                                                          int32_t chunks) {
+  const int64_t L = (int64_t)P * Bb;
+  const int64_t total = (int64_t)P * B * Bb * H * chunks;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t c = (int32_t)(idx % chunks);
+    int64_t r = idx / chunks;
+    const int32_t h = (int32_t)(r % H);
+    r /= H;
+    const int64_t x = r % Bb;
+    r /= Bb;
+    const int32_t b = (int32_t)(r % B);
+    const int32_t s = (int32_t)(r / B);
+    const int64_t t = token_position(layout, P, Bb, s, x);
+    const int64_t orig = (((int64_t)b * L + t) * H + h) * chunks + c;
+    if (inverse)
+      reinterpret_cast<u32x4*>(dst)[orig] = reinterpret_cast<const u32x4*>(src)[idx];
+    else
+      reinterpret_cast<u32x4*>(dst)[idx] = reinterpret_cast<const u32x4*>(src)[orig];
+  }
+}
+
+__device__ __forceinline__ float load_elem(const void* base, int64_t off, int32_t bf16) {
+  if (bf16) {
+    const uint16_t u = reinterpret_cast<const uint16_t*>(base)[off];
+    return __uint_as_float((uint32_t)u << 16);
+  }
+  return reinterpret_cast<const float*>(base)[off];
+}
+
+// D = rowsum(dO * O) per (rank, batch, head, row) ("Ring Attention 論文分析"
+// (blog), section "逆伝播での KV 再循環"), and zeroing of that row's fp32 dQ
+// accumulator. One wave per row.
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p, int32_t bf16) {
+  const int lane = threadIdx.x % 64;
+  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
+  if (row >= rows) return;
+  int64_t r = row;
+  const int64_t x = r % p.Bb;
+  r /= p.Bb;
+  const int32_t h = (int32_t)(r % p.H);
+  r /= p.H;
+  const int32_t b = (int32_t)(r % p.B);
+  const int32_t ri = (int32_t)(r / p.B);
+  const int64_t oo = ri * p.o.s_blk + b * p.o.s_batch + x * p.o.s_tok + h * p.o.s_head;
+  const int64_t od = ri * p.dout.s_blk + b * p.dout.s_batch + x * p.dout.s_tok + h * p.dout.s_head;
+  float acc = 0.0f;
+  for (int e = lane; e < p.D; e += 64) acc = fmaf(load_elem(p.o.ptr, oo + e, bf16), load_elem(p.dout.ptr, od + e, bf16), acc);
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) p.dsum[row] = acc;
+  float* dqa = p.dq_acc + row * p.D;
+  for (int e = lane; e < p.D; e += 64) dqa[e] = 0.0f;
+}
+
+// dQ = scale * accumulator, cast to the problem dtype (round to nearest even).
+__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int32_t bf16) {
+  const int64_t total = (int64_t)p.n_ranks * p.B * p.H * p.Bb * p.D;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t e = (int32_t)(idx % p.D);
+    int64_t r = idx / p.D;
+    const int64_t x = r % p.Bb;
+    r /= p.Bb;
+    const int32_t h = (int32_t)(r % p.H);
+    r /= p.H;
+    const int32_t b = (int32_t)(r % p.B);
+    const int32_t ri = (int32_t)(r / p.B);
+    const int64_t off = ri * p.dq.s_blk + b * p.dq.s_batch + x * p.dq.s_tok + h * p.dq.s_head + e;
+    const float val = p.dq_acc[idx] * p.scale;
+    if (bf16)
+      reinterpret_cast<__bf16*>(p.dq.ptr)[off] = (__bf16)val;
+    else
+      reinterpret_cast<float*>(p.dq.ptr)[off] = val;
+  }
+}
+
+inline uint32_t grid_for(int64_t items, int32_t per_block) {
+  int64_t g = (items + per_block - 1) / per_block;
+  if (g > 1048576) g = 1048576;  // grid-stride beyond this
+  if (g < 1) g = 1;
+  return (uint32_t)g;
+}
+
+}  // namespace
+
+hipError_t launch_merge_lse(int64_t rows, int32_t d, const float* oa, const float* la,
+                            const float* ob, const float* lb, float* oo, float* lo,
+                            hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t grid = (rows + 3) / 4;
+  hipLaunchKernelGGL(merge_lse_kernel, dim3((uint32_t)grid), dim3(256), 0, s, rows, d, oa, la, ob, lb, oo, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_block(const Seq& src, int32_t blk, void* dst, int32_t B, int32_t H,
+                               int32_t D, int64_t Bb, int32_t es, hipStream_t s) {
+  const int32_t chunks = D * es / 16;
+  const int64_t total = (int64_t)B * Bb * H * chunks;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_block_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const char*>(src.ptr), src.s_blk, src.s_batch, src.s_tok,
+                     src.s_head, blk, reinterpret_cast<char*>(dst), B, H, Bb, chunks, es);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout_copy(const void* src, void* dst, int32_t B, int32_t H, int32_t D,
+                              int32_t P, int64_t Bb, int32_t layout, int32_t inverse, int32_t es,
+                              hipStream_t s) {
+  const int32_t chunks = D * es / 16;
+  const int64_t total = (int64_t)P * B * Bb * H * chunks;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(layout_copy_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const char*>(src), reinterpret_cast<char*>(dst), B, H, P, Bb,
+                     layout, inverse, chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_preprocess(const BwdParams& p, int32_t bf16, hipStream_t s) {
+  const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, s, p, bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_finalize(const BwdParams& p, int32_t bf16, hipStream_t s) {
+  const int64_t total = (int64_t)p.n_ranks * p.B * p.H * p.Bb * p.D;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dq_finalize_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, p, bf16);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -2,20 +2,26 @@
 
 This module is shared by the GPU path's tests/bench and by the CPU oracle's
 tests. It holds no attention arithmetic: it draws i.i.d. N(0, 1) float32
-samples from a counter-free, seeded numpy generator, rounds them to bfloat16
+samples from seeded numpy generators (one per chunk), rounds them to bfloat16
 bit patterns when a workload is bf16, and widens bit patterns back to floats
 so that both sides see exactly the same values.
 
-Seeding: ``numpy.random.Generator(PCG64(SeedSequence([workload_id,
-tensor_id])))`` with tensor ids Q=0, K=1, V=2, dO=3; values are drawn with
-``standard_normal(dtype=float32)`` in the [B, L, H, d] (original token order)
-layout.
+Seeding: the tensor, flattened in its [B, L, H, d] (original token order)
+layout, is cut into chunks of 2**22 elements; chunk c is drawn with
+``standard_normal(dtype=float32)`` from
+``numpy.random.Generator(PCG64(SeedSequence([workload_id, tensor_id, c])))``
+with tensor ids Q=0, K=1, V=2, dO=3. Chunks are independent, so they are drawn
+(and rounded) on several host threads.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
+
+CHUNK = 1 << 22
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
 
@@ -68,14 +74,49 @@ WORKLOADS = {
 }
 
 
-def rng_for(workload_id: int, tensor_id: int) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload_id, tensor_id])))
+def rng_for(workload_id: int, tensor_id: int, chunk: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([workload_id, tensor_id, chunk])))
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunked(n: int, fn):
+    """Run fn(c, lo, hi) over the CHUNK-sized pieces of range(n), threaded."""
+    pieces = [(c, lo, min(n, lo + CHUNK)) for c, lo in enumerate(range(0, n, CHUNK))]
+    if len(pieces) <= 1:
+        for p in pieces:
+            fn(*p)
+        return
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        list(ex.map(lambda p: fn(*p), pieces))
 
 
 def normal_f32(workload_id: int, tensor: str, shape) -> np.ndarray:
     """i.i.d. N(0,1) float32 array of ``shape`` for (workload, tensor)."""
-    g = rng_for(workload_id, TENSOR_IDS[tensor])
-    return g.standard_normal(size=tuple(shape), dtype=np.float32)
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    tid = TENSOR_IDS[tensor]
+
+    def draw(c, lo, hi):
+        out[lo:hi] = rng_for(workload_id, tid, c).standard_normal(size=hi - lo, dtype=np.float32)
+
+    _chunked(n, draw)
+    return out.reshape(shape)
+
+
+def _round_bits(u: np.ndarray) -> np.ndarray:
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    out = t.astype(np.uint16)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -83,18 +124,36 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
     NaN inputs map to a quiet NaN; the synthetic data never holds one.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    rounded = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
-    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
-    out = rounded.astype(np.uint16)
-    out[nan] = np.uint16(0x7FC0)
-    return out
+    u = np.ascontiguousarray(x, dtype=np.float32).reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+
+    def rnd(c, lo, hi):
+        out[lo:hi] = _round_bits(u[lo:hi])
+
+    _chunked(u.size, rnd)
+    return out.reshape(np.shape(x))
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def make_payload(workload_id: int, tensor: str, shape, dtype: str) -> np.ndarray:
+    """The values the GPU receives: float32, or uint16 bfloat16 bit patterns."""
+    x = normal_f32(workload_id, tensor, shape)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def to_f64(payload: np.ndarray) -> np.ndarray:
+    """Exact float64 widening of a payload (float32 or bf16 bit patterns)."""
+    if payload.dtype == np.uint16:
+        return bf16_bits_to_f32(payload).astype(np.float64)
+    return payload.astype(np.float64)
 
 
 def make_tensor(workload_id: int, tensor: str, shape, dtype: str):

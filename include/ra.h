@@ -1,0 +1,195 @@
+/*
+ * ra.h — C ABI of the MI355X (gfx950) exact blockwise ring-attention library.
+ *
+ * What it computes. Softmax attention O = softmax(scale * Q K^T) V, exactly
+ * (up to floating-point rounding order), computed the way one device of a
+ * ring computes it: the device keeps its query block Q_i resident and visits
+ * the P key/value blocks in ring order j = (i - k) mod P, k = 0..P-1, merging
+ * the partial results with an online softmax (running max, running sum of
+ * exponentials, rescaled accumulator).
+ *   Sources: "Ring Attention 論文分析" (blog), sections "ブロック単位の分割戦略"
+ *   (blockwise online softmax), "リングトポロジーと KV の循環" (ring loop:
+ *   send to rank+1, receive from rank-1), "Causal Masking の処理" (skip /
+ *   diagonal / full blocks) and "逆伝播での KV 再循環" (backward from the
+ *   saved log-sum-exp); "Ring Attention: Sequence Parallelism for Long
+ *   Context" (book chapter), sections "Ring Attention: Compute While You
+ *   Communicate" (step k attends KV block (i - k) mod P) and "The
+ *   Causal-Mask Problem: Striped Attention" (token t goes to device t mod P).
+ *
+ * One GPU plays one device's share (a single rank) or every device of the
+ * ring (a rank range); KV blocks are read in place, or, for a single rank,
+ * "received" into a double buffer by a copy on a second stream that overlaps
+ * the compute of the previous block.
+ *
+ * Conventions.
+ *   - A sequence of L = P * block_len tokens is split into P equal blocks.
+ *     Token positions (used by the causal mask) of local row x of block s:
+ *       RA_LAYOUT_CONTIGUOUS: t = s * block_len + x
+ *       RA_LAYOUT_STRIPED:    t = x * P + s   (ascending order within a block)
+ *     Causal: key t' is visible to query t iff t' <= t. Non-causal: all keys.
+ *   - scale > 0 is used as given; scale <= 0 selects 1 / sqrt(head_dim).
+ *   - lse (log-sum-exp) is the natural log of sum over visible keys of
+ *     exp(scale * q.k); fp32, laid out [rank - rank_begin][batch][head][row],
+ *     contiguous (row fastest).
+ *   - Accumulation is fp32 in every mode; outputs O, dQ, dK, dV are written
+ *     in the problem dtype, rounded to nearest even.
+ *
+ * Ownership and synchronisation. The caller owns every buffer (device memory)
+ * including the workspace, sized by ra_workspace_bytes(). The library never
+ * allocates or frees device memory; it creates and destroys only transient
+ * HIP events. Calls are asynchronous on the given stream(s); all work on the
+ * copy stream is joined back into the compute stream before the call returns,
+ * so outputs are ready when the compute stream reaches that point. Inputs must
+ * stay unmodified until then. The library keeps no state between calls.
+ *
+ * Errors. Every argument is validated before anything is enqueued; on a
+ * failed check the call returns a non-zero ra_status and launches nothing.
+ * A failing HIP call returns RA_ERR_HIP (work enqueued before it may run).
+ */
+#ifndef RA_H_
+#define RA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_LAYOUT_CONTIGUOUS = 0, /* device s owns tokens s*Bb .. s*Bb + Bb - 1 */
+  RA_LAYOUT_STRIPED = 1     /* token t belongs to device t mod P */
+} ra_layout;
+
+typedef enum {
+  RA_F32 = 0,  /* Q, K, V, O, dO, dQ, dK, dV are float32 */
+  RA_BF16 = 1  /* ... are bfloat16 (accumulation stays fp32) */
+} ra_dtype;
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_NULL = 1,        /* a required pointer is NULL */
+  RA_ERR_SHAPE = 2,       /* sizes, ranks, strides or layout out of range */
+  RA_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. head_dim) */
+  RA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
+  RA_ERR_ALIGN = 5,       /* a pointer or stride breaks 16-byte alignment */
+  RA_ERR_HIP = 6          /* a HIP runtime call failed */
+} ra_status;
+
+/* The problem: batch B, heads H, head dim d (= value dim), ring of P blocks
+ * of block_len tokens each. Supported: head_dim 64 or 128; any block_len >= 1
+ * (ragged tiles are masked); causal 0/1; layout matters only when causal. */
+typedef struct {
+  int32_t batch;
+  int32_t heads;
+  int32_t head_dim;
+  int32_t ring_size;  /* P >= 1 */
+  int64_t block_len;  /* tokens per block, all blocks equal */
+  int32_t layout;     /* ra_layout */
+  int32_t causal;     /* 0 or 1 */
+  float scale;        /* <= 0: 1/sqrt(head_dim) */
+  int32_t dtype;      /* ra_dtype */
+} ra_problem;
+
+/* A sequence tensor seen as ring blocks. Element (blk, b, x, h, e) — block,
+ * batch, local row, head, feature — is at
+ *     ptr + blk*s_blk + b*s_batch + x*s_tok + h*s_head + e
+ * counted in elements of the problem dtype (features are contiguous). An
+ * original-order [B, L, H, d] tensor is described without copying by
+ *     contiguous: s_blk = block_len*H*d, s_tok = H*d,   s_head = d, s_batch = L*H*d
+ *     striped:    s_blk = H*d,           s_tok = P*H*d, s_head = d, s_batch = L*H*d
+ * ptr and every stride times the element size must be multiples of 16 bytes. */
+typedef struct {
+  void* ptr;
+  int64_t s_blk;
+  int64_t s_batch;
+  int64_t s_tok;
+  int64_t s_head;
+} ra_seq;
+
+/* Bytes of workspace ra_forward (backward = 0) or ra_backward (backward = 1)
+ * needs for ranks [rank_begin, rank_end). use_copy_stream selects the
+ * forward's double-buffered receive mode. Returns 0 for an invalid problem
+ * (and when no workspace is needed). */
+size_t ra_workspace_bytes(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
+                          int32_t use_copy_stream, int32_t backward);
+
+/* Forward (blog: ring_attention_forward and the causal step; chapter: ring
+ * step k attends KV block (i - k) mod P). For every rank i in
+ * [rank_begin, rank_end): O_i and lse_i of query block i against all P KV
+ * blocks, visited in ring order, with the causal/striped mask; fully masked
+ * KV tiles are skipped.
+ *   q, o : blocks indexed by i - rank_begin (o written, dtype of problem)
+ *   k, v : blocks indexed by absolute block id 0..P-1
+ *   lse  : fp32 output, [rank_end - rank_begin][B][H][block_len]
+ *   copy : NULL -> one launch reads KV blocks in place, state stays on chip;
+ *          non-NULL -> requires rank_end = rank_begin + 1: each ring step's
+ *          KV block is gathered into a double buffer on `copy` while the
+ *          previous step computes on `compute` (events order both hazards);
+ *          the running state is merged between steps by log-sum-exp.
+ *   workspace: ra_workspace_bytes(pb, rb, re, copy != NULL, 0) bytes. */
+ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
+                     const ra_seq* q, const ra_seq* k, const ra_seq* v, const ra_seq* o,
+                     float* lse, void* workspace, size_t workspace_bytes,
+                     hipStream_t compute, hipStream_t copy);
+
+/* Backward (blog, section "逆伝播での KV 再循環"): recomputes P = exp(S - lse)
+ * with the forward's mask and returns dQ, dK, dV of sum(dO * O). D =
+ * rowsum(dO * O) is computed first from the given O. Each KV block visits the
+ * query blocks of ranks [rank_begin, rank_end) in ring order
+ * ((j + k) mod P at step k) carrying its dK/dV accumulators on chip; dQ is
+ * accumulated in an fp32 workspace.
+ *   q, o, dout, dq, lse: indexed by i - rank_begin; k, v, dk, dv: absolute.
+ *   dk, dv receive the contributions of the ranks in range (all P ranks:
+ *   the full gradient). Blocks of dk/dv are written for every j.
+ *   workspace: ra_workspace_bytes(pb, rb, re, 0, 1) bytes. */
+ra_status ra_backward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
+                      const ra_seq* q, const ra_seq* k, const ra_seq* v, const ra_seq* o,
+                      const ra_seq* dout, const float* lse, const ra_seq* dq,
+                      const ra_seq* dk, const ra_seq* dv, void* workspace,
+                      size_t workspace_bytes, hipStream_t compute);
+
+/* One stage of ra_backward, with the same arguments (ra_backward runs stages
+ * 0, 1, 2 in order on `compute`): 0 = D = rowsum(dO * O) and zeroing of the
+ * dQ accumulator; 1 = the ring walk (recompute, dV, dP, dS, dQ, dK); 2 = dQ
+ * scaled and cast to the problem dtype. Stage k reads what stage k-1 wrote to
+ * the workspace, so they must run in order on one stream; lets a caller
+ * time or interleave the stages. Unknown stage: RA_ERR_SHAPE. */
+ra_status ra_backward_stage(int32_t stage, const ra_problem* pb, int32_t rank_begin,
+                            int32_t rank_end, const ra_seq* q, const ra_seq* k, const ra_seq* v,
+                            const ra_seq* o, const ra_seq* dout, const float* lse,
+                            const ra_seq* dq, const ra_seq* dk, const ra_seq* dv,
+                            void* workspace, size_t workspace_bytes, hipStream_t compute);
+
+/* Merge two partial results over disjoint key sets (blog, section
+ * "ブロック単位の分割戦略": the online-softmax correction; here in its
+ * log-sum-exp form): lse = M + ln(e^(lse_a - M) + e^(lse_b - M)),
+ * M = max(lse_a, lse_b); O = e^(lse_a - lse) O_a + e^(lse_b - lse) O_b.
+ * A -inf partial has weight 0; two give lse = -inf, O = 0.
+ * o_*: fp32 [rows][head_dim]; lse_*: fp32 [rows]. o_out/lse_out may alias
+ * the a or b inputs exactly (in place). head_dim in 1..1024. */
+ra_status ra_merge_lse(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a,
+                       const float* o_b, const float* lse_b, float* o_out, float* lse_out,
+                       hipStream_t stream);
+
+/* Layout gather (chapter, section "The Causal-Mask Problem: Striped
+ * Attention"): copy an original-order [B, L, H, d] tensor `src` into blocked
+ * order `dst` ([P][B][block_len][H][d], block of rank 0 first) for the given
+ * layout, or back when inverse != 0. Pure data movement: bit-exact. Uses the
+ * problem's batch, heads, head_dim, ring_size, block_len, layout and dtype. */
+ra_status ra_layout_copy(const ra_problem* pb, const void* src, void* dst, int32_t inverse,
+                         hipStream_t stream);
+
+/* Static description of a status code. */
+const char* ra_status_string(int32_t status);
+
+/* ABI version: increments when a signature or struct above changes. */
+int32_t ra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H_ */

@@ -20,6 +20,7 @@ library routines, the invariants the pages state, or values the pages print).
 from .attention import (  # noqa: F401
     attention_fwd,
     attention_bwd,
+    attention_bwd_sampled,
     merge_lse,
     blockwise_ring_fwd,
     NEG_INF,

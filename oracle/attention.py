@@ -134,6 +134,50 @@ def attention_bwd(q, k, v, do, causal, scale=None, heads=None, row_chunk=1024):
     return dq, dk, dv, o, lse
 
 
+def attention_bwd_sampled(q, k, v, do, causal, q_rows, k_rows, scale=None, heads=None, row_chunk=1024):
+    """dQ at query rows ``q_rows`` and dK, dV at key rows ``k_rows``.
+
+    The same formulas as attention_bwd, evaluated only where asked: a row of
+    dQ needs that query's scores against all keys; a row of dK / dV needs
+    that key's column of probabilities over all queries, which needs every
+    query's lse and D = rowsum(dO * O) (so the forward runs on all rows).
+    Returns (dq [B, nq, Hs, d], dk [B, nk, Hs, d], dv [B, nk, Hs, d], o, lse).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, L, H, d = q.shape
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    heads = list(range(H)) if heads is None else list(heads)
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    o, lse = attention_fwd(q, k, v, causal, scale=scale, heads=heads, row_chunk=row_chunk)
+    t = np.arange(L, dtype=np.int64)
+    dq = np.zeros((B, len(q_rows), len(heads), d))
+    dk = np.zeros((B, len(k_rows), len(heads), d))
+    dv = np.zeros((B, len(k_rows), len(heads), v.shape[3]))
+    for b in range(B):
+        for hi, h in enumerate(heads):
+            qq, kk, vv, dd_o = q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h]
+            dsum = (dd_o * o[b, :, hi]).sum(axis=1)
+            lrow = lse[b, :, hi]
+            for c0 in range(0, len(q_rows), row_chunk):
+                rows = q_rows[c0:c0 + row_chunk]
+                s = _scores(qq[rows], kk, scale, rows, t, causal)
+                p = np.exp(s - lrow[rows][:, None])
+                ds = _dsoftmax(p, dd_o[rows] @ vv.T, dsum[rows])
+                dq[b, c0:c0 + len(rows), hi] = scale * (ds @ kk)
+            for c0 in range(0, len(k_rows), row_chunk):
+                cols = k_rows[c0:c0 + row_chunk]
+                s = _scores(qq, kk[cols], scale, t, cols, causal)  # [L, nc]
+                p = np.exp(s - lrow[:, None])
+                dv[b, c0:c0 + len(cols), hi] = p.T @ dd_o
+                ds = _dsoftmax(p, dd_o @ vv[cols].T, dsum)
+                dk[b, c0:c0 + len(cols), hi] = scale * (ds.T @ qq)
+    return dq, dk, dv, o, lse
+
+
 def _dsoftmax(p, dp, dd):
     """Gradient through the row softmax: dS = P * (dP - D)."""
     return p * (dp - dd[:, None])

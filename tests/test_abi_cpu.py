@@ -1,0 +1,167 @@
+"""The C-ABI library loads on a machine without a GPU, exports every function
+include/ra.h declares, and rejects invalid arguments before touching HIP.
+
+None of these calls reaches the GPU: every checked call fails validation,
+which the library performs before its first HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_blockwise_attention_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ra.library_path),
+                                reason="libra.so not built (python -m exact_blockwise_attention_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_functions():
+    assert declared_functions() == sorted(ra.EXPORTED_FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ra.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", ra.library_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (ra_[a-z_]+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_and_version():
+    assert ra.abi_version() == 1
+    assert ra.status_string(0) == "ok"
+    for code in range(1, 7):
+        assert ra.status_string(code) not in ("ok", "unknown status")
+    assert ra.status_string(99) == "unknown status"
+
+
+def problem(**kw):
+    base = dict(B=1, H=2, d=64, P=4, Bb=64, layout="striped", causal=True, dtype_code=ra.BF16)
+    base.update(kw)
+    return ra.make_problem(base["B"], base["H"], base["d"], base["P"], base["Bb"], base["layout"],
+                           base["causal"], base["dtype_code"])
+
+
+def fake_seq(ptr=0x10000, s_blk=128, s_batch=1 << 20, s_tok=512, s_head=64):
+    return ra.Seq(ptr, s_blk, s_batch, s_tok, s_head)
+
+
+def fwd_status(pb, rb=0, re_=None, seqs=None, lse=0x20000, ws=None, ws_bytes=0, copy=None):
+    re_ = pb.ring_size if re_ is None else re_
+    q, k, v, o = seqs or [fake_seq() for _ in range(4)]
+    lib = ra.library()
+    return lib.ra_forward(ctypes.byref(pb), rb, re_, ra._ref(q), ra._ref(k), ra._ref(v), ra._ref(o),
+                          lse, ws, ws_bytes, None, copy)
+
+
+def test_workspace_sizes():
+    pb = problem(d=128, P=8, Bb=4096, H=32)
+    assert ra.workspace_bytes(pb, 0, 8, False, False) == 0
+    blk = 1 * 4096 * 32 * 128 * 2
+    rows = 1 * 32 * 4096
+    expect_fwd = 4 * blk + rows * 128 * 4 + rows * 4  # all multiples of 256 here
+    assert ra.workspace_bytes(pb, 7, 8, True, False) == expect_fwd
+    rows8 = 8 * rows
+    assert ra.workspace_bytes(pb, 0, 8, False, True) == rows8 * 4 + rows8 * 128 * 4
+    assert ra.workspace_bytes(problem(d=96), 0, 4, False, True) == 0  # invalid problem
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, 2), ("heads", 0, 2), ("ring_size", 0, 2), ("block_len", 0, 2),
+    ("layout", 2, 2), ("causal", 3, 2), ("dtype", 7, 2), ("head_dim", 96, 3), ("head_dim", 32, 3),
+])
+def test_invalid_problem_fields(field, value, code):
+    pb = problem()
+    setattr(pb, field, value)
+    assert fwd_status(pb) == code
+
+
+def test_invalid_scale_nan():
+    pb = problem()
+    pb.scale = float("nan")
+    assert fwd_status(pb) == 2
+
+
+def test_invalid_rank_ranges():
+    pb = problem()
+    assert fwd_status(pb, rb=-1, re_=2) == 2
+    assert fwd_status(pb, rb=2, re_=2) == 2
+    assert fwd_status(pb, rb=0, re_=5) == 2
+
+
+def test_null_pointers():
+    lib = ra.library()
+    assert lib.ra_forward(None, 0, 1, None, None, None, None, None, None, 0, None, None) == 1
+    pb = problem()
+    seqs = [fake_seq() for _ in range(4)]
+    seqs[2] = None
+    assert fwd_status(pb, seqs=seqs) == 1
+    seqs = [fake_seq() for _ in range(4)]
+    seqs[0].ptr = None
+    assert fwd_status(pb, seqs=seqs) == 1
+    assert fwd_status(pb, lse=None) == 1
+
+
+def test_misaligned_pointers_and_strides():
+    pb = problem()
+    seqs = [fake_seq() for _ in range(4)]
+    seqs[1] = fake_seq(ptr=0x10008)
+    assert fwd_status(pb, seqs=seqs) == 5
+    seqs = [fake_seq() for _ in range(4)]
+    seqs[3] = fake_seq(s_tok=513)  # 1026 bytes: not a multiple of 16
+    assert fwd_status(pb, seqs=seqs) == 5
+    seqs = [fake_seq() for _ in range(4)]
+    seqs[0] = fake_seq(s_head=-64)
+    assert fwd_status(pb, seqs=seqs) == 2
+    assert fwd_status(pb, lse=0x20002) == 5
+
+
+def test_copy_mode_requires_one_rank_and_workspace():
+    pb = problem()
+    fake_stream = ctypes.c_void_p(0x1234)
+    assert fwd_status(pb, rb=0, re_=2, copy=fake_stream) == 2
+    assert fwd_status(pb, rb=1, re_=2, copy=fake_stream, ws=None) == 4
+    need = ra.workspace_bytes(pb, 1, 2, True, False)
+    assert fwd_status(pb, rb=1, re_=2, copy=fake_stream, ws=0x100000, ws_bytes=need - 1) == 4
+    assert fwd_status(pb, rb=1, re_=2, copy=fake_stream, ws=0x100010, ws_bytes=need) == 5
+
+
+def test_backward_validation():
+    lib = ra.library()
+    pb = problem()
+    s = [fake_seq() for _ in range(8)]
+    args = lambda ws, nbytes, lse=0x20000: (ctypes.byref(pb), 0, 4, *[ra._ref(x) for x in s[:5]], lse,
+                                            *[ra._ref(x) for x in s[5:]], ws, nbytes, None)
+    assert lib.ra_backward(*args(None, 0)) == 4
+    need = ra.workspace_bytes(pb, 0, 4, False, True)
+    assert lib.ra_backward(*args(0x100000, need - 4)) == 4
+    assert lib.ra_backward(*args(0x100000, need, lse=None)) == 1
+    s[6] = None
+    assert lib.ra_backward(*args(0x100000, need)) == 1
+
+
+def test_merge_and_layout_copy_validation():
+    lib = ra.library()
+    p = 0x10000
+    assert lib.ra_merge_lse(4, 64, None, p, p, p, p, p, None) == 1
+    assert lib.ra_merge_lse(-1, 64, p, p, p, p, p, p, None) == 2
+    assert lib.ra_merge_lse(4, 0, p, p, p, p, p, p, None) == 2
+    assert lib.ra_merge_lse(4, 2048, p, p, p, p, p, p, None) == 2
+    assert lib.ra_merge_lse(4, 64, p + 8, p, p, p, p, p, None) == 5
+    assert lib.ra_merge_lse(4, 64, p, p + 2, p, p, p, p, None) == 5
+    pb = problem()
+    assert lib.ra_layout_copy(ctypes.byref(pb), None, p, 0, None) == 1
+    assert lib.ra_layout_copy(ctypes.byref(pb), p + 4, p, 0, None) == 5
+    assert lib.ra_layout_copy(None, p, p, 0, None) == 1

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small cases compare every element; they span several tiles, ragged tails
+(block lengths that are not tile multiples), both layouts, causal and not,
+bf16 and fp32, head_dim 64 and 128, single-rank (double-buffered receive)
+and rank-range launches, and degenerate shapes (one block, one token per
+block). Bars: max |GPU - oracle| <= 2e-2 for bf16 inputs (fp32 accumulation)
+and <= 1e-4 for fp32 inputs, on O, lse, dQ, dK and dV; data movement
+(layout gathers, pre-permuted vs strided inputs) must be bit-exact.
+"""
+import numpy as np
+import pytest
+
+import exact_blockwise_attention_amd as ra
+import oracle
+from gpu_cases import TOL, Case, assert_close, lse_to_original, log, payloads, rank_positions, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ra.library()  # the HIP library must load; there is no fallback
+
+
+def run_fwd(case, dev, rank_range=None, copy=False):
+    stream = torch.cuda.Stream() if copy else None
+    o, lse = ra.attention_forward(dev["q"], dev["k"], dev["v"], case.P, case.layout, case.causal,
+                                  rank_range=rank_range, copy_stream=stream)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_fwd(case, o, lse, ref_o, ref_lse, ranks):
+    pos, lse_vals = lse_to_original(case, lse, ranks)
+    tol = TOL[case.dtype]
+    assert_close("O", to_f64(o)[:, pos], ref_o[:, pos], tol, case)
+    assert_close("lse", lse_vals, ref_lse[:, pos], tol, case)
+
+
+SMALL_FWD = [
+    Case(101, 1, 2, 1024, 128, 4, False, "contiguous", "bf16"),
+    Case(102, 2, 2, 800, 128, 4, True, "contiguous", "bf16"),
+    Case(103, 2, 2, 800, 128, 4, True, "striped", "bf16"),
+    Case(104, 1, 3, 408, 128, 3, True, "striped", "bf16"),
+    Case(105, 1, 2, 650, 64, 5, True, "striped", "bf16"),
+    Case(106, 2, 1, 128, 64, 2, True, "contiguous", "bf16"),
+    Case(107, 1, 1, 1024, 64, 4, False, "contiguous", "f32"),
+    Case(108, 1, 2, 400, 64, 4, True, "striped", "f32"),
+    Case(109, 1, 2, 210, 128, 3, True, "contiguous", "f32"),
+    Case(110, 1, 2, 300, 128, 1, True, "contiguous", "bf16"),   # one block
+    Case(111, 1, 2, 8, 128, 8, True, "striped", "bf16"),        # one token per block
+    Case(112, 1, 2, 8, 64, 8, True, "contiguous", "f32"),
+    Case(113, 1, 1, 4096, 128, 2, True, "striped", "bf16"),     # many tiles per block
+]
+
+
+@pytest.mark.parametrize("case", SMALL_FWD, ids=str)
+def test_forward_small(case):
+    log(f"forward {case}")
+    p = payloads(case)
+    dev = {n: to_device(x) for n, x in p.items()}
+    ref_o, ref_lse = oracle.attention_fwd(*(syn_f64(p[n]) for n in "qkv"), case.causal)
+    o, lse = run_fwd(case, dev)
+    check_fwd(case, o, lse, ref_o, ref_lse, range(case.P))
+
+
+def syn_f64(x):
+    from exact_blockwise_attention_amd import synthetic as syn
+    return syn.to_f64(x)
+
+
+STEP_CASES = [
+    Case(121, 1, 2, 800, 128, 4, True, "striped", "bf16"),
+    Case(122, 1, 2, 800, 128, 4, True, "contiguous", "bf16"),
+    Case(123, 1, 2, 520, 64, 4, False, "contiguous", "bf16"),
+    Case(124, 1, 1, 400, 64, 4, True, "striped", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", STEP_CASES, ids=str)
+def test_forward_single_rank_with_receive_stream(case):
+    """One device's share: every ring step's KV block is gathered into a
+    double buffer on a second stream; the state is merged between steps."""
+    p = payloads(case)
+    dev = {n: to_device(x) for n, x in p.items()}
+    ref_o, ref_lse = oracle.attention_fwd(*(syn_f64(p[n]) for n in "qkv"), case.causal)
+    for r in range(case.P):
+        log(f"single rank {r} with receive stream: {case}")
+        o, lse = run_fwd(case, dev, rank_range=(r, r + 1), copy=True)
+        check_fwd(case, o, lse, ref_o, ref_lse, [r])
+        o2, lse2 = run_fwd(case, dev, rank_range=(r, r + 1), copy=False)
+        check_fwd(case, o2, lse2, ref_o, ref_lse, [r])
+    log(f"rank range [1, 3): {case}")
+    o, lse = run_fwd(case, dev, rank_range=(1, 3))
+    check_fwd(case, o, lse, ref_o, ref_lse, [1, 2])
+
+
+def test_forward_is_deterministic_and_grid_independent():
+    """Same inputs give bitwise-equal outputs, whether a rank is computed
+    alone or with the whole ring in one launch."""
+    case = Case(131, 1, 2, 1024, 128, 4, True, "striped", "bf16")
+    log(f"determinism {case}")
+    dev = {n: to_device(x) for n, x in payloads(case).items()}
+    o1, l1 = run_fwd(case, dev)
+    o2, l2 = run_fwd(case, dev)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    o3, l3 = run_fwd(case, dev, rank_range=(2, 3))
+    pos = rank_positions(case, [2])[0]
+    assert torch.equal(o1[:, pos].view(torch.int16), o3[:, pos].view(torch.int16))
+    assert torch.equal(l1[2], l3[0])
+
+
+def test_layout_copy_is_bit_exact():
+    case = Case(132, 2, 3, 96, 64, 4, True, "striped", "bf16")
+    log(f"layout copy {case}")
+    for layout in ("striped", "contiguous"):
+        p = payloads(case, ("q",))["q"]
+        x = to_device(p)
+        blk = ra.layout_copy(x, case.P, layout)
+        torch.cuda.synchronize()
+        perm = oracle.layout_perm(case.L, case.P, layout)
+        expect = p[:, perm].reshape(case.B, case.P, case.Bb, case.H, case.d).transpose(1, 0, 2, 3, 4)
+        got = blk.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, expect)
+        back = ra.layout_copy(blk, case.P, layout, inverse=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(back.view(torch.int16).cpu().numpy().view(np.uint16), p)
+
+
+def test_prepermuted_input_gives_bitwise_equal_output():
+    """Striped attention on blocked (pre-permuted) tensors equals, bit for
+    bit, striped attention on original-order tensors described by strides."""
+    case = Case(133, 1, 2, 1000, 128, 4, True, "striped", "bf16")
+    log(f"pre-permuted vs strided {case}")
+    dev = {n: to_device(x) for n, x in payloads(case).items()}
+    o, lse = run_fwd(case, dev)
+    blk = {n: ra.layout_copy(t, case.P, "striped") for n, t in dev.items()}
+    o_blk = torch.empty_like(blk["q"])
+    lse_blk = torch.empty_like(lse)
+    pb = ra.make_problem(case.B, case.H, case.d, case.P, case.Bb, "striped", True, ra.BF16)
+    ra.forward_raw(pb, 0, case.P, ra.seq_blocked(blk["q"]), ra.seq_blocked(blk["k"]), ra.seq_blocked(blk["v"]),
+                   ra.seq_blocked(o_blk), lse_blk.data_ptr(), None, 0, ra._stream_handle(None), None)
+    o_back = ra.layout_copy(o_blk, case.P, "striped", inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_back.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(lse_blk, lse)
+
+
+def test_merge_lse_kernel():
+    rng = np.random.default_rng(134)
+    rows, d = 1000, 128
+    oa, ob = rng.standard_normal((rows, d)), rng.standard_normal((rows, d))
+    la, lb = rng.standard_normal(rows) * 5, rng.standard_normal(rows) * 5
+    la[::7] = -np.inf
+    lb[::11] = -np.inf
+    ref_o, ref_l = oracle.merge_lse(oa, la, ob, lb)
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")  # noqa: E731
+    log("merge_lse rows=1000 d=128")
+    o, l = ra.merge_lse(t(oa), t(la), t(ob), t(lb))
+    torch.cuda.synchronize()
+    assert_close("merge O", o.cpu().numpy(), ref_o, 1e-5)
+    lg = l.cpu().numpy()
+    assert np.array_equal(np.isneginf(lg), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert_close("merge lse", lg[fin], ref_l[fin], 1e-5)
+    # in place, odd head_dim (scalar path)
+    oa3, ob3 = t(oa[:, :37]).contiguous(), t(ob[:, :37]).contiguous()
+    la3 = t(la)
+    ref_o3, ref_l3 = oracle.merge_lse(oa[:, :37], la, ob[:, :37], lb)
+    ra.merge_lse(oa3, la3, ob3, t(lb), out=oa3, lse_out=la3)
+    torch.cuda.synchronize()
+    assert_close("merge O in place", oa3.cpu().numpy(), ref_o3, 1e-5)
+    assert_close("merge lse in place", la3.cpu().numpy()[fin], ref_l3[fin], 1e-5)
+
+
+SMALL_BWD = [
+    Case(141, 1, 2, 800, 128, 4, True, "striped", "bf16"),
+    Case(142, 2, 1, 800, 128, 4, True, "contiguous", "bf16"),
+    Case(143, 1, 2, 512, 128, 4, False, "contiguous", "bf16"),
+    Case(144, 1, 2, 650, 64, 5, True, "striped", "bf16"),
+    Case(145, 1, 1, 300, 128, 1, True, "contiguous", "bf16"),
+    Case(146, 1, 2, 400, 64, 4, True, "striped", "f32"),
+    Case(147, 1, 1, 210, 128, 3, True, "contiguous", "f32"),
+    Case(148, 1, 1, 8, 128, 8, True, "striped", "bf16"),
+]
+
+
+def run_bwd(case, dev, rank_range=None):
+    o, lse = run_fwd(case, dev, rank_range=rank_range)
+    dq, dk, dv = ra.attention_backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, case.P, case.layout,
+                                       case.causal, rank_range=rank_range)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("case", SMALL_BWD, ids=str)
+def test_backward_small(case):
+    log(f"backward {case}")
+    p = payloads(case, ("q", "k", "v", "do"))
+    dev = {n: to_device(x) for n, x in p.items()}
+    f = {n: syn_f64(x) for n, x in p.items()}
+    dq_r, dk_r, dv_r, _, _ = oracle.attention_bwd(f["q"], f["k"], f["v"], f["do"], case.causal)
+    dq, dk, dv = run_bwd(case, dev)
+    tol = TOL[case.dtype]
+    assert_close("dQ", to_f64(dq), dq_r, tol, case)
+    assert_close("dK", to_f64(dk), dk_r, tol, case)
+    assert_close("dV", to_f64(dv), dv_r, tol, case)
+
+
+def test_backward_rank_range():
+    """Ranks [1, 3): dQ of their rows, and dK/dV holding only their queries'
+    contributions (the oracle's gradient with dO zero outside those rows)."""
+    case = Case(149, 1, 2, 800, 128, 4, True, "striped", "bf16")
+    log(f"backward rank range [1,3) {case}")
+    p = payloads(case, ("q", "k", "v", "do"))
+    dev = {n: to_device(x) for n, x in p.items()}
+    f = {n: syn_f64(x) for n, x in p.items()}
+    pos = rank_positions(case, [1, 2]).reshape(-1)
+    do_masked = np.zeros_like(f["do"])
+    do_masked[:, pos] = f["do"][:, pos]
+    dq_r, dk_r, dv_r, _, _ = oracle.attention_bwd(f["q"], f["k"], f["v"], do_masked, case.causal)
+    dq, dk, dv = run_bwd(case, dev, rank_range=(1, 3))
+    tol = TOL[case.dtype]
+    assert_close("dQ", to_f64(dq)[:, pos], dq_r[:, pos], tol, case)
+    assert_close("dK", to_f64(dk), dk_r, tol, case)
+    assert_close("dV", to_f64(dv), dv_r, tol, case)

@@ -193,6 +193,19 @@ def test_bwd_column_identities(causal):
     assert np.max(np.abs(dv.sum(axis=1) - do.sum(axis=1))) < 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_sampled_equals_full(causal):
+    """Row/column-sampled gradients equal the corresponding rows of the full
+    backward (which is pinned to autograd and finite differences above)."""
+    q, k, v, do = (rnd(s, 2, 41, 3, 5) for s in (48, 49, 80, 81))
+    full = attention_bwd(q, k, v, do, causal, heads=[2, 0], row_chunk=9)
+    qr, kr = np.array([0, 7, 40, 13]), np.array([40, 0, 22, 5, 6])
+    dq, dk, dv, _, _ = oracle.attention_bwd_sampled(q, k, v, do, causal, qr, kr, heads=[2, 0], row_chunk=3)
+    assert np.max(np.abs(dq - full[0][:, qr])) < 1e-13
+    assert np.max(np.abs(dk - full[1][:, kr])) < 1e-13
+    assert np.max(np.abs(dv - full[2][:, kr])) < 1e-13
+
+
 def test_bwd_head_subset_equals_full():
     q, k, v, do = (rnd(s, 1, 20, 4, 4) for s in (44, 45, 46, 47))
     full = attention_bwd(q, k, v, do, True)
