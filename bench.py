@@ -28,7 +28,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_blockwise_attention_amd/csrc/" + f for f in
-                  ("ra_fwd.hip", "ra_bwd.hip", "ra_misc.hip", "ra_api.cpp", "ra_schedule.h", "ra_internal.h")]
+                  ("ra_fwd.hip", "ra_bwd.hip", "ra_dq.hip", "ra_misc.hip", "ra_api.cpp", "ra_schedule.h", "ra_internal.h", "ra_lds.h", "ra_kvwalk.h")]
 
 
 def parse():
@@ -191,32 +191,31 @@ def main():
         bwd_ws = torch.empty(bws, dtype=torch.uint8, device="cuda")
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
-    def step(timing=None):
+    def mark(timing, key):
         if timing is not None:
-            timing["f0"].append(ev())
-            timing["f0"][-1].record(stream)
+            e = ev()
+            e.record(stream)
+            timing[key].append(e)
+
+    def step(timing=None):
+        mark(timing, "f0")
         ra.forward_raw(pb, rb, re_, so(t["q"]), sk(t["k"]), sk(t["v"]), so(o), lse.data_ptr(),
                        fwd_ws.data_ptr() if fws else None, fws, sh, ch)
-        if timing is not None:
-            timing["f1"].append(ev())
-            timing["f1"][-1].record(stream)
+        mark(timing, "f1")
         if bwd:
             args_ = (pb, rb, re_, so(t["q"]), sk(t["k"]), sk(t["v"]), so(o), so(t["do"]), lse.data_ptr(), so(dq),
                      sk(dk), sk(dv), bwd_ws.data_ptr(), bws, sh)
             ra.backward_stage_raw(0, *args_)
-            if timing is not None:
-                timing["b0"].append(ev())
-                timing["b0"][-1].record(stream)
+            mark(timing, "b0")
             ra.backward_stage_raw(1, *args_)
-            if timing is not None:
-                timing["b1"].append(ev())
-                timing["b1"][-1].record(stream)
+            mark(timing, "b1")
             ra.backward_stage_raw(2, *args_)
+            mark(timing, "b2")
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    timing = {"f0": [], "f1": [], "b0": [], "b1": []}
+    timing = {"f0": [], "f1": [], "b0": [], "b1": [], "b2": []}
     start, stop = ev(), ev()
     torch.cuda.synchronize()
     start.record(stream)
@@ -227,19 +226,32 @@ def main():
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
 
+    def span(a, b):
+        return sum(x.elapsed_time(y) for x, y in zip(timing[a], timing[b])) / args.steps
+
     pairs = pair_count(layout, w.causal, P, Bb, ranks) * w.batch * w.heads
-    fwd_flops = 4 * d * pairs
-    bwd_flops = 10 * d * pairs if bwd else 0
-    fwd_ms = sum(a.elapsed_time(b) for a, b in zip(timing["f0"], timing["f1"])) / args.steps
-    details = {"pairs": pairs, "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_flops / fwd_ms / 1e9, 2)}
+    d_ = d
+    fwd_flops = 4 * d_ * pairs
+    bwd_flops = 10 * d_ * pairs if bwd else 0
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    fwd_ms = span("f0", "f1")
+    # per kernel: (ms, algorithmic flops it performs, tag). The dK/dV walk does
+    # the S recompute, dP, dV and dK products (8d per pair); the dQ walk adds
+    # only dQ (2d per pair) to the method's work, its S/dP recompute is extra.
+    kern = {"fwd": (fwd_ms, fwd_flops, "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel")}
+    details = {"pairs": pairs, "fwd_ms": round(fwd_ms, 4), "fwd_tflops": round(fwd_flops / fwd_ms / 1e9, 2)}
     if bwd:
-        bwd_main_ms = sum(a.elapsed_time(b) for a, b in zip(timing["b0"], timing["b1"])) / args.steps
-        details.update({"bwd_main_ms": round(bwd_main_ms, 4), "bwd_main_tflops": round(bwd_flops / bwd_main_ms / 1e9, 2),
-                        "bwd_other_ms": round(ms - fwd_ms - bwd_main_ms, 4)})
-        dom_ms, dom_flops, tag = bwd_main_ms, bwd_flops, "bwd_bf16_kernel"
-    else:
-        dom_ms, dom_flops, tag = fwd_ms, fwd_flops, "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel"
+        pre_ms, dkdv_ms, dq_ms = span("f1", "b0"), span("b0", "b1"), span("b1", "b2")
+        kern["dkdv"] = (dkdv_ms, 8 * d_ * pairs, "dkdv_bf16_kernel")
+        kern["dq"] = (dq_ms, 2 * d_ * pairs, "dq_bf16_kernel")
+        details.update({"bwd_pre_ms": round(pre_ms, 4), "dkdv_ms": round(dkdv_ms, 4), "dq_ms": round(dq_ms, 4),
+                        "dkdv_tflops": round(8 * d_ * pairs / dkdv_ms / 1e9, 2),
+                        "dq_tflops_alg": round(2 * d_ * pairs / dq_ms / 1e9, 2),
+                        "dq_tflops_mfma": round(6 * d_ * pairs / dq_ms / 1e9, 2),
+                        "bwd_ms": round(pre_ms + dkdv_ms + dq_ms, 4),
+                        "bwd_tflops": round(bwd_flops / (pre_ms + dkdv_ms + dq_ms) / 1e9, 2)})
+    dom = max(kern, key=lambda k_: kern[k_][0])
+    dom_ms, dom_flops, tag = kern[dom]
     achieved = dom_flops / dom_ms / 1e9
     value = (fwd_flops + bwd_flops) / ms / 1e9
     roof = {"bound": "mfma", "kernel": tag, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",

@@ -5,7 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/ra.h"
+#include "ra.h"
 #include "ra_internal.h"
 #include "ra_schedule.h"
 
@@ -85,15 +85,14 @@ FwdWs fwd_ws_layout(const ra_problem* pb, int32_t n_ranks, int32_t copy) {
 }
 
 struct BwdWs {
-  size_t dsum, dq_acc, total;
+  size_t dsum, total;
 };
 
 BwdWs bwd_ws_layout(const ra_problem* pb, int32_t n_ranks) {
   BwdWs w{};
   const size_t rows = (size_t)n_ranks * pb->batch * pb->heads * pb->block_len;
   w.dsum = 0;
-  w.dq_acc = align_up(rows * sizeof(float));
-  w.total = align_up(w.dq_acc + rows * pb->head_dim * sizeof(float));
+  w.total = align_up(rows * sizeof(float));
   return w;
 }
 
@@ -257,7 +256,6 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
   p.dv = to_seq(dv);
   p.lse = lse;
   p.dsum = reinterpret_cast<float*>(ws + w.dsum);
-  p.dq_acc = reinterpret_cast<float*>(ws + w.dq_acc);
   p.B = pb->batch;
   p.H = pb->heads;
   p.D = pb->head_dim;
@@ -272,8 +270,9 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
   const int32_t bf16 = pb->dtype == RA_BF16;
   if (first_stage <= 0 && last_stage >= 0) RA_HIP(ra::launch_bwd_preprocess(p, bf16, compute));
   if (first_stage <= 1 && last_stage >= 1)
-    RA_HIP(bf16 ? ra::launch_bwd_bf16(p, compute) : ra::launch_bwd_f32(p, compute));
-  if (first_stage <= 2 && last_stage >= 2) RA_HIP(ra::launch_dq_finalize(p, bf16, compute));
+    RA_HIP(bf16 ? ra::launch_dkdv_bf16(p, compute) : ra::launch_dkdv_f32(p, compute));
+  if (first_stage <= 2 && last_stage >= 2)
+    RA_HIP(bf16 ? ra::launch_dq_bf16(p, compute) : ra::launch_dq_f32(p, compute));
   return RA_OK;
 }
 

@@ -6,107 +6,63 @@
 // dS = P * (dP - D) with D = rowsum(dO * O), dQ = scale * dS K and
 // dK = scale * dS^T Q; the dK/dV partials belong to the KV block's owner.
 //
-// Here one workgroup owns a tile of keys of KV block j for one (batch, head)
-// and carries its dK/dV accumulators on chip while the block travels the
-// ring: at step k it meets the query block of rank (j + k) mod P. Query
-// tiles the causal/striped mask hides from every key of the tile are
-// skipped. dQ of the met query rows is accumulated with fp32 atomics in a
-// workspace and scaled/cast once at the end.
+// This file holds the dK/dV half: one workgroup owns a tile of 128 keys of KV
+// block j for one (batch, head) and carries its dK/dV accumulators on chip
+// while the block travels the ring: at step k it meets the query block of
+// rank (j + k) mod P. Query tiles the causal/striped mask hides from every
+// key of the tile are skipped. The dQ half (ra_dq.hip) walks the ring from
+// the query side, so neither half needs atomics.
 //
-// bf16 path, per wave (32 keys of the tile's 128): K and V of the wave's keys
-// live in registers as MFMA B operands; S = Q K^T and dP = dO V^T come out
-// with lane (h, n) holding key n against 16 query rows, which is the operand
-// layout the dV^T += dO^T P and dK^T += Q^T dS products need (contraction
-// over query rows, whose order inside an MFMA is free). dS goes through LDS
-// once, row-major, for dQ = dS K with K^T staged in LDS.
+// bf16 path: 8 waves; wave w owns keys 32(w%4) .. +31 of the tile and query
+// rows 32(w/4) .. +31 of each 64-row query tile (the two waves sharing keys
+// add their dK/dV partials at the end). K and V of the tile and a double
+// buffer of Q/dO tiles sit row-major in LDS; the next Q/dO tile travels
+// through registers while the current one is computed. S = Q K^T and
+// dP = dO V^T come out with lane (h, n) holding key n against 16 query rows —
+// the operand layout dV^T += dO^T P and dK^T += Q^T dS need (contraction over
+// query rows, whose order inside an MFMA is free); the dO^T and Q^T operands
+// come from transposing LDS reads.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
 #include "ra_internal.h"
+#include "ra_lds.h"
 #include "ra_schedule.h"
 
 namespace ra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kThreads = 256;
-constexpr int kKn = 128;  // keys per workgroup (32 per wave)
-constexpr int kQm = 64;   // query rows per visited tile
-constexpr int kBandAll = 1 << 30;
+constexpr int kBandAllKeys = 1 << 30;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKn = 128;  // keys per workgroup (32 per wave, two waves per key group)
+constexpr int kQm = 64;   // query rows per visited tile (32 per wave)
 
 template <int D>
 struct BwdLds {
-  static constexpr int RS = D + 8;     // [rows][D] row stride
-  static constexpr int TS = kQm + 4;   // [D][64 rows] transposed stride
-  static constexpr int KTS = kKn + 8;  // K^T [D][128 keys] stride
-  static constexpr int DSS = kKn + 8;  // dS [64 rows][128 keys] stride
-  static constexpr int Q_ROW = 0;
-  static constexpr int DO_ROW = Q_ROW + kQm * RS;
-  static constexpr int Q_T = DO_ROW + kQm * RS;
-  static constexpr int DO_T = Q_T + D * TS;
-  static constexpr int K_T = DO_T + D * TS;
-  static constexpr int DS = K_T + D * KTS;
-  static constexpr int BF16_ELEMS = DS + kQm * DSS;
-  static constexpr int F32_OFF = (BF16_ELEMS * 2 + 15) / 16 * 16;  // bytes
-  static constexpr int BYTES = F32_OFF + 2 * kQm * 4;
+  static constexpr int RS = PadRow<D>::RS;
+  static constexpr int K = 0;                   // [128][D] padded
+  static constexpr int V = K + kKn * RS;        // [128][D] padded
+  static constexpr int Q = V + kKn * RS;        // [2 stages][64][D] padded
+  static constexpr int DO = Q + 2 * kQm * RS;   // [2 stages][64][D] padded
+  static constexpr int BF16_ELEMS = DO + 2 * kQm * RS;
+  static constexpr int F32_OFF = BF16_ELEMS * 2;       // bytes
+  static constexpr int BYTES = F32_OFF + 4 * kQm * 4;  // lse2[2][64], dsum[2][64]
+  static_assert(4 * ((D / 32) * 16) * 64 * 4 <= F32_OFF, "the dK (then dV) exchange must fit in the tile area");
 };
 
-// Rows [r_lo, r_lo + ROWS) of a [rows][D] strided tensor into LDS, row-major.
-template <int D, int ROWS>
-__device__ __forceinline__ void stage_rows(__bf16* dst, int stride, const __bf16* base, int64_t s_tok,
-                                           int64_t r_lo, int64_t nrows, int tid) {
-  constexpr int CR = D / 8;
-  constexpr int RPP = kThreads / CR;
-  const int c = tid % CR;
-  const int r0 = tid / CR;
-#pragma unroll
-  for (int p = 0; p < ROWS / RPP; ++p) {
-    const int r = r0 + RPP * p;
-    const int64_t x = r_lo + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (x < nrows) val = *reinterpret_cast<const u32x4*>(base + x * s_tok + 8 * c);
-    *reinterpret_cast<u32x4*>(dst + r * stride + 8 * c) = val;
-  }
-}
-
-// Same rows transposed: dst[e][r] (feature-major), written as 8-byte chunks.
-template <int D, int ROWS>
-__device__ __forceinline__ void stage_transposed(__bf16* dst, int stride, const __bf16* base,
-                                                 int64_t s_tok, int64_t r_lo, int64_t nrows, int tid) {
-  constexpr int NP = D / 2;
-  constexpr int NG = kThreads / NP;
-  constexpr int KG = ROWS / NG;
-  const int pr = tid % NP;
-  const int g = tid / NP;
-  uint32_t w[KG];
-#pragma unroll
-  for (int q = 0; q < KG; ++q) {
-    const int64_t x = r_lo + KG * g + q;
-    w[q] = (x < nrows) ? *reinterpret_cast<const uint32_t*>(base + x * s_tok + 2 * pr) : 0u;
-  }
-  __bf16* even = dst + (2 * pr) * stride + KG * g;
-  __bf16* odd = even + stride;
-#pragma unroll
-  for (int q = 0; q < KG; q += 4) {
-    u32x2 e, o;
-    e[0] = (w[q] & 0xFFFFu) | (w[q + 1] << 16);
-    e[1] = (w[q + 2] & 0xFFFFu) | (w[q + 3] << 16);
-    o[0] = (w[q] >> 16) | (w[q + 1] & 0xFFFF0000u);
-    o[1] = (w[q + 2] >> 16) | (w[q + 3] & 0xFFFF0000u);
-    *reinterpret_cast<u32x2*>(even + q) = e;
-    *reinterpret_cast<u32x2*>(odd + q) = o;
-  }
-}
+// Registers carrying the next Q/dO tile from global memory to LDS.
+template <int D>
+struct QTileRegs {
+  static constexpr int CR = D / 8;
+  static constexpr int RPP = kThreads / CR;
+  static constexpr int NP = kQm / RPP;
+  u32x4 q[NP], o[NP];
+  float lse2, dsum;
+};
 
 // Heaviest KV tiles first: early keys are seen by more query rows.
 __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int32_t tiles, int32_t* j,
@@ -120,19 +76,98 @@ __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int3
   }
 }
 
+// The (rank, query tile) pairs a KV tile meets, in ring order.
+struct QTileIter {
+  int32_t kstep, i, qt, qtiles, band;
+  int32_t j, P, rb, re, layout, causal, kv0;
+  __device__ bool step_rank() {
+    while (++kstep < P) {
+      i = ring_rank(j, kstep, P);
+      if (i < rb || i >= re) continue;
+      const BlockRel rel = block_relation(layout, causal, i, j);
+      if (rel.kind == kNone) continue;
+      band = (rel.kind == kAll) ? kBandAllKeys : rel.band;
+      int32_t a_first = (rel.kind == kAll) ? 0 : kv0 - band;  // first row any key can see
+      if (a_first < 0) a_first = 0;
+      qt = a_first / kQm;
+      if (qt < qtiles) return true;
+    }
+    return false;
+  }
+  __device__ bool next() { return (++qt < qtiles) ? true : step_rank(); }
+};
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdParams p) {
+__device__ __forceinline__ void load_qtile(QTileRegs<D>& r, const BwdParams& p, const QTileIter& it,
+                                           int32_t b, int32_t h, int tid) {
+  using T = QTileRegs<D>;
+  const int32_t ri = it.i - p.rank_begin;
+  const int32_t q0 = it.qt * kQm;
+  const int32_t Bb = (int32_t)p.Bb;
+  const __bf16* qb = reinterpret_cast<const __bf16*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
+  const __bf16* ob = reinterpret_cast<const __bf16*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch +
+                     h * p.dout.s_head;
+  const int c = tid % T::CR;
+  const int r0 = tid / T::CR;
+#pragma unroll
+  for (int k = 0; k < T::NP; ++k) {
+    const int32_t x = q0 + r0 + T::RPP * k;
+    u32x4 vq = {0u, 0u, 0u, 0u}, vo = {0u, 0u, 0u, 0u};
+    if (x < Bb) {
+      vq = *reinterpret_cast<const u32x4*>(qb + (int64_t)x * p.q.s_tok + 8 * c);
+      vo = *reinterpret_cast<const u32x4*>(ob + (int64_t)x * p.dout.s_tok + 8 * c);
+    }
+    r.q[k] = vq;
+    r.o[k] = vo;
+  }
+  const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
+  r.lse2 = 0.0f;
+  r.dsum = 0.0f;
+  if (tid < kQm) {
+    const int32_t x = q0 + tid;
+    if (x < Bb) r.lse2 = p.lse[srow + x] * kLog2e;
+  } else if (tid < 2 * kQm) {
+    const int32_t x = q0 + tid - kQm;
+    if (x < Bb) r.dsum = p.dsum[srow + x];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_qtile(const QTileRegs<D>& r, __bf16* lds, float* f32s, int stage, int tid) {
+  using T = QTileRegs<D>;
+  using L = BwdLds<D>;
+  __bf16* qs = lds + L::Q + stage * kQm * L::RS;
+  __bf16* os = lds + L::DO + stage * kQm * L::RS;
+  const int c = tid % T::CR;
+  const int r0 = tid / T::CR;
+#pragma unroll
+  for (int k = 0; k < T::NP; ++k) {
+    const int row = r0 + T::RPP * k;
+    *reinterpret_cast<u32x4*>(qs + tile_off<D>(row, 8 * c)) = r.q[k];
+    *reinterpret_cast<u32x4*>(os + tile_off<D>(row, 8 * c)) = r.o[k];
+  }
+  if (tid < kQm)
+    f32s[stage * kQm + tid] = r.lse2;
+  else if (tid < 2 * kQm)
+    f32s[2 * kQm + stage * kQm + tid - kQm] = r.dsum;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   using L = BwdLds<D>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __bf16* lds = reinterpret_cast<__bf16*>(smem_raw);
-  float* lse_s = reinterpret_cast<float*>(smem_raw + L::F32_OFF);
-  float* dsum_s = lse_s + kQm;
+  float* f32s = reinterpret_cast<float*>(smem_raw + L::F32_OFF);  // lse2[2][64], dsum[2][64]
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
   const int n = lane % 32;
   const int hf = lane / 32;
+  const int grp = (lane / 16) % 2;
+  const int j16 = lane % 16;
+  const int kg = wave % 4;
+  const int qh = wave / 4;
 
   const int32_t BH = p.B * p.H;
   const int32_t tiles = (int32_t)((p.Bb + kKn - 1) / kKn);
@@ -142,28 +177,33 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdParams p) {
   const int32_t h = bh % p.H;
   int32_t j, tile;
   kv_tile_of(p, id / BH, tiles, &j, &tile);
-  const int64_t kv0 = (int64_t)tile * kKn;
-  const int64_t kw = kv0 + 32 * wave;  // the wave's first key
-  const int64_t key = kw + n;          // this lane's key
+  const int32_t Bb = (int32_t)p.Bb;
+  const int32_t kv0 = tile * kKn;
+  const int32_t kw = kv0 + 32 * kg;  // first key of this wave
+  const int32_t key = kw + n;        // this lane's key
 
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch +
-                        h * p.k.s_head;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch +
-                        h * p.v.s_head;
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // K and V of the tile, once
+  {
+    constexpr int CR = D / 8, RPP = kThreads / CR;
+    const int c = tid % CR;
+    const int r0 = tid / CR;
+    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + h * p.k.s_head;
+    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + h * p.v.s_head;
 #pragma unroll
-  for (int ss = 0; ss < D / 16; ++ss) {
-    u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (key < p.Bb) {
-      kv = *reinterpret_cast<const u32x4*>(kbase + key * p.k.s_tok + 16 * ss + 8 * hf);
-      vv = *reinterpret_cast<const u32x4*>(vbase + key * p.v.s_tok + 16 * ss + 8 * hf);
+    for (int k = 0; k < kKn / RPP; ++k) {
+      const int r = r0 + RPP * k;
+      const int32_t x = kv0 + r;
+      u32x4 vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (x < Bb) {
+        vk = *reinterpret_cast<const u32x4*>(kb + (int64_t)x * p.k.s_tok + 8 * c);
+        vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)x * p.v.s_tok + 8 * c);
+      }
+      *reinterpret_cast<u32x4*>(lds + L::K + tile_off<D>(r, 8 * c)) = vk;
+      *reinterpret_cast<u32x4*>(lds + L::V + tile_off<D>(r, 8 * c)) = vv;
     }
-    kreg[ss] = __builtin_bit_cast(bf16x8, kv);
-    vreg[ss] = __builtin_bit_cast(bf16x8, vv);
   }
-  stage_transposed<D, kKn>(lds + L::K_T, L::KTS, kbase, p.k.s_tok, kv0, p.Bb, tid);
 
-  f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: [dt][i] = feature 32dt + 8(i/4) + 4hf + i%4
+  f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: [dt][i] = feature 32dt + 8(i/4) + 4hf + i%4, key n
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
     f32x16 z = {};
@@ -171,139 +211,122 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     dv[dt] = z;
   }
   const float c2 = p.scale_log2;
-  const int32_t qtiles = (int32_t)((p.Bb + kQm - 1) / kQm);
 
-  for (int32_t kstep = 0; kstep < p.P; ++kstep) {
-    const int32_t i = ring_rank(j, kstep, p.P);
-    if (i < p.rank_begin || i >= p.rank_begin + p.n_ranks) continue;
-    const int32_t ri = i - p.rank_begin;
-    const BlockRel rel = block_relation(p.layout, p.causal, i, j);
-    if (rel.kind == kNone) continue;
-    const int32_t band = (rel.kind == kAll) ? kBandAll : rel.band;
-    // first query row any key of the tile can see: a >= kv0 - band
-    int64_t a_first = (rel.kind == kAll) ? 0 : kv0 - band;
-    if (a_first < 0) a_first = 0;
-    const int32_t qt0 = (int32_t)(a_first / kQm);
-    const __bf16* qbase = reinterpret_cast<const __bf16*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch +
-                          h * p.q.s_head;
-    const __bf16* dobase = reinterpret_cast<const __bf16*>(p.dout.ptr) + ri * p.dout.s_blk +
-                           b * p.dout.s_batch + h * p.dout.s_head;
-    const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
-    for (int32_t qt = qt0; qt < qtiles; ++qt) {
-      const int64_t q0 = (int64_t)qt * kQm;
-      __syncthreads();  // previous tile's LDS reads are done
-      stage_rows<D, kQm>(lds + L::Q_ROW, L::RS, qbase, p.q.s_tok, q0, p.Bb, tid);
-      stage_rows<D, kQm>(lds + L::DO_ROW, L::RS, dobase, p.dout.s_tok, q0, p.Bb, tid);
-      stage_transposed<D, kQm>(lds + L::Q_T, L::TS, qbase, p.q.s_tok, q0, p.Bb, tid);
-      stage_transposed<D, kQm>(lds + L::DO_T, L::TS, dobase, p.dout.s_tok, q0, p.Bb, tid);
-      if (tid < kQm) {
-        const int64_t a = q0 + tid;
-        lse_s[tid] = (a < p.Bb) ? p.lse[srow + a] * kLog2e : 0.0f;
-        dsum_s[tid] = (a < p.Bb) ? p.dsum[srow + a] : 0.0f;
+  QTileIter cur;
+  cur.kstep = -1;
+  cur.qtiles = (Bb + kQm - 1) / kQm;
+  cur.j = j;
+  cur.P = p.P;
+  cur.rb = p.rank_begin;
+  cur.re = p.rank_begin + p.n_ranks;
+  cur.layout = p.layout;
+  cur.causal = p.causal;
+  cur.kv0 = kv0;
+  const bool any = cur.step_rank();
+  QTileRegs<D> regs;
+  if (any) {
+    load_qtile<D>(regs, p, cur, b, h, tid);
+    store_qtile<D>(regs, lds, f32s, 0, tid);
+  }
+  int stage = 0;
+  while (any) {
+    __syncthreads();  // this Q/dO stage is in LDS; the other one is no longer read
+    QTileIter nx = cur;
+    const bool more = nx.next();
+    if (more) load_qtile<D>(regs, p, nx, b, h, tid);  // in flight during the compute below
+
+    const int32_t band = cur.band;
+    const int32_t q0 = cur.qt * kQm;
+    const int32_t qw = q0 + 32 * qh;  // first row of this wave
+    const __bf16* qs = lds + L::Q + stage * kQm * L::RS;
+    const __bf16* os = lds + L::DO + stage * kQm * L::RS;
+    const float* lse_s = f32s + stage * kQm;
+    const float* dsum_s = f32s + 2 * kQm + stage * kQm;
+    const bool dead = (kw >= Bb) || (qw >= Bb) || (kw - (qw + 31) > band);
+    if (!dead) {
+      const bool need_mask = (kw + 31 - qw > band) || (qw + 32 > Bb) || (kw + 32 > Bb);
+      // row operands: (row, 8hf) + 16 ss; the padded layout keeps that affine
+      const int qoff = tile_off<D>(32 * qh + n, 8 * hf);
+      const int koff = tile_off<D>(32 * kg + n, 8 * hf);
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + qoff + 16 * ss);
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(lds + L::K + koff + 16 * ss);
+        s = mfma32(qa, kb, s);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(os + qoff + 16 * ss);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(lds + L::V + koff + 16 * ss);
+        dp = mfma32(oa, vb, dp);
       }
-      __syncthreads();
-
-      const bool wave_dead = (kw >= p.Bb) || (kw - (q0 + kQm - 1) > (int64_t)band);
-      const bool need_mask = (kw + 31 - q0 > (int64_t)band) || (q0 + kQm > p.Bb) || (kw + 32 > p.Bb);
-      __bf16* ds_s = lds + L::DS;
-      if (wave_dead) {
+      // lane (hf, n): key n against rows 8(i/4) + 4hf + i%4 of the wave's 32
+      bf16x8 pb[2], dsb[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+      for (int g = 0; g < 4; ++g) {
+        const int qr0 = 32 * qh + 8 * g + 4 * hf;  // row within the 64-row tile
+        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qr0);
+        const float4 d4 = *reinterpret_cast<const float4*>(dsum_s + qr0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-          for (int i4 = 0; i4 < 16; ++i4) {
-            const int qr = 32 * mt + 8 * (i4 / 4) + 4 * hf + (i4 % 4);
-            ds_s[qr * L::DSS + 32 * wave + n] = (__bf16)0.0f;
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          float pv = fexp2(fmaf(s[i], c2, -lv[e]));
+          if (need_mask) {
+            const int32_t a = q0 + qr0 + e;
+            if (key - a > band || a >= Bb || key >= Bb) pv = 0.0f;
           }
-      } else {
-        f32x16 s[2], dp[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          f32x16 z = {};
-          s[mt] = z;
-          dp[mt] = z;
-#pragma unroll
-          for (int ss = 0; ss < D / 16; ++ss) {
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(lds + L::Q_ROW + (32 * mt + n) * L::RS + 16 * ss + 8 * hf);
-            const bf16x8 oa = *reinterpret_cast<const bf16x8*>(lds + L::DO_ROW + (32 * mt + n) * L::RS + 16 * ss + 8 * hf);
-            s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[ss], s[mt], 0, 0, 0);
-            dp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[ss], dp[mt], 0, 0, 0);
-          }
-        }
-        bf16x8 pb[4], dsb[4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int qr0 = 32 * mt + 8 * g4 + 4 * hf;
-            const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qr0);
-            const float4 d4 = *reinterpret_cast<const float4*>(dsum_s + qr0);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i4 = 4 * g4 + e;
-              float pv = fexp2(fmaf(s[mt][i4], c2, -lv[e]));
-              if (need_mask) {
-                const int64_t a = q0 + qr0 + e;
-                if (key - a > (int64_t)band || a >= p.Bb || key >= p.Bb) pv = 0.0f;
-              }
-              const float dsv = pv * (dp[mt][i4] - dvv[e]);
-              pb[2 * mt + i4 / 8][i4 % 8] = (__bf16)pv;
-              const __bf16 dsh = (__bf16)dsv;
-              dsb[2 * mt + i4 / 8][i4 % 8] = dsh;
-              ds_s[(qr0 + e) * L::DSS + 32 * wave + n] = dsh;
-            }
-          }
-        // dV^T += dO^T P, dK^T += Q^T dS (contraction over the 64 query rows)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int kq = 0; kq < 4; ++kq) {
-            const __bf16* orow = lds + L::DO_T + (32 * dt + n) * L::TS + 16 * kq + 4 * hf;
-            const __bf16* qrow = lds + L::Q_T + (32 * dt + n) * L::TS + 16 * kq + 4 * hf;
-            const bf16x8 ot = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(orow),
-                                                      *reinterpret_cast<const bf16x4*>(orow + 8), 0, 1, 2,
-                                                      3, 4, 5, 6, 7);
-            const bf16x8 qtv = __builtin_shufflevector(*reinterpret_cast<const bf16x4*>(qrow),
-                                                       *reinterpret_cast<const bf16x4*>(qrow + 8), 0, 1, 2,
-                                                       3, 4, 5, 6, 7);
-            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot, pb[kq], dv[dt], 0, 0, 0);
-            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtv, dsb[kq], dk[dt], 0, 0, 0);
-          }
-      }
-      __syncthreads();  // dS of all 128 keys is in LDS
-
-      // dQ[q][d] += sum over the tile's keys dS[q][key] K[key][d]
-      constexpr int NT = 2 * (D / 32);  // 32x32 output tiles
-      constexpr int PER_WAVE = NT / 4;
-#pragma unroll
-      for (int u = 0; u < PER_WAVE; ++u) {
-        const int t = wave * PER_WAVE + u;
-        const int mt = t / (D / 32);
-        const int dt = t % (D / 32);
-        f32x16 acc = {};
-#pragma unroll
-        for (int kk = 0; kk < kKn / 16; ++kk) {
-          const bf16x8 da = *reinterpret_cast<const bf16x8*>(ds_s + (32 * mt + n) * L::DSS + 16 * kk + 8 * hf);
-          const bf16x8 kt = *reinterpret_cast<const bf16x8*>(lds + L::K_T + (32 * dt + n) * L::KTS + 16 * kk + 8 * hf);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, kt, acc, 0, 0, 0);
-        }
-        // acc lane (hf, n): feature 32dt + n, query rows 32mt + 8(i/4) + 4hf + i%4
-#pragma unroll
-        for (int i4 = 0; i4 < 16; ++i4) {
-          const int64_t a = q0 + 32 * mt + 8 * (i4 / 4) + 4 * hf + (i4 % 4);
-          if (a < p.Bb) unsafeAtomicAdd(p.dq_acc + (srow + a) * D + 32 * dt + n, acc[i4]);
+          const float dsv = pv * (dp[i] - dd[e]);
+          pb[g / 2][4 * (g % 2) + e] = (__bf16)pv;
+          dsb[g / 2][4 * (g % 2) + e] = (__bf16)dsv;
         }
       }
+      // dV^T += dO^T P, dK^T += Q^T dS: contraction over the wave's 32 rows;
+      // transposing reads at (row, col) + 16kq rows (+8) + 32dt columns
+      const int troff = opaque(tile_off<D>(32 * qh + 4 * hf + j16 / 4, 16 * grp + 4 * (j16 % 4)));
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          const int o1 = troff + 16 * kq * L::RS + 32 * dt;
+          const int o2 = o1 + 8 * L::RS;
+          const bf16x8 ot = cat(tr_read(os + o1), tr_read(os + o2));
+          const bf16x8 qt = cat(tr_read(qs + o1), tr_read(qs + o2));
+          dv[dt] = mfma32(ot, pb[kq], dv[dt]);
+          dk[dt] = mfma32(qt, dsb[kq], dk[dt]);
+        }
     }
+    if (!more) break;
+    store_qtile<D>(regs, lds, f32s, stage ^ 1, tid);  // read last in the previous iteration
+    cur = nx;
+    stage ^= 1;
   }
 
-  // write dK = scale * dK^T^T and dV for this lane's key
-  if (key >= p.Bb) return;
+  // the two waves of a key group add their partial dK^T, then dV^T
+  float* red = reinterpret_cast<float*>(smem_raw);  // [4 key groups][D/32*16 values][64 lanes]
+  constexpr int NV = (D / 32) * 16;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    f32x16* acc = which == 0 ? dk : dv;
+    __syncthreads();  // the LDS area is free
+    if (qh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[(kg * NV + dt * 16 + i) * 64 + lane] = acc[dt][i];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] += red[(kg * NV + dt * 16 + i) * 64 + lane];
+    }
+  }
+  if (qh == 1 || key >= Bb) return;
   __bf16* dkrow = reinterpret_cast<__bf16*>(p.dk.ptr) + j * p.dk.s_blk + b * p.dk.s_batch +
-                  key * p.dk.s_tok + h * p.dk.s_head;
+                  (int64_t)key * p.dk.s_tok + h * p.dk.s_head;
   __bf16* dvrow = reinterpret_cast<__bf16*>(p.dv.ptr) + j * p.dv.s_blk + b * p.dv.s_batch +
-                  key * p.dv.s_tok + h * p.dv.s_head;
+                  (int64_t)key * p.dv.s_tok + h * p.dv.s_head;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -319,9 +342,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_bf16_kernel(BwdParams p) {
     }
 }
 
+
 // ---------------------------------------------------------------- fp32 path
 // Plain VALU kernel for float32: one lane per key (64 keys per workgroup),
-// dK/dV of that key in registers, query tiles of 32 rows staged in LDS.
+// dK/dV of that key in registers, query tiles of 32 rows staged in LDS (dQ:
+// dq_f32_kernel).
 constexpr int kF32Keys = 64;
 constexpr int kF32Rows = 32;
 
@@ -332,15 +357,14 @@ struct BwdF32Lds {
   static constexpr int VS = KS + kF32Keys * S;
   static constexpr int QS = VS + kF32Keys * S;
   static constexpr int OS = QS + kF32Rows * S;
-  static constexpr int DS = OS + kF32Rows * S;
-  static constexpr int LSE = DS + kF32Rows * (kF32Keys + 1);
+  static constexpr int LSE = OS + kF32Rows * S;
   static constexpr int DSUM = LSE + kF32Rows;
   static constexpr int FLOATS = DSUM + kF32Rows;
   static constexpr int BYTES = FLOATS * 4;
 };
 
 template <int D>
-__global__ __launch_bounds__(kF32Keys) void bwd_f32_kernel(BwdParams p) {
+__global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
   using L = BwdF32Lds<D>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* sm = reinterpret_cast<float*>(smem_raw);
@@ -348,7 +372,6 @@ __global__ __launch_bounds__(kF32Keys) void bwd_f32_kernel(BwdParams p) {
   float* vs = sm + L::VS;
   float* qs = sm + L::QS;
   float* os = sm + L::OS;
-  float* dss = sm + L::DS;
   float* lse_s = sm + L::LSE;
   float* dsum_s = sm + L::DSUM;
   const int tid = threadIdx.x;
@@ -384,7 +407,7 @@ __global__ __launch_bounds__(kF32Keys) void bwd_f32_kernel(BwdParams p) {
     const int32_t ri = i - p.rank_begin;
     const BlockRel rel = block_relation(p.layout, p.causal, i, j);
     if (rel.kind == kNone) continue;
-    const int32_t band = (rel.kind == kAll) ? kBandAll : rel.band;
+    const int32_t band = (rel.kind == kAll) ? kBandAllKeys : rel.band;
     int64_t a_first = (rel.kind == kAll) ? 0 : kv0 - band;
     if (a_first < 0) a_first = 0;
     const float* qbase = reinterpret_cast<const float*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
@@ -421,21 +444,6 @@ __global__ __launch_bounds__(kF32Keys) void bwd_f32_kernel(BwdParams p) {
           dv[e] = fmaf(pv, os[r * L::S + e], dv[e]);
           dk[e] = fmaf(dsv, qs[r * L::S + e], dk[e]);
         }
-        dss[r * (kF32Keys + 1) + tid] = dsv;
-      }
-      __syncthreads();
-      // dQ rows of the tile: lane -> (row tid % 32, half of the features)
-      {
-        const int r = tid % kF32Rows;
-        const int half = tid / kF32Rows;
-        const int64_t a = q0 + r;
-        if (a < p.Bb) {
-          for (int e = half * (D / 2); e < (half + 1) * (D / 2); ++e) {
-            float acc = 0.0f;
-            for (int kk = 0; kk < kF32Keys; ++kk) acc = fmaf(dss[r * (kF32Keys + 1) + kk], ks[kk * L::S + e], acc);
-            unsafeAtomicAdd(p.dq_acc + (srow + a) * D + e, acc);
-          }
-        }
       }
     }
   }
@@ -459,16 +467,16 @@ hipError_t launch_dyn(K kernel, int64_t grid, int threads, int bytes, hipStream_
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
+hipError_t launch_dkdv_bf16(const BwdParams& p, hipStream_t s) {
   const int64_t grid = ((p.Bb + kKn - 1) / kKn) * (int64_t)p.P * p.B * p.H;
-  if (p.D == 128) return launch_dyn(bwd_bf16_kernel<128>, grid, kThreads, BwdLds<128>::BYTES, s, p);
-  return launch_dyn(bwd_bf16_kernel<64>, grid, kThreads, BwdLds<64>::BYTES, s, p);
+  if (p.D == 128) return launch_dyn(dkdv_bf16_kernel<128>, grid, kThreads, BwdLds<128>::BYTES, s, p);
+  return launch_dyn(dkdv_bf16_kernel<64>, grid, kThreads, BwdLds<64>::BYTES, s, p);
 }
 
-hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s) {
+hipError_t launch_dkdv_f32(const BwdParams& p, hipStream_t s) {
   const int64_t grid = ((p.Bb + kF32Keys - 1) / kF32Keys) * (int64_t)p.P * p.B * p.H;
-  if (p.D == 128) return launch_dyn(bwd_f32_kernel<128>, grid, kF32Keys, BwdF32Lds<128>::BYTES, s, p);
-  return launch_dyn(bwd_f32_kernel<64>, grid, kF32Keys, BwdF32Lds<64>::BYTES, s, p);
+  if (p.D == 128) return launch_dyn(dkdv_f32_kernel<128>, grid, kF32Keys, BwdF32Lds<128>::BYTES, s, p);
+  return launch_dyn(dkdv_f32_kernel<64>, grid, kF32Keys, BwdF32Lds<64>::BYTES, s, p);
 }
 
 }  // namespace ra

@@ -1,0 +1,282 @@
+// ra_dq.hip — the dQ half of the backward (gfx950).
+//
+// "Ring Attention 論文分析" (blog), section "逆伝播での KV 再循環": with P
+// recomputed from the saved log-sum-exp, dS = P * (dP - D), dP = dO V^T and
+// D = rowsum(dO * O), the query gradient is dQ = scale * dS K. Here a
+// workgroup owns 256 query rows and walks the KV blocks in ring order exactly
+// as the forward does (ra_kvwalk.h), accumulating dQ of its rows on chip — no
+// atomics, so the result does not depend on scheduling. The dK/dV half runs
+// in ra_bwd.hip with the roles of queries and keys swapped.
+//
+// bf16 path, per wave (32 query rows): S^T = K Q^T and dP^T = V dO^T leave
+// lane (h, n) with query n against 16 keys; dS^T stays in registers as the B
+// operand of dQ^T += K^T dS^T, whose K^T operand comes from transposing reads
+// of the row-major K tile.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ra_internal.h"
+#include "ra_kvwalk.h"
+#include "ra_lds.h"
+#include "ra_schedule.h"
+
+namespace ra {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int D>
+__global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
+  using L = KvLds<D>;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __bf16* lds = reinterpret_cast<__bf16*>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int n = lane % 32;
+  const int hf = lane / 32;
+  const int grp = (lane / 16) % 2;
+  const int j16 = lane % 16;
+
+  const int32_t BH = p.B * p.H;
+  const int32_t Bb = (int32_t)p.Bb;
+  const int32_t tiles = (Bb + kQTm - 1) / kQTm;
+  const int64_t id = blockIdx.x;
+  const int32_t bh = (int32_t)(id % BH);
+  const int32_t b = bh / p.H;
+  const int32_t h = bh % p.H;
+  int32_t ri, tile;
+  query_tile_of(p.causal, p.layout, p.n_ranks, id / BH, tiles, &ri, &tile);
+  const int32_t i = p.rank_begin + ri;
+  const int32_t a0 = tile * kQTm;
+  const int32_t aw = a0 + 32 * wave;
+  const int32_t a = aw + n;
+  const int32_t a_hi = (a0 + kQTm - 1 < Bb - 1) ? a0 + kQTm - 1 : Bb - 1;
+
+  // this lane's query and output-gradient rows, as B operands
+  const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch +
+                       (int64_t)a * p.q.s_tok + h * p.q.s_head;
+  const __bf16* orow = reinterpret_cast<const __bf16*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch +
+                       (int64_t)a * p.dout.s_tok + h * p.dout.s_head;
+  bf16x8 qreg[D / 16], oreg[D / 16];
+#pragma unroll
+  for (int ss = 0; ss < D / 16; ++ss) {
+    u32x4 vq = {0u, 0u, 0u, 0u}, vo = {0u, 0u, 0u, 0u};
+    if (a < Bb) {
+      vq = *reinterpret_cast<const u32x4*>(qrow + 16 * ss + 8 * hf);
+      vo = *reinterpret_cast<const u32x4*>(orow + 16 * ss + 8 * hf);
+    }
+    qreg[ss] = __builtin_bit_cast(bf16x8, vq);
+    oreg[ss] = __builtin_bit_cast(bf16x8, vo);
+  }
+  const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
+  const float lse2 = (a < Bb) ? p.lse[srow + a] * kLog2e : 0.0f;
+  const float dsum = (a < Bb) ? p.dsum[srow + a] : 0.0f;
+
+  f32x16 acc[D / 32];  // dQ^T: feature 32dt + 8(i/4) + 4hf + i%4, query n
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    f32x16 z = {};
+    acc[dt] = z;
+  }
+
+  KvIter it;
+  it.kstep = -1;
+  it.nsteps = p.P;
+  it.single_block = -1;
+  it.i = i;
+  it.P = p.P;
+  it.layout = p.layout;
+  it.causal = p.causal;
+  it.a_hi = a_hi;
+  it.Bb = Bb;
+  auto kv_base = [&](const Seq& sq, int32_t blk) {
+    return reinterpret_cast<const __bf16*>(sq.ptr) + (int64_t)blk * sq.s_blk + b * sq.s_batch + h * sq.s_head;
+  };
+
+  const float c2 = p.scale_log2;
+  bool any = it.next_block();
+  KvRegs<D> regs;
+  if (any) {
+    load_kv<D>(regs, kv_base(p.k, it.j), kv_base(p.v, it.j), p.k.s_tok, p.v.s_tok, 0, Bb, tid);
+    store_kv<D>(regs, lds, tid);
+  }
+  int stage = 0;
+  while (any) {
+    __syncthreads();  // this stage is in LDS; the other one is no longer read
+    KvIter nx = it;
+    const bool more = nx.next();
+    if (more)
+      load_kv<D>(regs, kv_base(p.k, nx.j), kv_base(p.v, nx.j), p.k.s_tok, p.v.s_tok, nx.t * kKvTn, Bb, tid);
+
+    const int32_t band = it.band;
+    const int32_t b0 = it.t * kKvTn;
+    const __bf16* ks = lds + stage * L::STAGE;
+    const __bf16* vs = ks + L::TILE;
+    const bool dead = (aw >= Bb) || (b0 - (aw + 31) > band);
+    if (!dead) {
+      const bool need_mask = (b0 + kKvTn - 1 - aw > band) || (b0 + kKvTn > Bb);
+      const int koff = tile_off<D>(n, 8 * hf);
+      const int toff = opaque(tile_off<D>(4 * hf + j16 / 4, 16 * grp + 4 * (j16 % 4)));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {  // 32-key halves of the tile
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ss = 0; ss < D / 16; ++ss) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff + 32 * t * L::RS + 16 * ss);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + koff + 32 * t * L::RS + 16 * ss);
+          s = mfma32(kf, qreg[ss], s);
+          dp = mfma32(vf, oreg[ss], dp);
+        }
+        // lane (hf, n): query n against keys 32t + 8(e/4) + 4hf + e%4
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float pv = fexp2(fmaf(s[e], c2, -lse2));
+          if (need_mask) {
+            const int32_t kb = b0 + 32 * t + 8 * (e / 4) + 4 * hf + (e % 4);
+            if (kb - a > band || kb >= Bb) pv = 0.0f;
+          }
+          dsb[e / 8][e % 8] = (__bf16)(pv * (dp[e] - dsum));
+        }
+        // dQ^T += K^T dS^T; dS element e of k-step kk = 2t + u is key 16kk + 8(e/4) + 4hf + e%4
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int o1 = toff + 16 * (2 * t + u) * L::RS + 32 * dt;
+            const bf16x8 kt = cat(tr_read(ks + o1), tr_read(ks + o1 + 8 * L::RS));
+            acc[dt] = mfma32(kt, dsb[u], acc[dt]);
+          }
+      }
+    }
+    if (!more) break;
+    store_kv<D>(regs, lds + (stage ^ 1) * L::STAGE, tid);
+    it = nx;
+    stage ^= 1;
+  }
+
+  if (a >= Bb) return;
+  __bf16* drow = reinterpret_cast<__bf16*>(p.dq.ptr) + ri * p.dq.s_blk + b * p.dq.s_batch +
+                 (int64_t)a * p.dq.s_tok + h * p.dq.s_head;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[dt][4 * g4 + e] * p.scale);
+      *reinterpret_cast<bf16x4*>(drow + 32 * dt + 8 * g4 + 4 * hf) = w;
+    }
+}
+
+// ---------------------------------------------------------------- fp32 path
+// Plain VALU kernel for float32: one lane per query row, KV tiles staged in
+// LDS and read as broadcasts; same ring walk and masks as the forward.
+constexpr int kF32Rows = 64;
+
+template <int D>
+__global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
+  constexpr int TN = 2048 / D;  // keys per staged tile: 16 KiB of LDS for K and V
+  __shared__ float ks[TN][D];
+  __shared__ float vs[TN][D];
+  const int tid = threadIdx.x;
+  const int32_t BH = p.B * p.H;
+  const int32_t Bb = (int32_t)p.Bb;
+  const int32_t tiles = (Bb + kF32Rows - 1) / kF32Rows;
+  const int64_t id = blockIdx.x;
+  const int32_t bh = (int32_t)(id % BH);
+  const int32_t b = bh / p.H;
+  const int32_t h = bh % p.H;
+  int32_t ri, tile;
+  query_tile_of(p.causal, p.layout, p.n_ranks, id / BH, tiles, &ri, &tile);
+  const int32_t i = p.rank_begin + ri;
+  const int32_t a0 = tile * kF32Rows;
+  const int32_t a = a0 + tid;
+  const int32_t a_hi = (a0 + kF32Rows - 1 < Bb - 1) ? a0 + kF32Rows - 1 : Bb - 1;
+  const bool live = a < Bb;
+  const float* qrow = reinterpret_cast<const float*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch +
+                      (int64_t)a * p.q.s_tok + h * p.q.s_head;
+  const float* orow = reinterpret_cast<const float*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch +
+                      (int64_t)a * p.dout.s_tok + h * p.dout.s_head;
+  float qv[D], ov[D], dq[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qv[e] = live ? qrow[e] : 0.0f;
+    ov[e] = live ? orow[e] : 0.0f;
+    dq[e] = 0.0f;
+  }
+  const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
+  const float lse2 = live ? p.lse[srow + a] * kLog2e : 0.0f;
+  const float dsum = live ? p.dsum[srow + a] : 0.0f;
+  const float c2 = p.scale_log2;
+  for (int32_t kstep = 0; kstep < p.P; ++kstep) {
+    const int32_t j = ring_block(i, kstep, p.P);
+    const BlockRel rel = block_relation(p.layout, p.causal, i, j);
+    const int64_t extent = visible_key_extent(rel, a_hi, p.Bb);
+    if (extent <= 0) continue;
+    const int32_t band = (rel.kind == kAll) ? kBandAll : rel.band;
+    const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + (int64_t)j * p.k.s_blk + b * p.k.s_batch +
+                         h * p.k.s_head;
+    const float* vbase = reinterpret_cast<const float*>(p.v.ptr) + (int64_t)j * p.v.s_blk + b * p.v.s_batch +
+                         h * p.v.s_head;
+    for (int32_t b0 = 0; b0 < extent; b0 += TN) {
+      __syncthreads();
+      for (int idx = tid; idx < TN * D; idx += kF32Rows) {
+        const int r = idx / D, e = idx % D;
+        const int32_t x = b0 + r;
+        ks[r][e] = (x < Bb) ? kbase[(int64_t)x * p.k.s_tok + e] : 0.0f;
+        vs[r][e] = (x < Bb) ? vbase[(int64_t)x * p.v.s_tok + e] : 0.0f;
+      }
+      __syncthreads();
+      if (!live) continue;
+      for (int u = 0; u < TN; ++u) {
+        const int32_t kb = b0 + u;
+        float s = 0.0f, dpv = 0.0f;
+#pragma unroll
+        for (int e = 0; e < D; ++e) {
+          s = fmaf(qv[e], ks[u][e], s);
+          dpv = fmaf(ov[e], vs[u][e], dpv);
+        }
+        const bool vis = kb - a <= band && kb < Bb;
+        const float pv = vis ? fexp2(fmaf(s, c2, -lse2)) : 0.0f;
+        const float dsv = pv * (dpv - dsum);
+#pragma unroll
+        for (int e = 0; e < D; ++e) dq[e] = fmaf(dsv, ks[u][e], dq[e]);
+      }
+    }
+  }
+  if (!live) return;
+  float* drow = reinterpret_cast<float*>(p.dq.ptr) + ri * p.dq.s_blk + b * p.dq.s_batch + (int64_t)a * p.dq.s_tok +
+                h * p.dq.s_head;
+#pragma unroll
+  for (int e = 0; e < D; ++e) drow[e] = dq[e] * p.scale;
+}
+
+}  // namespace
+
+hipError_t launch_dq_bf16(const BwdParams& p, hipStream_t s) {
+  const int64_t grid = ((p.Bb + kQTm - 1) / kQTm) * (int64_t)p.n_ranks * p.B * p.H;
+  if (grid <= 0) return hipSuccess;
+  if (p.D == 128) {
+    hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3((uint32_t)grid), dim3(kQThreads), KvLds<128>::BYTES, s, p);
+  } else {
+    hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3((uint32_t)grid), dim3(kQThreads), KvLds<64>::BYTES, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_f32(const BwdParams& p, hipStream_t s) {
+  const int64_t grid = ((p.Bb + kF32Rows - 1) / kF32Rows) * (int64_t)p.n_ranks * p.B * p.H;
+  if (grid <= 0) return hipSuccess;
+  if (p.D == 128) {
+    hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((uint32_t)grid), dim3(kF32Rows), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((uint32_t)grid), dim3(kF32Rows), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -32,12 +32,11 @@ struct FwdParams {
   int32_t mode, step_block, first, last;
 };
 
-// Backward launch (whole ring for ranks in range).
+// Backward launches (whole ring for ranks in range).
 struct BwdParams {
   Seq q, k, v, o, dout, dq, dk, dv;
   const float* lse;  // [n_ranks][B][H][Bb]
   float* dsum;       // workspace: D = rowsum(dO * O), [n_ranks][B][H][Bb]
-  float* dq_acc;     // workspace: fp32 [n_ranks][B][H][Bb][D] (unscaled)
   int32_t B, H, D, P;
   int64_t Bb;
   int32_t layout, causal;
@@ -48,9 +47,10 @@ struct BwdParams {
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int32_t bf16, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
-hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
-hipError_t launch_dq_finalize(const BwdParams& p, int32_t bf16, hipStream_t s);
+hipError_t launch_dkdv_bf16(const BwdParams& p, hipStream_t s);
+hipError_t launch_dkdv_f32(const BwdParams& p, hipStream_t s);
+hipError_t launch_dq_bf16(const BwdParams& p, hipStream_t s);
+hipError_t launch_dq_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_merge_lse(int64_t rows, int32_t d, const float* oa, const float* la,
                             const float* ob, const float* lb, float* oo, float* lo,
                             hipStream_t s);

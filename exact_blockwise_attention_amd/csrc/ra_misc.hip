@@ -1,6 +1,5 @@
 // ra_misc.hip — memory-bound kernels: log-sum-exp merge of partial results,
-// the KV block receive copy, layout gathers, and the backward's row sums and
-// dQ finalisation.
+// the KV block receive copy, layout gathers, and the backward's row sums.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -96,59 +95,51 @@ __global__ __launch_bounds__(256) void layout_copy_kernel(const char* src, char*
   }
 }
 
-__device__ __forceinline__ float load_elem(const void* base, int64_t off, int32_t bf16) {
+// Eight consecutive elements of a row as floats (16 bytes of bf16, or two
+// 16-byte loads of fp32).
+__device__ __forceinline__ void load8(const void* base, int64_t off, int32_t bf16, float* out) {
   if (bf16) {
-    const uint16_t u = reinterpret_cast<const uint16_t*>(base)[off];
-    return __uint_as_float((uint32_t)u << 16);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[2 * k] = __uint_as_float(w[k] << 16);
+      out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
   }
-  return reinterpret_cast<const float*>(base)[off];
 }
 
 // D = rowsum(dO * O) per (rank, batch, head, row) ("Ring Attention 論文分析"
-// (blog), section "逆伝播での KV 再循環"), and zeroing of that row's fp32 dQ
-// accumulator. One wave per row.
+// (blog), section "逆伝播での KV 再循環"). Each lane handles 8 features; D/8
+// lanes share a row.
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p, int32_t bf16) {
-  const int lane = threadIdx.x % 64;
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
+  const int tpr = p.D / 8;  // lanes per row (16 or 8), a power of two dividing 64
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / tpr;
+  const int part = threadIdx.x % tpr;
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
-  if (row >= rows) return;
-  int64_t r = row;
-  const int64_t x = r % p.Bb;
-  r /= p.Bb;
-  const int32_t h = (int32_t)(r % p.H);
-  r /= p.H;
-  const int32_t b = (int32_t)(r % p.B);
-  const int32_t ri = (int32_t)(r / p.B);
-  const int64_t oo = ri * p.o.s_blk + b * p.o.s_batch + x * p.o.s_tok + h * p.o.s_head;
-  const int64_t od = ri * p.dout.s_blk + b * p.dout.s_batch + x * p.dout.s_tok + h * p.dout.s_head;
   float acc = 0.0f;
-  for (int e = lane; e < p.D; e += 64) acc = fmaf(load_elem(p.o.ptr, oo + e, bf16), load_elem(p.dout.ptr, od + e, bf16), acc);
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) p.dsum[row] = acc;
-  float* dqa = p.dq_acc + row * p.D;
-  for (int e = lane; e < p.D; e += 64) dqa[e] = 0.0f;
-}
-
-// dQ = scale * accumulator, cast to the problem dtype (round to nearest even).
-__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdParams p, int32_t bf16) {
-  const int64_t total = (int64_t)p.n_ranks * p.B * p.H * p.Bb * p.D;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t e = (int32_t)(idx % p.D);
-    int64_t r = idx / p.D;
+  if (row < rows) {
+    int64_t r = row;
     const int64_t x = r % p.Bb;
     r /= p.Bb;
     const int32_t h = (int32_t)(r % p.H);
     r /= p.H;
     const int32_t b = (int32_t)(r % p.B);
     const int32_t ri = (int32_t)(r / p.B);
-    const int64_t off = ri * p.dq.s_blk + b * p.dq.s_batch + x * p.dq.s_tok + h * p.dq.s_head + e;
-    const float val = p.dq_acc[idx] * p.scale;
-    if (bf16)
-      reinterpret_cast<__bf16*>(p.dq.ptr)[off] = (__bf16)val;
-    else
-      reinterpret_cast<float*>(p.dq.ptr)[off] = val;
+    const int64_t oo = ri * p.o.s_blk + b * p.o.s_batch + x * p.o.s_tok + h * p.o.s_head + 8 * part;
+    const int64_t od = ri * p.dout.s_blk + b * p.dout.s_batch + x * p.dout.s_tok + h * p.dout.s_head + 8 * part;
+    float o8[8], d8[8];
+    load8(p.o.ptr, oo, bf16, o8);
+    load8(p.dout.ptr, od, bf16, d8);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc = fmaf(o8[k], d8[k], acc);
   }
+  for (int off = tpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) p.dsum[row] = acc;
 }
 
 inline uint32_t grid_for(int64_t items, int32_t per_block) {
@@ -195,14 +186,8 @@ hipError_t launch_layout_copy(const void* src, void* dst, int32_t B, int32_t H, 
 hipError_t launch_bwd_preprocess(const BwdParams& p, int32_t bf16, hipStream_t s) {
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((uint32_t)((rows + 3) / 4)), dim3(256), 0, s, p, bf16);
-  return hipGetLastError();
-}
-
-hipError_t launch_dq_finalize(const BwdParams& p, int32_t bf16, hipStream_t s) {
-  const int64_t total = (int64_t)p.n_ranks * p.B * p.H * p.Bb * p.D;
-  if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dq_finalize_kernel, dim3(grid_for(total, 256)), dim3(256), 0, s, p, bf16);
+  const int64_t lanes = rows * (p.D / 8);
+  hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((uint32_t)((lanes + 255) / 256)), dim3(256), 0, s, p, bf16);
   return hipGetLastError();
 }
 

@@ -137,10 +137,12 @@ ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
 
 /* Backward (blog, section "逆伝播での KV 再循環"): recomputes P = exp(S - lse)
  * with the forward's mask and returns dQ, dK, dV of sum(dO * O). D =
- * rowsum(dO * O) is computed first from the given O. Each KV block visits the
- * query blocks of ranks [rank_begin, rank_end) in ring order
- * ((j + k) mod P at step k) carrying its dK/dV accumulators on chip; dQ is
- * accumulated in an fp32 workspace.
+ * rowsum(dO * O) is computed first from the given O (into the workspace).
+ * Each KV block visits the query blocks of ranks [rank_begin, rank_end) in
+ * ring order ((j + k) mod P at step k) carrying its dK/dV accumulators on
+ * chip; then each query block of the range walks the KV blocks in ring order
+ * ((i - k) mod P) carrying its dQ accumulator. No atomics: the result is
+ * deterministic.
  *   q, o, dout, dq, lse: indexed by i - rank_begin; k, v, dk, dv: absolute.
  *   dk, dv receive the contributions of the ranks in range (all P ranks:
  *   the full gradient). Blocks of dk/dv are written for every j.
@@ -152,11 +154,11 @@ ra_status ra_backward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end
                       size_t workspace_bytes, hipStream_t compute);
 
 /* One stage of ra_backward, with the same arguments (ra_backward runs stages
- * 0, 1, 2 in order on `compute`): 0 = D = rowsum(dO * O) and zeroing of the
- * dQ accumulator; 1 = the ring walk (recompute, dV, dP, dS, dQ, dK); 2 = dQ
- * scaled and cast to the problem dtype. Stage k reads what stage k-1 wrote to
- * the workspace, so they must run in order on one stream; lets a caller
- * time or interleave the stages. Unknown stage: RA_ERR_SHAPE. */
+ * 0, 1, 2 in order on `compute`): 0 = D = rowsum(dO * O) into the workspace;
+ * 1 = the key-side ring walk (recompute S and P, dP, dS; dV and dK);
+ * 2 = the query-side ring walk (recompute S, P, dP, dS; dQ). Stages 1 and 2
+ * read D, so stage 0 must complete first; lets a caller time or interleave
+ * the stages. Unknown stage: RA_ERR_SHAPE. */
 ra_status ra_backward_stage(int32_t stage, const ra_problem* pb, int32_t rank_begin,
                             int32_t rank_end, const ra_seq* q, const ra_seq* k, const ra_seq* v,
                             const ra_seq* o, const ra_seq* dout, const float* lse,

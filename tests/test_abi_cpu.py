@@ -74,7 +74,7 @@ def test_workspace_sizes():
     expect_fwd = 4 * blk + rows * 128 * 4 + rows * 4  # all multiples of 256 here
     assert ra.workspace_bytes(pb, 7, 8, True, False) == expect_fwd
     rows8 = 8 * rows
-    assert ra.workspace_bytes(pb, 0, 8, False, True) == rows8 * 4 + rows8 * 128 * 4
+    assert ra.workspace_bytes(pb, 0, 8, False, True) == rows8 * 4  # D = rowsum(dO * O)
     assert ra.workspace_bytes(problem(d=96), 0, 4, False, True) == 0  # invalid problem
 
 
