@@ -39,7 +39,28 @@ def parse():
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layout", default=None, help="workload 3: contiguous or striped")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (the library's layout copy with one block) three "
+                         "times, as the reference for HBM byte counters")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """Copy 1 GiB once per launch with ra_layout_copy (P = 1: blocked order is
+    the original order, so it is a plain copy): reads and writes 2**30 bytes."""
+    import torch
+
+    import exact_blockwise_attention_amd as ra
+    B, L, H, d = 1, 131072, 32, 128  # bf16: 2**30 bytes
+    x = torch.empty((B, L, H, d), dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    y = torch.empty((1, B, L, H, d), dtype=torch.bfloat16, device="cuda")
+    pb = ra.make_problem(B, H, d, 1, L, "contiguous", True, ra.BF16)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        ra.layout_copy_raw(pb, x.data_ptr(), y.data_ptr(), False, ra._stream_handle(None))
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": 2 ** 30, "calibrate_copy_bytes_written": 2 ** 30,
+                      "launches": 3}), flush=True)
 
 
 def pair_count(layout, causal, P, Bb, ranks):
@@ -143,6 +164,9 @@ def main():
     from exact_blockwise_attention_amd import synthetic as syn
 
     ra.library()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     w = syn.WORKLOADS[args.workload]
     layout = args.layout or w.layouts[-1]
     P, Bb, d = w.ring_size, w.block_len, w.head_dim

@@ -16,8 +16,9 @@
 // bf16 path: 8 waves; wave w owns keys 32(w%4) .. +31 of the tile and query
 // rows 32(w/4) .. +31 of each 64-row query tile (the two waves sharing keys
 // add their dK/dV partials at the end). K and V of the tile and a double
-// buffer of Q/dO tiles sit row-major in LDS; the next Q/dO tile travels
-// through registers while the current one is computed. S = Q K^T and
+// buffer of Q/dO tiles sit row-major in swizzled LDS, copied there directly
+// from global memory; the next query tile is copied while the current one is
+// computed. S = Q K^T and
 // dP = dO V^T come out with lane (h, n) holding key n against 16 query rows —
 // the operand layout dV^T += dO^T P and dK^T += Q^T dS need (contraction over
 // query rows, whose order inside an MFMA is free); the dO^T and Q^T operands
@@ -27,6 +28,7 @@
 #include <stdint.h>
 
 #include "ra_internal.h"
+#include "ra_kvwalk.h"
 #include "ra_lds.h"
 #include "ra_schedule.h"
 
@@ -43,25 +45,14 @@ constexpr int kQm = 64;   // query rows per visited tile (32 per wave)
 
 template <int D>
 struct BwdLds {
-  static constexpr int RS = PadRow<D>::RS;
-  static constexpr int K = 0;                   // [128][D] padded
-  static constexpr int V = K + kKn * RS;        // [128][D] padded
-  static constexpr int Q = V + kKn * RS;        // [2 stages][64][D] padded
-  static constexpr int DO = Q + 2 * kQm * RS;   // [2 stages][64][D] padded
-  static constexpr int BF16_ELEMS = DO + 2 * kQm * RS;
+  static constexpr int K = 0;                  // [128][D] swizzled
+  static constexpr int V = K + kKn * D;        // [128][D] swizzled
+  static constexpr int Q = V + kKn * D;        // [2 stages][64][D] swizzled
+  static constexpr int DO = Q + 2 * kQm * D;   // [2 stages][64][D] swizzled
+  static constexpr int BF16_ELEMS = DO + 2 * kQm * D;
   static constexpr int F32_OFF = BF16_ELEMS * 2;       // bytes
   static constexpr int BYTES = F32_OFF + 4 * kQm * 4;  // lse2[2][64], dsum[2][64]
   static_assert(4 * ((D / 32) * 16) * 64 * 4 <= F32_OFF, "the dK (then dV) exchange must fit in the tile area");
-};
-
-// Registers carrying the next Q/dO tile from global memory to LDS.
-template <int D>
-struct QTileRegs {
-  static constexpr int CR = D / 8;
-  static constexpr int RPP = kThreads / CR;
-  static constexpr int NP = kQm / RPP;
-  u32x4 q[NP], o[NP];
-  float lse2, dsum;
 };
 
 // Heaviest KV tiles first: early keys are seen by more query rows.
@@ -97,59 +88,23 @@ struct QTileIter {
   __device__ bool next() { return (++qt < qtiles) ? true : step_rank(); }
 };
 
+// Copies query tile `it` (Q and dO rows, lse and D) into LDS stage `stage`
+// (asynchronous; wait_dma() and a barrier make it visible).
 template <int D>
-__device__ __forceinline__ void load_qtile(QTileRegs<D>& r, const BwdParams& p, const QTileIter& it,
-                                           int32_t b, int32_t h, int tid) {
-  using T = QTileRegs<D>;
+__device__ __forceinline__ void dma_qtile(const BwdParams& p, const QTileIter& it, int32_t b, int32_t h,
+                                          __bf16* lds, float* f32s, int stage, int wave, int lane) {
+  using L = BwdLds<D>;
   const int32_t ri = it.i - p.rank_begin;
   const int32_t q0 = it.qt * kQm;
   const int32_t Bb = (int32_t)p.Bb;
   const __bf16* qb = reinterpret_cast<const __bf16*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
   const __bf16* ob = reinterpret_cast<const __bf16*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch +
                      h * p.dout.s_head;
-  const int c = tid % T::CR;
-  const int r0 = tid / T::CR;
-#pragma unroll
-  for (int k = 0; k < T::NP; ++k) {
-    const int32_t x = q0 + r0 + T::RPP * k;
-    u32x4 vq = {0u, 0u, 0u, 0u}, vo = {0u, 0u, 0u, 0u};
-    if (x < Bb) {
-      vq = *reinterpret_cast<const u32x4*>(qb + (int64_t)x * p.q.s_tok + 8 * c);
-      vo = *reinterpret_cast<const u32x4*>(ob + (int64_t)x * p.dout.s_tok + 8 * c);
-    }
-    r.q[k] = vq;
-    r.o[k] = vo;
-  }
+  dma_rows<D, kQm, kWaves>(lds + L::Q + stage * kQm * D, qb, p.q.s_tok, q0, Bb, wave, lane);
+  dma_rows<D, kQm, kWaves>(lds + L::DO + stage * kQm * D, ob, p.dout.s_tok, q0, Bb, wave, lane);
   const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
-  r.lse2 = 0.0f;
-  r.dsum = 0.0f;
-  if (tid < kQm) {
-    const int32_t x = q0 + tid;
-    if (x < Bb) r.lse2 = p.lse[srow + x] * kLog2e;
-  } else if (tid < 2 * kQm) {
-    const int32_t x = q0 + tid - kQm;
-    if (x < Bb) r.dsum = p.dsum[srow + x];
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_qtile(const QTileRegs<D>& r, __bf16* lds, float* f32s, int stage, int tid) {
-  using T = QTileRegs<D>;
-  using L = BwdLds<D>;
-  __bf16* qs = lds + L::Q + stage * kQm * L::RS;
-  __bf16* os = lds + L::DO + stage * kQm * L::RS;
-  const int c = tid % T::CR;
-  const int r0 = tid / T::CR;
-#pragma unroll
-  for (int k = 0; k < T::NP; ++k) {
-    const int row = r0 + T::RPP * k;
-    *reinterpret_cast<u32x4*>(qs + tile_off<D>(row, 8 * c)) = r.q[k];
-    *reinterpret_cast<u32x4*>(os + tile_off<D>(row, 8 * c)) = r.o[k];
-  }
-  if (tid < kQm)
-    f32s[stage * kQm + tid] = r.lse2;
-  else if (tid < 2 * kQm)
-    f32s[2 * kQm + stage * kQm + tid - kQm] = r.dsum;
+  if (wave == 0) dma_f32_64(f32s + stage * kQm, p.lse + srow, q0, Bb, lane);
+  if (wave == 1) dma_f32_64(f32s + 2 * kQm + stage * kQm, p.dsum + srow, q0, Bb, lane);
 }
 
 template <int D>
@@ -171,12 +126,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
 
   const int32_t BH = p.B * p.H;
   const int32_t tiles = (int32_t)((p.Bb + kKn - 1) / kKn);
-  const int64_t id = blockIdx.x;
-  const int32_t bh = (int32_t)(id % BH);
+  // consecutive logical indices share (batch, head, block) and take its key
+  // tiles in order (early keys are seen by more rows), so the workgroups of
+  // one XCD walk the same query tiles together and share them in L2
+  const int64_t lw = xcd_logical(blockIdx.x, (int64_t)BH * p.P * tiles);
+  const int32_t tile = (int32_t)(lw % tiles);
+  const int64_t g = lw / tiles;
+  const int32_t bh = (int32_t)(g / p.P);
+  const int32_t j = (int32_t)(g % p.P);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
-  int32_t j, tile;
-  kv_tile_of(p, id / BH, tiles, &j, &tile);
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t kv0 = tile * kKn;
   const int32_t kw = kv0 + 32 * kg;  // first key of this wave
@@ -184,23 +143,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
 
   // K and V of the tile, once
   {
-    constexpr int CR = D / 8, RPP = kThreads / CR;
-    const int c = tid % CR;
-    const int r0 = tid / CR;
     const __bf16* kb = reinterpret_cast<const __bf16*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + h * p.k.s_head;
     const __bf16* vb = reinterpret_cast<const __bf16*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + h * p.v.s_head;
-#pragma unroll
-    for (int k = 0; k < kKn / RPP; ++k) {
-      const int r = r0 + RPP * k;
-      const int32_t x = kv0 + r;
-      u32x4 vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (x < Bb) {
-        vk = *reinterpret_cast<const u32x4*>(kb + (int64_t)x * p.k.s_tok + 8 * c);
-        vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)x * p.v.s_tok + 8 * c);
-      }
-      *reinterpret_cast<u32x4*>(lds + L::K + tile_off<D>(r, 8 * c)) = vk;
-      *reinterpret_cast<u32x4*>(lds + L::V + tile_off<D>(r, 8 * c)) = vv;
-    }
+    dma_rows<D, kKn, kWaves>(lds + L::K, kb, p.k.s_tok, kv0, Bb, wave, lane);
+    dma_rows<D, kKn, kWaves>(lds + L::V, vb, p.v.s_tok, kv0, Bb, wave, lane);
   }
 
   f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: [dt][i] = feature 32dt + 8(i/4) + 4hf + i%4, key n
@@ -223,39 +169,44 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   cur.causal = p.causal;
   cur.kv0 = kv0;
   const bool any = cur.step_rank();
-  QTileRegs<D> regs;
-  if (any) {
-    load_qtile<D>(regs, p, cur, b, h, tid);
-    store_qtile<D>(regs, lds, f32s, 0, tid);
-  }
+  if (any) dma_qtile<D>(p, cur, b, h, lds, f32s, 0, wave, lane);
+  wait_dma();  // K, V and the first query tile
+  // per-lane element offsets: row operands at rows n (+32 key group / +32
+  // row half) and columns 16ss + 8hf; transposing reads at rows
+  // 4hf + j16/4 (+8) (+32qh + 16kq) and columns 32dt + 16grp + 4(j16%4)
+  int roff[D / 16], toff[2][D / 32];
+#pragma unroll
+  for (int ss = 0; ss < D / 16; ++ss) roff[ss] = tile_off<D>(n, 16 * ss + 8 * hf);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      toff[h2][dt] = tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
   int stage = 0;
   while (any) {
-    __syncthreads();  // this Q/dO stage is in LDS; the other one is no longer read
+    __syncthreads();  // this query stage is in LDS; the other one is no longer read
     QTileIter nx = cur;
     const bool more = nx.next();
-    if (more) load_qtile<D>(regs, p, nx, b, h, tid);  // in flight during the compute below
+    if (more) dma_qtile<D>(p, nx, b, h, lds, f32s, stage ^ 1, wave, lane);  // lands during the compute below
 
     const int32_t band = cur.band;
     const int32_t q0 = cur.qt * kQm;
     const int32_t qw = q0 + 32 * qh;  // first row of this wave
-    const __bf16* qs = lds + L::Q + stage * kQm * L::RS;
-    const __bf16* os = lds + L::DO + stage * kQm * L::RS;
+    const __bf16* qs = lds + L::Q + stage * kQm * D;
+    const __bf16* os = lds + L::DO + stage * kQm * D;
     const float* lse_s = f32s + stage * kQm;
     const float* dsum_s = f32s + 2 * kQm + stage * kQm;
     const bool dead = (kw >= Bb) || (qw >= Bb) || (kw - (qw + 31) > band);
     if (!dead) {
       const bool need_mask = (kw + 31 - qw > band) || (qw + 32 > Bb) || (kw + 32 > Bb);
-      // row operands: (row, 8hf) + 16 ss; the padded layout keeps that affine
-      const int qoff = tile_off<D>(32 * qh + n, 8 * hf);
-      const int koff = tile_off<D>(32 * kg + n, 8 * hf);
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + qoff + 16 * ss);
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(lds + L::K + koff + 16 * ss);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + roff[ss] + 32 * qh * D);
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(lds + L::K + roff[ss] + 32 * kg * D);
         s = mfma32(qa, kb, s);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(os + qoff + 16 * ss);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(lds + L::V + koff + 16 * ss);
+        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(os + roff[ss] + 32 * qh * D);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(lds + L::V + roff[ss] + 32 * kg * D);
         dp = mfma32(oa, vb, dp);
       }
       // lane (hf, n): key n against rows 8(i/4) + 4hf + i%4 of the wave's 32
@@ -265,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         const int qr0 = 32 * qh + 8 * g + 4 * hf;  // row within the 64-row tile
         const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qr0);
         const float4 d4 = *reinterpret_cast<const float4*>(dsum_s + qr0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
         const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -280,23 +231,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
           dsb[g / 2][4 * (g % 2) + e] = (__bf16)dsv;
         }
       }
-      // dV^T += dO^T P, dK^T += Q^T dS: contraction over the wave's 32 rows;
-      // transposing reads at (row, col) + 16kq rows (+8) + 32dt columns
-      const int troff = opaque(tile_off<D>(32 * qh + 4 * hf + j16 / 4, 16 * grp + 4 * (j16 % 4)));
+      // dV^T += dO^T P, dK^T += Q^T dS: contraction over the wave's 32 rows
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int kq = 0; kq < 2; ++kq) {
-          const int o1 = troff + 16 * kq * L::RS + 32 * dt;
-          const int o2 = o1 + 8 * L::RS;
-          const bf16x8 ot = cat(tr_read(os + o1), tr_read(os + o2));
-          const bf16x8 qt = cat(tr_read(qs + o1), tr_read(qs + o2));
+          const int rows = (32 * qh + 16 * kq) * D;
+          const bf16x8 ot = cat(tr_read(os + toff[0][dt] + rows), tr_read(os + toff[1][dt] + rows));
+          const bf16x8 qt = cat(tr_read(qs + toff[0][dt] + rows), tr_read(qs + toff[1][dt] + rows));
           dv[dt] = mfma32(ot, pb[kq], dv[dt]);
           dk[dt] = mfma32(qt, dsb[kq], dk[dt]);
         }
     }
     if (!more) break;
-    store_qtile<D>(regs, lds, f32s, stage ^ 1, tid);  // read last in the previous iteration
+    wait_dma();
     cur = nx;
     stage ^= 1;
   }

@@ -43,12 +43,10 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   const int32_t BH = p.B * p.H;
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t tiles = (Bb + kQTm - 1) / kQTm;
-  const int64_t id = blockIdx.x;
-  const int32_t bh = (int32_t)(id % BH);
+  int32_t bh, ri, tile;
+  query_work_of(blockIdx.x, BH, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
-  int32_t ri, tile;
-  query_tile_of(p.causal, p.layout, p.n_ranks, id / BH, tiles, &ri, &tile);
   const int32_t i = p.rank_begin + ri;
   const int32_t a0 = tile * kQTm;
   const int32_t aw = a0 + 32 * wave;
@@ -82,80 +80,118 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
     acc[dt] = z;
   }
 
-  KvIter it;
-  it.kstep = -1;
-  it.nsteps = p.P;
-  it.single_block = -1;
-  it.i = i;
-  it.P = p.P;
-  it.layout = p.layout;
-  it.causal = p.causal;
-  it.a_hi = a_hi;
-  it.Bb = Bb;
+  // per-lane element offsets inside a tile: K / V rows n (+32t) at columns
+  // 16ss + 8hf; K^T transposing reads at rows 4hf + j16/4 (+8) (+16kk) and
+  // columns 32dt + 16grp + 4(j16%4)
+  int koff[D / 16], toff[2][D / 32];
+#pragma unroll
+  for (int ss = 0; ss < D / 16; ++ss) koff[ss] = tile_off<D>(n, 16 * ss + 8 * hf);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      toff[h2][dt] = tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
+
+  KvIter c0;
+  c0.kstep = -1;
+  c0.nsteps = p.P;
+  c0.single_block = -1;
+  c0.i = i;
+  c0.P = p.P;
+  c0.layout = p.layout;
+  c0.causal = p.causal;
+  c0.a_hi = a_hi;
+  c0.Bb = Bb;
   auto kv_base = [&](const Seq& sq, int32_t blk) {
     return reinterpret_cast<const __bf16*>(sq.ptr) + (int64_t)blk * sq.s_blk + b * sq.s_batch + h * sq.s_head;
   };
-
-  const float c2 = p.scale_log2;
-  bool any = it.next_block();
-  KvRegs<D> regs;
-  if (any) {
-    load_kv<D>(regs, kv_base(p.k, it.j), kv_base(p.v, it.j), p.k.s_tok, p.v.s_tok, 0, Bb, tid);
-    store_kv<D>(regs, lds, tid);
-  }
-  int stage = 0;
-  while (any) {
-    __syncthreads();  // this stage is in LDS; the other one is no longer read
-    KvIter nx = it;
-    const bool more = nx.next();
-    if (more)
-      load_kv<D>(regs, kv_base(p.k, nx.j), kv_base(p.v, nx.j), p.k.s_tok, p.v.s_tok, nx.t * kKvTn, Bb, tid);
-
-    const int32_t band = it.band;
-    const int32_t b0 = it.t * kKvTn;
+  auto dma_tile = [&](const KvIter& t, int stage) {
+    __bf16* st = lds + stage * L::STAGE;
+    dma_rows<D, kKvTn, kQWaves>(st, kv_base(p.k, t.j), p.k.s_tok, t.t * kKvTn, Bb, wave, lane);
+    dma_rows<D, kKvTn, kQWaves>(st + L::TILE, kv_base(p.v, t.j), p.v.s_tok, t.t * kKvTn, Bb, wave, lane);
+  };
+  auto dead = [&](const KvIter& t) { return (aw >= Bb) || (t.t * kKvTn - (aw + 31) > t.band); };
+  // S^T = K Q^T and dP^T = V dO^T for keys 32 half .. +31 of a tile
+  auto produce = [&](int stage, int half, f32x16* sd) {
     const __bf16* ks = lds + stage * L::STAGE;
     const __bf16* vs = ks + L::TILE;
-    const bool dead = (aw >= Bb) || (b0 - (aw + 31) > band);
-    if (!dead) {
-      const bool need_mask = (b0 + kKvTn - 1 - aw > band) || (b0 + kKvTn > Bb);
-      const int koff = tile_off<D>(n, 8 * hf);
-      const int toff = opaque(tile_off<D>(4 * hf + j16 / 4, 16 * grp + 4 * (j16 % 4)));
+    f32x16 z = {};
+    sd[0] = z;
+    sd[1] = z;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {  // 32-key halves of the tile
-        f32x16 s = {}, dp = {};
-#pragma unroll
-        for (int ss = 0; ss < D / 16; ++ss) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff + 32 * t * L::RS + 16 * ss);
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + koff + 32 * t * L::RS + 16 * ss);
-          s = mfma32(kf, qreg[ss], s);
-          dp = mfma32(vf, oreg[ss], dp);
-        }
-        // lane (hf, n): query n against keys 32t + 8(e/4) + 4hf + e%4
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float pv = fexp2(fmaf(s[e], c2, -lse2));
-          if (need_mask) {
-            const int32_t kb = b0 + 32 * t + 8 * (e / 4) + 4 * hf + (e % 4);
-            if (kb - a > band || kb >= Bb) pv = 0.0f;
-          }
-          dsb[e / 8][e % 8] = (__bf16)(pv * (dp[e] - dsum));
-        }
-        // dQ^T += K^T dS^T; dS element e of k-step kk = 2t + u is key 16kk + 8(e/4) + 4hf + e%4
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int o1 = toff + 16 * (2 * t + u) * L::RS + 32 * dt;
-            const bf16x8 kt = cat(tr_read(ks + o1), tr_read(ks + o1 + 8 * L::RS));
-            acc[dt] = mfma32(kt, dsb[u], acc[dt]);
-          }
-      }
+    for (int ss = 0; ss < D / 16; ++ss) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff[ss] + 32 * half * D);
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + koff[ss] + 32 * half * D);
+      sd[0] = mfma32(kf, qreg[ss], sd[0]);
+      sd[1] = mfma32(vf, oreg[ss], sd[1]);
     }
-    if (!more) break;
-    store_kv<D>(regs, lds + (stage ^ 1) * L::STAGE, tid);
-    it = nx;
-    stage ^= 1;
+  };
+  const float c2 = p.scale_log2;
+  // dS^T from the half's scores, then dQ^T += K^T dS^T
+  auto consume = [&](const KvIter& t, int stage, int half, f32x16* sd) {
+    const int32_t band = t.band;
+    const int32_t b0 = t.t * kKvTn + 32 * half;
+    const __bf16* ks = lds + stage * L::STAGE;
+    const bool need_mask = (b0 + 31 - aw > band) || (b0 + 32 > Bb);
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float pv = fexp2(fmaf(sd[0][e], c2, -lse2));
+      if (need_mask) {
+        const int32_t kb = b0 + 8 * (e / 4) + 4 * hf + (e % 4);
+        if (kb - a > band || kb >= Bb) pv = 0.0f;
+      }
+      dsb[e / 8][e % 8] = (__bf16)(pv * (sd[1][e] - dsum));
+    }
+    // dS element e of k-step 2 half + u is key 16(2 half + u) + 8(e/4) + 4hf + e%4
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rows = 16 * (2 * half + u) * D;
+        const bf16x8 kt = cat(tr_read(ks + toff[0][dt] + rows), tr_read(ks + toff[1][dt] + rows));
+        acc[dt] = mfma32(kt, dsb[u], acc[dt]);
+      }
+  };
+
+  if (c0.next_block()) {
+    KvIter c1 = c0;
+    bool v1 = c1.next();
+    dma_tile(c0, 0);
+    if (v1) dma_tile(c1, 1);
+    wait_dma();
+    __syncthreads();
+    f32x16 sa[2], sb[2];  // scores of half 0 / half 1 of a tile
+    bool da = dead(c0);
+    if (!da) produce(0, 0, sa);
+    int sc = 0;
+    // the MFMA pipe gets the next half's products before the current half's
+    // exponentials are computed; the tile after next is copied meanwhile
+    while (true) {
+      KvIter c2 = c1;
+      const bool v2 = v1 && c2.next();
+      const int s1 = (sc == 2) ? 0 : sc + 1;
+      const int s2 = (s1 == 2) ? 0 : s1 + 1;
+      if (v2) dma_tile(c2, s2);
+      if (!da) {
+        produce(sc, 1, sb);
+        consume(c0, sc, 0, sa);
+      }
+      bool db = true;
+      if (v1) {
+        db = dead(c1);
+        if (!db) produce(s1, 0, sa);
+      }
+      if (!da) consume(c0, sc, 1, sb);
+      if (!v1) break;
+      wait_dma();
+      __syncthreads();  // tile c2 is in LDS; stage sc is free
+      c0 = c1;
+      c1 = c2;
+      v1 = v2;
+      da = db;
+      sc = s1;
+    }
   }
 
   if (a >= Bb) return;

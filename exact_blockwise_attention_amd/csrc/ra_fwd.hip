@@ -33,6 +33,11 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the reference max
+// Instruction interleave requested from the scheduler for the block that
+// issues the next tile's score MFMAs, this tile's exponentials and its P V
+// MFMAs: 0 = compiler default, 1 = score MFMAs with 6 VALU each then the P V
+// MFMAs with their reads, 2 = score MFMAs with 10 VALU each (fastest measured).
+constexpr int kFwdInterleave = 2;
 
 // Work order for the fp32 kernel (64-row tiles); same rule as query_tile_of.
 __device__ __forceinline__ void tile_of(const FwdParams& p, int64_t ord, int32_t tiles, int32_t* rank_idx,
@@ -57,12 +62,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const int32_t BH = p.B * p.H;
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t tiles = (Bb + kQTm - 1) / kQTm;
-  const int64_t id = blockIdx.x;
-  const int32_t bh = (int32_t)(id % BH);
+  int32_t bh, ri, tile;
+  query_work_of(blockIdx.x, BH, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
-  int32_t ri, tile;
-  query_tile_of(p.causal, p.layout, p.n_ranks, id / BH, tiles, &ri, &tile);
   const int32_t i = p.rank_begin + ri;
   const int32_t a0 = tile * kQTm;
   const int32_t aw = a0 + 32 * wave;  // first row of this wave
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     qreg[ss] = __builtin_bit_cast(bf16x8, val);
   }
 
-  // online-softmax state: acc[dt][i] = O^T feature 32dt + 8(i/4) + 4hf + i%4
+  // online-softmax state: acc[dt][e] = O^T feature 32dt + 8(e/4) + 4hf + e%4
   f32x16 acc[D / 32];
   float m, l;
   const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;  // state / lse row base
@@ -108,108 +111,187 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  KvIter it;
-  it.kstep = -1;
-  it.nsteps = (p.mode == 0) ? p.P : 1;
-  it.single_block = (p.mode == 0) ? -1 : p.step_block;
-  it.i = i;
-  it.P = p.P;
-  it.layout = p.layout;
-  it.causal = p.causal;
-  it.a_hi = a_hi;
-  it.Bb = Bb;
+  // per-lane element offsets inside a tile: K rows n (+32t) at columns
+  // 16ss + 8hf; V^T transposing reads at rows 4hf + j16/4 (+8) (+16kk) and
+  // columns 32dt + 16grp + 4(j16%4)
+  int koff[D / 16], voff[2][D / 32];
+#pragma unroll
+  for (int ss = 0; ss < D / 16; ++ss) koff[ss] = tile_off<D>(n, 16 * ss + 8 * hf);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      voff[h2][dt] = tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
+
+  KvIter c0;
+  c0.kstep = -1;
+  c0.nsteps = (p.mode == 0) ? p.P : 1;
+  c0.single_block = (p.mode == 0) ? -1 : p.step_block;
+  c0.i = i;
+  c0.P = p.P;
+  c0.layout = p.layout;
+  c0.causal = p.causal;
+  c0.a_hi = a_hi;
+  c0.Bb = Bb;
   const int64_t kvblk_mul = (p.mode == 0) ? 1 : 0;  // the single-step buffer holds one block
   auto kv_base = [&](const Seq& sq, int32_t blk) {
     return reinterpret_cast<const __bf16*>(sq.ptr) + kvblk_mul * blk * sq.s_blk + b * sq.s_batch + h * sq.s_head;
   };
-
-  const float c2 = p.scale_log2;
-  bool any = it.next_block();
-  KvRegs<D> regs;
-  if (any) {
-    load_kv<D>(regs, kv_base(p.k, it.j), kv_base(p.v, it.j), p.k.s_tok, p.v.s_tok, 0, Bb, tid);
-    store_kv<D>(regs, lds, tid);
-  }
-  int stage = 0;
-  while (any) {
-    __syncthreads();  // this stage is in LDS; the other one is no longer read
-    KvIter nx = it;
-    const bool more = nx.next();
-    if (more)
-      load_kv<D>(regs, kv_base(p.k, nx.j), kv_base(p.v, nx.j), p.k.s_tok, p.v.s_tok, nx.t * kKvTn, Bb, tid);
-
-    const int32_t band = it.band;
-    const int32_t b0 = it.t * kKvTn;
+  auto dma_tile = [&](const KvIter& t, int stage) {
+    __bf16* st = lds + stage * L::STAGE;
+    dma_rows<D, kKvTn, kQWaves>(st, kv_base(p.k, t.j), p.k.s_tok, t.t * kKvTn, Bb, wave, lane);
+    dma_rows<D, kKvTn, kQWaves>(st + L::TILE, kv_base(p.v, t.j), p.v.s_tok, t.t * kKvTn, Bb, wave, lane);
+  };
+  // S^T = K Q^T for the tile's 64 keys (two 32-key halves)
+  auto scores = [&](int stage, f32x16* s) {
     const __bf16* ks = lds + stage * L::STAGE;
-    const __bf16* vs = ks + L::TILE;
-    const bool dead = (aw >= Bb) || (b0 - (aw + 31) > band);
-    if (!dead) {
-      const bool need_mask = (b0 + kKvTn - 1 - aw > band) || (b0 + kKvTn > Bb);
-      const int koff = tile_off<D>(n, 8 * hf);
-      f32x16 s[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x16 z = {};
-        s[t] = z;
+    for (int t = 0; t < 2; ++t) {
+      f32x16 z = {};
+      s[t] = z;
 #pragma unroll
-        for (int ss = 0; ss < D / 16; ++ss) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff + 32 * t * L::RS + 16 * ss);
-          s[t] = mfma32(kf, qreg[ss], s[t]);
-        }
+      for (int ss = 0; ss < D / 16; ++ss) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff[ss] + 32 * t * D);
+        s[t] = mfma32(kf, qreg[ss], s[t]);
       }
-      if (need_mask) {
+    }
+  };
+  const float c2 = p.scale_log2;
+  // Mask and running-max update of tile t (scores in s); returns the max to
+  // subtract. Rows whose keys are all masked keep a zero weight.
+  auto prepare = [&](const KvIter& t, f32x16* s) {
+    const int32_t band = t.band;
+    const int32_t b0 = t.t * kKvTn;
+    if ((b0 + kKvTn - 1 - aw > band) || (b0 + kKvTn > Bb)) {
+      // key b0 + off is visible iff off <= min(band + a - b0, Bb - 1 - b0)
+      const int32_t lim0 = band + a - b0, lim1 = Bb - 1 - b0;
+      const int32_t lim = lim0 < lim1 ? lim0 : lim1;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int32_t kb = b0 + 32 * t + 8 * (e / 4) + 4 * hf + (e % 4);
-            if (kb - a > band || kb >= Bb) s[t][e] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mt = mx * c2;  // tile max, log2 units
-      if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m, mt);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : fexp2(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
-        m = m_new;
-      }
-      const float m_use = (m == -INFINITY) ? 0.0f : m;
-      bf16x8 pb[4];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pv = fexp2(fmaf(s[t][e], c2, -m_use));
-          lsum += pv;
-          pb[2 * t + e / 8][e % 8] = (__bf16)pv;
+          const int32_t off = 32 * t2 + 8 * (e / 4) + 4 * hf + (e % 4);
+          if (off > lim) s[t2][e] = -INFINITY;
         }
-      l += lsum;
-      // O^T += V^T P^T; P element e of k-step kk is key 16kk + 8(e/4) + 4hf + e%4
-      const int voff = opaque(tile_off<D>(4 * hf + j16 / 4, 16 * grp + 4 * (j16 % 4)));
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * c2;  // tile max, log2 units
+    if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fexp2(m - m_new);
+      l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int o1 = voff + 16 * kk * L::RS + 32 * dt;
-          const bf16x8 vf = cat(tr_read(vs + o1), tr_read(vs + o1 + 8 * L::RS));
-          acc[dt] = mfma32(vf, pb[kk], acc[dt]);
-        }
+        for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
+      m = m_new;
     }
-    if (!more) break;
-    store_kv<D>(regs, lds + (stage ^ 1) * L::STAGE, tid);
-    it = nx;
-    stage ^= 1;
+    return (m == -INFINITY) ? 0.0f : m;
+  };
+  // One branch-free block: the next tile's scores (into s_next, from stage
+  // s1), this tile's probabilities (from s_cur) and O^T += V^T P^T (stage sc).
+  auto fused = [&](int sc, int s1, f32x16* s_cur, f32x16* s_next, float m_use) {
+    scores(s1, s_next);
+    const __bf16* vs = lds + sc * L::STAGE + L::TILE;
+    bf16x8 pb[4];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = fexp2(fmaf(s_cur[t2][e], c2, -m_use));
+        lsum += pv;
+        pb[2 * t2 + e / 8][e % 8] = (__bf16)pv;
+      }
+    l += lsum;
+    // P element e of k-step kk is key 16kk + 8(e/4) + 4hf + e%4
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 vf = cat(tr_read(vs + voff[0][dt] + 16 * kk * D), tr_read(vs + voff[1][dt] + 16 * kk * D));
+        acc[dt] = mfma32(vf, pb[kk], acc[dt]);
+      }
+    if (kFwdInterleave == 2) {
+#pragma unroll
+      for (int k = 0; k < D / 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+      }
+    }
+    if (kFwdInterleave == 1) {
+      // 16 score MFMAs each followed by a K read and 6 VALU (exponentials),
+      // then the 16 P V MFMAs with their V^T reads
+#pragma unroll
+      for (int k = 0; k < D / 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+#pragma unroll
+      for (int k = 0; k < D / 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+  };
+
+  if (c0.next_block()) {
+    KvIter c1 = c0;
+    bool v1 = c1.next();
+    dma_tile(c0, 0);
+    if (v1) dma_tile(c1, 1);
+    wait_dma();
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    scores(0, sa);
+    int sc = 0;
+    // Each half: this tile's softmax runs while the next tile's score MFMAs
+    // are on the matrix pipe, and the tile after next is being copied. Two
+    // halves per trip swap the score buffers without copies. Every wave does
+    // every tile (a tile hidden from a wave by the mask is fully masked and
+    // contributes zero), which keeps the block free of branches; the last
+    // half computes scores of a stale stage and drops them.
+    while (true) {
+      {
+        KvIter c2 = c1;
+        const bool v2 = v1 && c2.next();
+        const int s1 = (sc == 2) ? 0 : sc + 1;
+        const int s2 = (s1 == 2) ? 0 : s1 + 1;
+        if (v2) dma_tile(c2, s2);
+        const float m_use = prepare(c0, sa);
+        fused(sc, s1, sa, sb, m_use);
+        if (!v1) break;
+        wait_dma();
+        __syncthreads();  // tile c2 is in LDS; stage sc is free
+        c0 = c1;
+        c1 = c2;
+        v1 = v2;
+        sc = s1;
+      }
+      {
+        KvIter c2 = c1;
+        const bool v2 = v1 && c2.next();
+        const int s1 = (sc == 2) ? 0 : sc + 1;
+        const int s2 = (s1 == 2) ? 0 : s1 + 1;
+        if (v2) dma_tile(c2, s2);
+        const float m_use = prepare(c0, sb);
+        fused(sc, s1, sb, sa, m_use);
+        if (!v1) break;
+        wait_dma();
+        __syncthreads();
+        c0 = c1;
+        c1 = c2;
+        v1 = v2;
+        sc = s1;
+      }
+    }
   }
 
   // finalise: combine the two halves' sums, normalise, export

@@ -8,9 +8,9 @@
 // Communicate") and, in each block, the 64-key tiles that some row of the
 // workgroup can see under the causal / striped mask ("Ring Attention 論文分析"
 // (blog), section "Causal Masking の処理": later blocks skipped, the diagonal
-// masked); a single-step launch visits one given block only. KV tiles are
-// double-buffered in LDS, the next one travelling through registers while the
-// current one is computed.
+// masked); a single-step launch visits one given block only. KV tiles go
+// straight from global memory to a ring of three LDS stages, two tiles ahead
+// of the one whose softmax is being computed.
 #ifndef RA_KVWALK_H_
 #define RA_KVWALK_H_
 
@@ -26,14 +26,41 @@ constexpr int kQTm = 32 * kQWaves;  // query rows per workgroup
 constexpr int kKvTn = 64;           // keys per KV tile
 constexpr int kBandAll = 1 << 30;
 
-// LDS: two stages of (K tile, V tile), each [64][D] padded.
+// LDS: three stages of (K tile, V tile), each [64][D] swizzled.
 template <int D>
 struct KvLds {
-  static constexpr int RS = PadRow<D>::RS;
-  static constexpr int TILE = kKvTn * RS;
+  static constexpr int TILE = kKvTn * D;
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int BYTES = 2 * STAGE * 2;
+  static constexpr int NSTAGE = 3;
+  static constexpr int BYTES = NSTAGE * STAGE * 2;
 };
+
+// Workgroups are dealt to the 8 XCDs round-robin by linear id, and each XCD
+// has its own L2. This maps the linear id to a logical index such that the
+// workgroups of one XCD cover a contiguous range of logical indices (XCD x
+// gets ids x, x+8, ... and the logical range that starts after the ranges of
+// XCDs 0..x-1). A bijection for any grid size.
+__device__ __forceinline__ int64_t xcd_logical(int64_t id, int64_t n) {
+  const int64_t x = id % 8, s = id / 8;
+  const int64_t q = n / 8, r = n % 8;
+  return x * q + (x < r ? x : r) + s;
+}
+
+// Query-tile workgroups: consecutive logical indices share (batch, head,
+// rank) and take its query tiles heaviest first, so the workgroups resident
+// on one XCD walk the same KV tiles at about the same time and share them in
+// L2. Heavier ranks come first (contiguous causal work grows with the rank).
+__device__ __forceinline__ void query_work_of(int64_t id, int32_t BH, int32_t n_ranks, int32_t tiles,
+                                              int32_t causal, int32_t layout, int32_t* bh, int32_t* rank_idx,
+                                              int32_t* tile) {
+  const int64_t n = (int64_t)BH * n_ranks * tiles;
+  const int64_t L = xcd_logical(id, n);
+  const int64_t g = L / tiles;
+  *tile = tiles - 1 - (int32_t)(L % tiles);
+  *bh = (int32_t)(g / n_ranks);
+  const int32_t r = (int32_t)(g % n_ranks);
+  *rank_idx = (causal && layout == kContiguous) ? n_ranks - 1 - r : r;
+}
 
 // Work order: the heaviest query tiles are dispatched first. Contiguous
 // causal work grows with the rank, striped and non-causal work with the row.
@@ -69,47 +96,41 @@ struct KvIter {
   __device__ bool next() { return (++t < ntile) ? true : next_block(); }
 };
 
-// One KV tile on its way from global memory to LDS.
-template <int D>
-struct KvRegs {
-  static constexpr int CR = D / 8;
-  static constexpr int RPP = kQThreads / CR;
-  static constexpr int NP = kKvTn / RPP;
-  u32x4 k[NP], v[NP];
-};
-
-template <int D>
-__device__ __forceinline__ void load_kv(KvRegs<D>& r, const __bf16* kb, const __bf16* vb, int64_t ks_tok,
-                                        int64_t vs_tok, int32_t b0, int32_t Bb, int tid) {
-  using T = KvRegs<D>;
-  const int c = tid % T::CR;
-  const int r0 = tid / T::CR;
+// Direct global -> LDS copy (global_load_lds_dwordx4: lane l of a wave
+// writes its 16 bytes at the wave's LDS base + 16 l) of rows
+// [r_lo, r_lo + ROWS) of a strided [rows][D] tensor into a swizzled LDS tile,
+// shared by the NW waves of the workgroup. Each lane fetches the logical
+// chunk that belongs at its physical position. Rows at or beyond `nrows` read
+// row nrows-1 instead (finite data; the kernels mask those rows). The copy is
+// asynchronous: wait_dma() and a barrier make it visible.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_rows(__bf16* tile, const __bf16* base, int64_t s_tok, int32_t r_lo,
+                                         int32_t nrows, int wave, int lane) {
+  constexpr int RW = 1024 / (2 * D);  // rows per wave copy
+  constexpr int CPR = D / 8;          // chunks per row
+  constexpr int COPIES = ROWS / RW;
+  static_assert(COPIES % NW == 0, "copies must split evenly over the waves");
 #pragma unroll
-  for (int q = 0; q < T::NP; ++q) {
-    const int32_t x = b0 + r0 + T::RPP * q;
-    u32x4 vk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (x < Bb) {
-      vk = *reinterpret_cast<const u32x4*>(kb + (int64_t)x * ks_tok + 8 * c);
-      vv = *reinterpret_cast<const u32x4*>(vb + (int64_t)x * vs_tok + 8 * c);
-    }
-    r.k[q] = vk;
-    r.v[q] = vv;
+  for (int k = 0; k < COPIES / NW; ++k) {
+    const int q = wave + NW * k;
+    const int row = q * RW + lane / CPR;
+    const int c = (lane % CPR) ^ chunk_swz<D>(row);
+    int32_t x = r_lo + row;
+    if (x > nrows - 1) x = nrows - 1;
+    const __bf16* g = base + (int64_t)x * s_tok + 8 * c;
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(tile + q * RW * D), 16, 0, 0);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void store_kv(const KvRegs<D>& r, __bf16* stage, int tid) {
-  using T = KvRegs<D>;
-  using L = KvLds<D>;
-  const int c = tid % T::CR;
-  const int r0 = tid / T::CR;
-#pragma unroll
-  for (int q = 0; q < T::NP; ++q) {
-    const int row = r0 + T::RPP * q;
-    *reinterpret_cast<u32x4*>(stage + tile_off<D>(row, 8 * c)) = r.k[q];
-    *reinterpret_cast<u32x4*>(stage + L::TILE + tile_off<D>(row, 8 * c)) = r.v[q];
-  }
+// fp32 rows (lse, D) of a query tile: lane l of one wave copies element
+// r_lo + l (clamped to nrows - 1) to tile[l]; 64 elements.
+__device__ __forceinline__ void dma_f32_64(float* tile, const float* base, int32_t r_lo, int32_t nrows, int lane) {
+  int32_t x = r_lo + lane;
+  if (x > nrows - 1) x = nrows - 1;
+  __builtin_amdgcn_global_load_lds(base + x, (__attribute__((address_space(3))) void*)tile, 4, 0, 0);
 }
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace ra
 

@@ -1,15 +1,18 @@
 // ra_lds.h — LDS tile layouts and operand helpers shared by the kernels.
 //
-// Tiles of bf16 rows live in LDS row-major with rows padded by 32 bytes
-// (row stride = 8 banks mod 32), and the two 16-byte halves of every 32-byte
-// piece swapped on rows whose bit 2 is set. Both read patterns the kernels
-// use are then free of bank conflicts, and addresses stay affine in the
-// unrolled loop indices (the swap only involves lane-dependent bits):
-//   * MFMA row operands: 8 consecutive lanes read the same 16-byte chunk of 8
-//     consecutive rows (rows 0..3 land 8 banks apart, rows 4..7 shifted by 4);
-//   * transposing reads (ds_read_b64_tr_b16): 16 lanes read 8 bytes each
-//     from 4 consecutive rows (starting at a multiple of 4) and one 32-byte
-//     piece of each, 8 banks apart.
+// Tiles of bf16 rows live in LDS row-major, unpadded, with the 16-byte
+// chunks of each row permuted by an XOR swizzle of the row index. On gfx950
+// the LDS serves 256 bytes per clock (64 banks of 4 bytes): a 16-byte read
+// is served 16 lanes at a time, an 8-byte read 32 lanes at a time. The
+// swizzle makes both read patterns the kernels use conflict-free (measured
+// with the SQ_LDS_BANK_CONFLICT counter):
+//   * MFMA row operands: 16 consecutive lanes read the same logical chunk of
+//     16 consecutive rows;
+//   * transposing reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive
+//     rows (starting at a multiple of 4) times 64 consecutive bytes.
+// For 256-byte rows (d = 128) the chunk index is XORed with
+// ((r & 3) << 2) | ((r >> 2) & 3); for 128-byte rows (d = 64) with
+// r1 | r2 << 1 | (r1 ^ r3) << 2 (r_k = bit k of the row).
 // A transposing read returns, to lane i of each 16-lane group, element i%4
 // of the 8 bytes read by lane 4e + i/4, for e = 0..3: with lane j reading
 // row r0 + j/4, columns c0 + 4(j%4) .. +3 of a row-major [k][m] tile, lane i
@@ -30,16 +33,22 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Row stride (elements) of a padded [rows][D] bf16 tile.
+// Row stride (elements) of a [rows][D] bf16 tile.
 template <int D>
 struct PadRow {
-  static constexpr int RS = D + 16;
+  static constexpr int RS = D;
 };
 
-// Element offset of (row r, column c) in a padded [rows][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ int chunk_swz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
+
+// Element offset of (row r, column c) in a swizzled [rows][D] bf16 tile.
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return r * PadRow<D>::RS + ((((c >> 3) ^ ((r >> 2) & 1)) << 3) | (c & 7));
+  return r * D + ((((c >> 3) ^ chunk_swz<D>(r)) << 3) | (c & 7));
 }
 
 // 8-byte unit swizzle for [rows][64] bf16 tiles (128-byte rows) written in
