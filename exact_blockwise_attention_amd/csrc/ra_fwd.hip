@@ -18,10 +18,24 @@
 // kept in log2 units. The reference max m is raised only when a tile's max
 // exceeds it by more than 8 (then the accumulator is rescaled), so most
 // tiles skip the rescale; probabilities then stay below 2^8, exact in the
-// fp32 sums and representable in bf16. lse is exported as a natural log.
+// fp32 sums and representable in bf16. The row sum adds the bf16-rounded
+// probabilities, the same values the P V product uses. lse is exported as a
+// natural log.
+//
+// Schedule. The 8 waves form two groups, waves 0-3 and 4-7; waves w and
+// w + 4 share a SIMD. Each wave alternates a matrix phase (the next tile's
+// scores and this tile's P V product: 32 MFMAs) and a vector phase (mask,
+// max, exponentials of the next tile). Workgroup barriers separate the
+// phases and group 1 runs one phase behind group 0, so on every SIMD one
+// wave feeds the matrix core while the other does the softmax. KV tiles go
+// straight from global memory to a ring of four LDS stages (K tiles in the
+// lower half of LDS, V tiles in the upper half); a tile is requested four
+// phases before its first use.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ra_internal.h"
 #include "ra_kvwalk.h"
@@ -33,31 +47,85 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the reference max
-// Instruction interleave requested from the scheduler for the block that
-// issues the next tile's score MFMAs, this tile's exponentials and its P V
-// MFMAs: 0 = compiler default, 1 = score MFMAs with 6 VALU each then the P V
-// MFMAs with their reads, 2 = score MFMAs with 10 VALU each (fastest measured).
-constexpr int kFwdInterleave = 2;
 
-// Work order for the fp32 kernel (64-row tiles); same rule as query_tile_of.
-__device__ __forceinline__ void tile_of(const FwdParams& p, int64_t ord, int32_t tiles, int32_t* rank_idx,
-                                        int32_t* tile) {
-  query_tile_of(p.causal, p.layout, p.n_ranks, ord, tiles, rank_idx, tile);
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+// LDS of the bf16 forward: NST stages of a K tile and a V tile ([64][D],
+// swizzled), K tiles first.
+template <int D>
+struct FwdLds {
+  static constexpr int NST = 4;
+  static constexpr int TILE_B = kKvTn * D * 2;  // bytes of one tile
+  static constexpr int VBASE_B = NST * TILE_B;  // byte offset of the V tiles
+  static constexpr int BYTES = 2 * NST * TILE_B;
+};
+
+// Direct copies of a 64-row tile: a wave instruction moves 1 KB (RW rows);
+// each wave issues CPW of them per tensor.
+template <int D>
+struct FwdDma {
+  static constexpr int RW = 1024 / (2 * D);
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static constexpr int CPW = kKvTn / RW / kQWaves;
+  static constexpr int NI = 2 * CPW;  // instructions per tile per wave (K and V)
+  static_assert(CPW >= 1 && (kKvTn / RW) % kQWaves == 0, "tile copies must split over the waves");
+};
+
+// Waits until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the implicit memory waits of __syncthreads: the
+// kernel waits for exactly the loads it needs before each barrier.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// max over the two half-waves (lanes n and n ^ 32)
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Transposing LDS read (ds_read_b64_tr_b16) at addr + OFF bytes. Issued as
+// inline assembly: the compiler would otherwise wait for every outstanding
+// global-to-LDS copy before it (it cannot tell that the copies target other
+// stages). The caller waits for the result with lds_wait().
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offsets are 16 bits");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Waits until at most N LDS reads of this wave are outstanding (LDS reads
+// complete in order); the operands are tied so that their uses stay after.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2 (&r)[4][2]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1]), "+v"(r[2][0]), "+v"(r[2][1]),
+                 "+v"(r[3][0]), "+v"(r[3][1])
+               : "n"(N));
 }
 
 template <int D>
 __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
-  using L = KvLds<D>;
+  using L = FwdLds<D>;
+  using DM = FwdDma<D>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __bf16* lds = reinterpret_cast<__bf16*>(smem_raw);
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int n = lane % 32;
   const int hf = lane / 32;
   const int grp = (lane / 16) % 2;
   const int j16 = lane % 16;
+  const bool g1 = wave >= kQWaves / 2;  // second ping-pong group
 
   const int32_t BH = p.B * p.H;
   const int32_t Bb = (int32_t)p.Bb;
@@ -111,55 +179,122 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     }
   }
 
-  // per-lane element offsets inside a tile: K rows n (+32t) at columns
+  // per-lane byte offsets inside a stage: K rows n (+32t) at columns
   // 16ss + 8hf; V^T transposing reads at rows 4hf + j16/4 (+8) (+16kk) and
   // columns 32dt + 16grp + 4(j16%4)
-  int koff[D / 16], voff[2][D / 32];
+  uint32_t koff[D / 16], voff[2][D / 32];
 #pragma unroll
-  for (int ss = 0; ss < D / 16; ++ss) koff[ss] = tile_off<D>(n, 16 * ss + 8 * hf);
+  for (int ss = 0; ss < D / 16; ++ss) koff[ss] = 2 * tile_off<D>(n, 16 * ss + 8 * hf);
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
-      voff[h2][dt] = tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
+      voff[h2][dt] = L::VBASE_B + 2 * tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
 
-  KvIter c0;
-  c0.kstep = -1;
-  c0.nsteps = (p.mode == 0) ? p.P : 1;
-  c0.single_block = (p.mode == 0) ? -1 : p.step_block;
-  c0.i = i;
-  c0.P = p.P;
-  c0.layout = p.layout;
-  c0.causal = p.causal;
-  c0.a_hi = a_hi;
-  c0.Bb = Bb;
+  // per-lane source offsets (bytes, from the tile's first row) of the rows
+  // this wave copies, and their swizzled chunk
+  uint32_t dk[DM::CPW], dv[DM::CPW];
+#pragma unroll
+  for (int kc = 0; kc < DM::CPW; ++kc) {
+    const int row = (wave + kQWaves * kc) * DM::RW + lane / DM::CPR;
+    const int c = (lane % DM::CPR) ^ chunk_swz<D>(row);
+    dk[kc] = (uint32_t)(2 * ((int64_t)row * p.k.s_tok + 8 * c));
+    dv[kc] = (uint32_t)(2 * ((int64_t)row * p.v.s_tok + 8 * c));
+  }
   const int64_t kvblk_mul = (p.mode == 0) ? 1 : 0;  // the single-step buffer holds one block
-  auto kv_base = [&](const Seq& sq, int32_t blk) {
-    return reinterpret_cast<const __bf16*>(sq.ptr) + kvblk_mul * blk * sq.s_blk + b * sq.s_batch + h * sq.s_head;
+  auto kv_base = [&](const Seq& sq, int32_t blk, int32_t r_lo) __attribute__((always_inline)) {
+    return reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(sq.ptr) + kvblk_mul * blk * sq.s_blk +
+                                         b * sq.s_batch + h * sq.s_head + (int64_t)r_lo * sq.s_tok);
   };
-  auto dma_tile = [&](const KvIter& t, int stage) {
-    __bf16* st = lds + stage * L::STAGE;
-    dma_rows<D, kKvTn, kQWaves>(st, kv_base(p.k, t.j), p.k.s_tok, t.t * kKvTn, Bb, wave, lane);
-    dma_rows<D, kKvTn, kQWaves>(st + L::TILE, kv_base(p.v, t.j), p.v.s_tok, t.t * kKvTn, Bb, wave, lane);
-  };
-  // S^T = K Q^T for the tile's 64 keys (two 32-key halves)
-  auto scores = [&](int stage, f32x16* s) {
-    const __bf16* ks = lds + stage * L::STAGE;
+  // Requests tile t into stage ST: this wave's CPW row groups of K and of V.
+  // Rows at or beyond Bb read row Bb - 1 (finite data; masked later).
+  auto dma = [&](const KvIter& t, auto STc) __attribute__((always_inline)) {
+    constexpr int ST = decltype(STc)::value;
+    const int32_t r_lo = t.t * kKvTn;
+    const char* kb = kv_base(p.k, t.j, r_lo);
+    const char* vb = kv_base(p.v, t.j, r_lo);
+    unsigned char* kd = smem_raw + ST * L::TILE_B;
+    unsigned char* vd = smem_raw + L::VBASE_B + ST * L::TILE_B;
+    if (r_lo + kKvTn <= Bb) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x16 z = {};
-      s[t] = z;
+      for (int kc = 0; kc < DM::CPW; ++kc) {
+        const int q = wave + kQWaves * kc;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(kb + dk[kc]), (__attribute__((address_space(3))) void*)(kd + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(vb + dv[kc]), (__attribute__((address_space(3))) void*)(vd + q * 1024), 16, 0, 0);
+      }
+    } else {
 #pragma unroll
-      for (int ss = 0; ss < D / 16; ++ss) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff[ss] + 32 * t * D);
-        s[t] = mfma32(kf, qreg[ss], s[t]);
+      for (int kc = 0; kc < DM::CPW; ++kc) {
+        const int q = wave + kQWaves * kc;
+        int row = q * DM::RW + lane / DM::CPR;
+        const int c = (lane % DM::CPR) ^ chunk_swz<D>(row);
+        if (row > Bb - 1 - r_lo) row = Bb - 1 - r_lo;
+        const int64_t ko = 2 * ((int64_t)row * p.k.s_tok + 8 * c), vo = 2 * ((int64_t)row * p.v.s_tok + 8 * c);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(kb + ko), (__attribute__((address_space(3))) void*)(kd + q * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>(vb + vo), (__attribute__((address_space(3))) void*)(vd + q * 1024), 16, 0, 0);
       }
     }
   };
+
   const float c2 = p.scale_log2;
-  // Mask and running-max update of tile t (scores in s); returns the max to
-  // subtract. Rows whose keys are all masked keep a zero weight.
-  auto prepare = [&](const KvIter& t, f32x16* s) {
+  f32x16 s[2];    // S^T of the tile in flight (32 keys each)
+  bf16x8 pb[4];   // its probabilities, B operand of the P V product
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // S^T = K Q^T for the 64 keys in stage ST
+  auto scores = [&](auto STc) __attribute__((always_inline)) {
+    constexpr int ST = decltype(STc)::value;
+    const unsigned char* ks = smem_raw + ST * L::TILE_B;
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      f32x16 z = {};
+      s[t2] = z;
+#pragma unroll
+      for (int ss = 0; ss < D / 16; ++ss) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff[ss] + t2 * 32 * D * 2);
+        s[t2] = mfma32(kf, qreg[ss], s[t2]);
+      }
+    }
+  };
+  // Matrix phase: scores of the tile in stage SK (if any) and O^T += V^T P^T
+  // with the V tile in stage SV. The V^T fragments of one 32-feature group
+  // (4 k-steps x 2 halves) are requested one group ahead of their MFMAs.
+  auto matrix = [&](auto SKc, auto SVc, bool with_scores) __attribute__((always_inline)) {
+    constexpr int SV = decltype(SVc)::value;
+    u32x2 vf[2][4][2];
+    auto request = [&](u32x2(&r)[4][2], int dt) __attribute__((always_inline)) {
+      // the addresses are loop-invariant; computing them here keeps the
+      // compiler from holding all of them in registers across the walk
+      const uint32_t o0 = opaque(voff[0][dt]), o1 = opaque(voff[1][dt]);
+      r[0][0] = tr_read_at<SV * L::TILE_B + 0 * 16 * D * 2>(o0);
+      r[0][1] = tr_read_at<SV * L::TILE_B + 0 * 16 * D * 2>(o1);
+      r[1][0] = tr_read_at<SV * L::TILE_B + 1 * 16 * D * 2>(o0);
+      r[1][1] = tr_read_at<SV * L::TILE_B + 1 * 16 * D * 2>(o1);
+      r[2][0] = tr_read_at<SV * L::TILE_B + 2 * 16 * D * 2>(o0);
+      r[2][1] = tr_read_at<SV * L::TILE_B + 2 * 16 * D * 2>(o1);
+      r[3][0] = tr_read_at<SV * L::TILE_B + 3 * 16 * D * 2>(o0);
+      r[3][1] = tr_read_at<SV * L::TILE_B + 3 * 16 * D * 2>(o1);
+    };
+    request(vf[0], 0);
+    if (with_scores) scores(SKc);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      if (dt + 1 < D / 32) {
+        request(vf[(dt + 1) & 1], dt + 1);
+        lds_wait<8>(vf[dt & 1]);
+      } else {
+        lds_wait<0>(vf[dt & 1]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vf[dt & 1][kk][0], vf[dt & 1][kk][1], 0, 1, 2, 3));
+        acc[dt] = mfma32(a8, pb[kk], acc[dt]);
+      }
+    }
+  };
+  // Vector phase of tile t (scores in s): mask, running max, probabilities,
+  // row sums. Rows whose keys are all masked keep a zero weight.
+  auto softmax = [&](const KvIter& t) __attribute__((always_inline)) {
     const int32_t band = t.band;
     const int32_t b0 = t.t * kKvTn;
     if ((b0 + kKvTn - 1 - aw > band) || (b0 + kKvTn > Bb)) {
@@ -179,7 +314,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t2][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float mt = mx * c2;  // tile max, log2 units
     if (__builtin_amdgcn_ballot_w64(mt > m + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m, mt);
@@ -191,107 +326,97 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
         for (int e = 0; e < 16; ++e) acc[dt][e] *= alpha;
       m = m_new;
     }
-    return (m == -INFINITY) ? 0.0f : m;
-  };
-  // One branch-free block: the next tile's scores (into s_next, from stage
-  // s1), this tile's probabilities (from s_cur) and O^T += V^T P^T (stage sc).
-  auto fused = [&](int sc, int s1, f32x16* s_cur, f32x16* s_next, float m_use) {
-    scores(s1, s_next);
-    const __bf16* vs = lds + sc * L::STAGE + L::TILE;
-    bf16x8 pb[4];
-    float lsum = 0.0f;
+    const float m_use = (m == -INFINITY) ? 0.0f : m;
+    // P element e of k-step kk is key 16kk + 8(e/4) + 4hf + e%4
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pv = fexp2(fmaf(s_cur[t2][e], c2, -m_use));
-        lsum += pv;
-        pb[2 * t2 + e / 8][e % 8] = (__bf16)pv;
-      }
-    l += lsum;
-    // P element e of k-step kk is key 16kk + 8(e/4) + 4hf + e%4
+      for (int e = 0; e < 16; ++e) pb[2 * t2 + e / 8][e % 8] = (__bf16)fexp2(fmaf(s[t2][e], c2, -m_use));
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 vf = cat(tr_read(vs + voff[0][dt] + 16 * kk * D), tr_read(vs + voff[1][dt] + 16 * kk * D));
-        acc[dt] = mfma32(vf, pb[kk], acc[dt]);
+      for (int e2 = 0; e2 < 4; ++e2)
+      {
+        const bf16x2 pr = {pb[kk][2 * e2], pb[kk][2 * e2 + 1]};
+        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
       }
-    if (kFwdInterleave == 2) {
-#pragma unroll
-      for (int k = 0; k < D / 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-      }
-    }
-    if (kFwdInterleave == 1) {
-      // 16 score MFMAs each followed by a K read and 6 VALU (exponentials),
-      // then the 16 P V MFMAs with their V^T reads
-#pragma unroll
-      for (int k = 0; k < D / 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
-      }
-#pragma unroll
-      for (int k = 0; k < D / 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-    }
   };
 
-  if (c0.next_block()) {
-    KvIter c1 = c0;
-    bool v1 = c1.next();
-    dma_tile(c0, 0);
-    if (v1) dma_tile(c1, 1);
-    wait_dma();
-    __syncthreads();
-    f32x16 sa[2], sb[2];
-    scores(0, sa);
-    int sc = 0;
-    // Each half: this tile's softmax runs while the next tile's score MFMAs
-    // are on the matrix pipe, and the tile after next is being copied. Two
-    // halves per trip swap the score buffers without copies. Every wave does
-    // every tile (a tile hidden from a wave by the mask is fully masked and
-    // contributes zero), which keeps the block free of branches; the last
-    // half computes scores of a stale stage and drops them.
-    while (true) {
-      {
-        KvIter c2 = c1;
-        const bool v2 = v1 && c2.next();
-        const int s1 = (sc == 2) ? 0 : sc + 1;
-        const int s2 = (s1 == 2) ? 0 : s1 + 1;
-        if (v2) dma_tile(c2, s2);
-        const float m_use = prepare(c0, sa);
-        fused(sc, s1, sa, sb, m_use);
-        if (!v1) break;
-        wait_dma();
-        __syncthreads();  // tile c2 is in LDS; stage sc is free
-        c0 = c1;
-        c1 = c2;
-        v1 = v2;
-        sc = s1;
+  KvIter first;
+  first.kstep = -1;
+  first.nsteps = (p.mode == 0) ? p.P : 1;
+  first.single_block = (p.mode == 0) ? -1 : p.step_block;
+  first.i = i;
+  first.P = p.P;
+  first.layout = p.layout;
+  first.causal = p.causal;
+  first.a_hi = a_hi;
+  first.Bb = Bb;
+  if (first.next_block()) {
+    // DMA walk: sticks at the last tile once the walk is done, so that the
+    // copies issued for tiles past the end re-read valid rows into a free
+    // stage and every wave issues the same number of loads per phase.
+    KvIter itd = first;
+    bool dvalid = true;
+    auto dadv = [&]() __attribute__((always_inline)) {
+      if (dvalid) {
+        KvIter nx = itd;
+        if (nx.next()) itd = nx;
+        else dvalid = false;
       }
-      {
-        KvIter c2 = c1;
-        const bool v2 = v1 && c2.next();
-        const int s1 = (sc == 2) ? 0 : sc + 1;
-        const int s2 = (s1 == 2) ? 0 : s1 + 1;
-        if (v2) dma_tile(c2, s2);
-        const float m_use = prepare(c0, sb);
-        fused(sc, s1, sb, sa, m_use);
-        if (!v1) break;
-        wait_dma();
-        __syncthreads();
-        c0 = c1;
-        c1 = c2;
-        v1 = v2;
-        sc = s1;
-      }
+    };
+    // prologue: tiles 0..2 (group 1 also tile 3, which group 0 requests in
+    // its first phase); tile 0's scores and probabilities
+    dma(itd, ic<0>{});
+    dadv();
+    dma(itd, ic<1>{});
+    dadv();
+    dma(itd, ic<2>{});
+    dadv();
+    if (g1) {
+      dma(itd, ic<3>{});
+      dadv();
+      wait_vm<3 * DM::NI>();
+    } else {
+      wait_vm<2 * DM::NI>();
     }
+    wg_barrier();
+    KvIter its = first;  // the tile whose scores are in s
+    scores(ic<0>{});
+    softmax(its);
+    if (g1) {
+      wait_vm<2 * DM::NI>();  // tile 1: group 0 reads it in the next phase
+      wg_barrier();
+    }
+    // Phase pair t: [matrix: scores of tile t+1, P V of tile t] then
+    // [vector: softmax of tile t+1]. Stage of tile t is t % 4.
+    auto step = [&](auto Uc) __attribute__((always_inline)) -> bool {
+      constexpr int U = decltype(Uc)::value;
+      KvIter nx = its;
+      const bool has_next = nx.next();
+      if (!g1) wait_vm<DM::NI>();  // tile t+1 (its K is read now)
+      wg_barrier();
+      if (!g1) {
+        dma(itd, ic<(U + 3) % 4>{});  // tile t+3 into the stage tile t-1 freed
+        dadv();
+      }
+      matrix(ic<(U + 1) % 4>{}, ic<U>{}, has_next);
+      if (g1) wait_vm<DM::NI>();  // tile t+2, read by group 0 in the next phase
+      wg_barrier();
+      if (g1) {
+        dma(itd, ic<U>{});  // tile t+4 into the stage tile t freed
+        dadv();
+      }
+      if (has_next) {
+        its = nx;
+        softmax(its);
+      }
+      return has_next;
+    };
+    while (step(ic<0>{}) && step(ic<1>{}) && step(ic<2>{}) && step(ic<3>{})) {
+    }
+    if (!g1) wg_barrier();  // group 1 started one barrier ahead
+    wait_vm<0>();           // no copy may land after the workgroup ends
   }
 
   // finalise: combine the two halves' sums, normalise, export
@@ -323,6 +448,12 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       }
     if (hf == 0) p.st_lse[srow + a] = (l_tot > 0.0f) ? m_use + log2f(l_tot) : -INFINITY;
   }
+}
+
+// Work order for the fp32 kernel (64-row tiles); same rule as query_tile_of.
+__device__ __forceinline__ void tile_of(const FwdParams& p, int64_t ord, int32_t tiles, int32_t* rank_idx,
+                                        int32_t* tile) {
+  query_tile_of(p.causal, p.layout, p.n_ranks, ord, tiles, rank_idx, tile);
 }
 
 // ---------------------------------------------------------------- fp32 path
@@ -444,9 +575,13 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
   const int64_t grid = tiles * p.n_ranks * p.B * p.H;
   if (grid <= 0) return hipSuccess;
   if (p.D == 128) {
-    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((uint32_t)grid), dim3(kQThreads), KvLds<128>::BYTES, s, p);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<128>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, FwdLds<128>::BYTES);
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, dim3((uint32_t)grid), dim3(kQThreads), FwdLds<128>::BYTES, s, p);
   } else {
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((uint32_t)grid), dim3(kQThreads), KvLds<64>::BYTES, s, p);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, FwdLds<64>::BYTES);
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((uint32_t)grid), dim3(kQThreads), FwdLds<64>::BYTES, s, p);
   }
   return hipGetLastError();
 }
