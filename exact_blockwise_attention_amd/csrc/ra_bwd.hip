@@ -209,13 +209,32 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         const bf16x8 vb = *reinterpret_cast<const bf16x8*>(lds + L::V + roff[ss] + 32 * kg * D);
         dp = mfma32(oa, vb, dp);
       }
-      // lane (hf, n): key n against rows 8(i/4) + 4hf + i%4 of the wave's 32
+      // lane (hf, n): key n against rows 8(i/4) + 4hf + i%4 of the wave's 32.
+      // lse and D of rows 8g + 4hf .. +3 are read one group ahead (inline
+      // LDS reads: see lds_read16).
       bf16x8 pb[2], dsb[2];
+      const uint32_t la = lds_addr(lse_s + 32 * qh + 4 * hf), dla = lds_addr(dsum_s + 32 * qh + 4 * hf);
+      u32x4 ldr[2][2];  // [slot][lse, D]
+      auto ld_rows = [&](u32x4(&r)[2], int g) __attribute__((always_inline)) {
+        switch (g) {
+          case 0: r[0] = lds_read16<0>(la); r[1] = lds_read16<0>(dla); break;
+          case 1: r[0] = lds_read16<32>(la); r[1] = lds_read16<32>(dla); break;
+          case 2: r[0] = lds_read16<64>(la); r[1] = lds_read16<64>(dla); break;
+          default: r[0] = lds_read16<96>(la); r[1] = lds_read16<96>(dla); break;
+        }
+      };
+      ld_rows(ldr[0], 0);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        if (g + 1 < 4) {
+          ld_rows(ldr[(g + 1) & 1], g + 1);
+          lds_wait<2>(ldr[g & 1]);
+        } else {
+          lds_wait<0>(ldr[g & 1]);
+        }
         const int qr0 = 32 * qh + 8 * g + 4 * hf;  // row within the 64-row tile
-        const float4 l4 = *reinterpret_cast<const float4*>(lse_s + qr0);
-        const float4 d4 = *reinterpret_cast<const float4*>(dsum_s + qr0);
+        const float4 l4 = __builtin_bit_cast(float4, ldr[g & 1][0]);
+        const float4 d4 = __builtin_bit_cast(float4, ldr[g & 1][1]);
         const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
         const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
@@ -231,17 +250,43 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
           dsb[g / 2][4 * (g % 2) + e] = (__bf16)dsv;
         }
       }
-      // dV^T += dO^T P, dK^T += Q^T dS: contraction over the wave's 32 rows
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          const int rows = (32 * qh + 16 * kq) * D;
-          const bf16x8 ot = cat(tr_read(os + toff[0][dt] + rows), tr_read(os + toff[1][dt] + rows));
-          const bf16x8 qt = cat(tr_read(qs + toff[0][dt] + rows), tr_read(qs + toff[1][dt] + rows));
-          dv[dt] = mfma32(ot, pb[kq], dv[dt]);
-          dk[dt] = mfma32(qt, dsb[kq], dk[dt]);
+      // dV^T += dO^T P, dK^T += Q^T dS: contraction over the wave's 32 rows.
+      // The transposing reads of (dt, kq) come in groups of 4, one group
+      // ahead of their MFMAs (inline LDS reads: see tr_read_at).
+      const uint32_t oa = lds_addr(os + 32 * qh * D), qa = lds_addr(qs + 32 * qh * D);
+      auto tr_group = [&](u32x2(&r)[2][2], int idx) __attribute__((always_inline)) {
+        const int dt = idx / 2;
+        const uint32_t o0 = oa + 2 * toff[0][dt], o1 = oa + 2 * toff[1][dt];
+        const uint32_t q0a = qa + 2 * toff[0][dt], q1a = qa + 2 * toff[1][dt];
+        if (idx % 2 == 0) {
+          r[0][0] = tr_read_at<0>(o0);
+          r[0][1] = tr_read_at<0>(o1);
+          r[1][0] = tr_read_at<0>(q0a);
+          r[1][1] = tr_read_at<0>(q1a);
+        } else {
+          r[0][0] = tr_read_at<16 * D * 2>(o0);
+          r[0][1] = tr_read_at<16 * D * 2>(o1);
+          r[1][0] = tr_read_at<16 * D * 2>(q0a);
+          r[1][1] = tr_read_at<16 * D * 2>(q1a);
         }
+      };
+      constexpr int NG = 2 * (D / 32);
+      u32x2 trg[2][2][2];
+      tr_group(trg[0], 0);
+#pragma unroll
+      for (int idx = 0; idx < NG; ++idx) {
+        if (idx + 1 < NG) {
+          tr_group(trg[(idx + 1) & 1], idx + 1);
+          lds_wait<4>(trg[idx & 1]);
+        } else {
+          lds_wait<0>(trg[idx & 1]);
+        }
+        const int dt = idx / 2, kq = idx % 2;
+        const bf16x8 ot = __builtin_bit_cast(bf16x8, __builtin_shufflevector(trg[idx & 1][0][0], trg[idx & 1][0][1], 0, 1, 2, 3));
+        const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(trg[idx & 1][1][0], trg[idx & 1][1][1], 0, 1, 2, 3));
+        dv[dt] = mfma32(ot, pb[kq], dv[dt]);
+        dk[dt] = mfma32(qt, dsb[kq], dk[dt]);
+      }
     }
     if (!more) break;
     wait_dma();

@@ -16,6 +16,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ra_internal.h"
 #include "ra_kvwalk.h"
 #include "ra_lds.h"
@@ -25,6 +27,9 @@ namespace ra {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 template <int D>
 __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
@@ -128,67 +133,90 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   };
   const float c2 = p.scale_log2;
   // dS^T from the half's scores, then dQ^T += K^T dS^T
-  auto consume = [&](const KvIter& t, int stage, int half, f32x16* sd) {
+  auto consume = [&](const KvIter& t, int stage, auto HALFc, f32x16* sd) __attribute__((always_inline)) {
+    constexpr int half = decltype(HALFc)::value;
     const int32_t band = t.band;
     const int32_t b0 = t.t * kKvTn + 32 * half;
-    const __bf16* ks = lds + stage * L::STAGE;
+    const uint32_t kb = lds_addr(lds + stage * L::STAGE);
     const bool need_mask = (b0 + 31 - aw > band) || (b0 + 32 > Bb);
     bf16x8 dsb[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float pv = fexp2(fmaf(sd[0][e], c2, -lse2));
       if (need_mask) {
-        const int32_t kb = b0 + 8 * (e / 4) + 4 * hf + (e % 4);
-        if (kb - a > band || kb >= Bb) pv = 0.0f;
+        const int32_t key = b0 + 8 * (e / 4) + 4 * hf + (e % 4);
+        if (key - a > band || key >= Bb) pv = 0.0f;
       }
       dsb[e / 8][e % 8] = (__bf16)(pv * (sd[1][e] - dsum));
     }
-    // dS element e of k-step 2 half + u is key 16(2 half + u) + 8(e/4) + 4hf + e%4
+    // dS element e of k-step 2 half + u is key 16(2 half + u) + 8(e/4) + 4hf + e%4.
+    // K^T fragments in groups of 4 reads (one 32-feature block)
+    constexpr int R0 = 16 * (2 * half) * D * 2, R1 = 16 * (2 * half + 1) * D * 2;  // bytes
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt) {
+      u32x2 g[2][2];
+      const uint32_t a0 = kb + 2 * toff[0][dt], a1 = kb + 2 * toff[1][dt];
+      g[0][0] = tr_read_at<R0>(a0);
+      g[0][1] = tr_read_at<R0>(a1);
+      g[1][0] = tr_read_at<R1>(a0);
+      g[1][1] = tr_read_at<R1>(a1);
+      lds_wait<0>(g);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int rows = 16 * (2 * half + u) * D;
-        const bf16x8 kt = cat(tr_read(ks + toff[0][dt] + rows), tr_read(ks + toff[1][dt] + rows));
+        const bf16x8 kt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(g[u][0], g[u][1], 0, 1, 2, 3));
         acc[dt] = mfma32(kt, dsb[u], acc[dt]);
       }
+    }
   };
 
+  // copies per K/V tile per wave (K and V), for the counted waits below
+  constexpr int NI = 2 * (kKvTn / (1024 / (2 * D))) / kQWaves;
   if (c0.next_block()) {
-    KvIter c1 = c0;
-    bool v1 = c1.next();
+    KvIter c1 = c0, c2;
+    const bool v1 = c1.next();
+    bool v2 = false;
+    if (v1) {
+      c2 = c1;
+      v2 = c2.next();
+    }
     dma_tile(c0, 0);
     if (v1) dma_tile(c1, 1);
-    wait_dma();
+    if (v2) dma_tile(c2, 2);
+    if (v2) wait_vm<NI>();  // tiles c0 and c1 are needed now, c2 may stay in flight
+    else wait_dma();
     __syncthreads();
     f32x16 sa[2], sb[2];  // scores of half 0 / half 1 of a tile
     bool da = dead(c0);
     if (!da) produce(0, 0, sa);
     int sc = 0;
+    bool w1 = v1, w2 = v2;
     // the MFMA pipe gets the next half's products before the current half's
-    // exponentials are computed; the tile after next is copied meanwhile
+    // exponentials are computed; a ring of four stages holds the tile, the
+    // next one and two more in flight
     while (true) {
-      KvIter c2 = c1;
-      const bool v2 = v1 && c2.next();
-      const int s1 = (sc == 2) ? 0 : sc + 1;
-      const int s2 = (s1 == 2) ? 0 : s1 + 1;
-      if (v2) dma_tile(c2, s2);
+      KvIter c3 = c2;
+      const bool v3 = w2 && c3.next();
+      const int s1 = (sc + 1) & 3;
+      if (v3) dma_tile(c3, (sc + 3) & 3);  // the stage the previous tile freed
       if (!da) {
         produce(sc, 1, sb);
-        consume(c0, sc, 0, sa);
+        consume(c0, sc, ic<0>{}, sa);
       }
       bool db = true;
-      if (v1) {
+      if (w1) {
         db = dead(c1);
         if (!db) produce(s1, 0, sa);
       }
-      if (!da) consume(c0, sc, 1, sb);
-      if (!v1) break;
-      wait_dma();
-      __syncthreads();  // tile c2 is in LDS; stage sc is free
+      if (!da) consume(c0, sc, ic<1>{}, sb);
+      if (!w1) break;
+      if (v3) wait_vm<NI>();  // tile c2 (read from the next step on) is in LDS
+      else wait_dma();
+      __syncthreads();  // stage sc is free
       c0 = c1;
       c1 = c2;
-      v1 = v2;
+      c2 = c3;
+      w1 = w2;
+      w2 = v3;
       da = db;
       sc = s1;
     }
@@ -297,8 +325,12 @@ hipError_t launch_dq_bf16(const BwdParams& p, hipStream_t s) {
   const int64_t grid = ((p.Bb + kQTm - 1) / kQTm) * (int64_t)p.n_ranks * p.B * p.H;
   if (grid <= 0) return hipSuccess;
   if (p.D == 128) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dq_bf16_kernel<128>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, KvLds<128>::BYTES);
     hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3((uint32_t)grid), dim3(kQThreads), KvLds<128>::BYTES, s, p);
   } else {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(dq_bf16_kernel<64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, KvLds<64>::BYTES);
     hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3((uint32_t)grid), dim3(kQThreads), KvLds<64>::BYTES, s, p);
   }
   return hipGetLastError();

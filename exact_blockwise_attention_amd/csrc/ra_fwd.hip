@@ -72,12 +72,6 @@ struct FwdDma {
   static_assert(CPW >= 1 && (kKvTn / RW) % kQWaves == 0, "tile copies must split over the waves");
 };
 
-// Waits until at most N vector-memory loads of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Workgroup barrier without the implicit memory waits of __syncthreads: the
 // kernel waits for exactly the loads it needs before each barrier.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -89,28 +83,6 @@ __device__ __forceinline__ float halves_max(float x) {
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Transposing LDS read (ds_read_b64_tr_b16) at addr + OFF bytes. Issued as
-// inline assembly: the compiler would otherwise wait for every outstanding
-// global-to-LDS copy before it (it cannot tell that the copies target other
-// stages). The caller waits for the result with lds_wait().
-template <int OFF>
-__device__ __forceinline__ u32x2 tr_read_at(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "DS offsets are 16 bits");
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
-}
-
-// Waits until at most N LDS reads of this wave are outstanding (LDS reads
-// complete in order); the operands are tied so that their uses stay after.
-template <int N>
-__device__ __forceinline__ void lds_wait(u32x2 (&r)[4][2]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1]), "+v"(r[2][0]), "+v"(r[2][1]),
-                 "+v"(r[3][0]), "+v"(r[3][1])
-               : "n"(N));
-}
 
 template <int D>
 __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
@@ -180,8 +152,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 
   // per-lane byte offsets inside a stage: K rows n (+32t) at columns
-  // 16ss + 8hf; V^T transposing reads at rows 4hf + j16/4 (+8) (+16kk) and
-  // columns 32dt + 16grp + 4(j16%4)
+  // 16ss + 8hf; V^T transposing reads (LDS addresses of stage 0) at rows
+  // 4hf + j16/4 (+8) (+16kk) and columns 32dt + 16grp + 4(j16%4)
   uint32_t koff[D / 16], voff[2][D / 32];
 #pragma unroll
   for (int ss = 0; ss < D / 16; ++ss) koff[ss] = 2 * tile_off<D>(n, 16 * ss + 8 * hf);
@@ -189,7 +161,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
-      voff[h2][dt] = L::VBASE_B + 2 * tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
+      voff[h2][dt] = lds_addr(smem_raw) + L::VBASE_B +
+                     2 * tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
 
   // per-lane source offsets (bytes, from the tile's first row) of the rows
   // this wave copies, and their swizzled chunk

@@ -9,8 +9,8 @@
 // workgroup can see under the causal / striped mask ("Ring Attention 論文分析"
 // (blog), section "Causal Masking の処理": later blocks skipped, the diagonal
 // masked); a single-step launch visits one given block only. KV tiles go
-// straight from global memory to a ring of three LDS stages, two tiles ahead
-// of the one whose softmax is being computed.
+// straight from global memory to a ring of LDS stages, requested a few tiles
+// ahead of their use.
 #ifndef RA_KVWALK_H_
 #define RA_KVWALK_H_
 
@@ -26,12 +26,12 @@ constexpr int kQTm = 32 * kQWaves;  // query rows per workgroup
 constexpr int kKvTn = 64;           // keys per KV tile
 constexpr int kBandAll = 1 << 30;
 
-// LDS: three stages of (K tile, V tile), each [64][D] swizzled.
+// LDS: four stages of (K tile, V tile), each [64][D] swizzled.
 template <int D>
 struct KvLds {
   static constexpr int TILE = kKvTn * D;
   static constexpr int STAGE = 2 * TILE;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = 4;
   static constexpr int BYTES = NSTAGE * STAGE * 2;
 };
 
@@ -131,6 +131,13 @@ __device__ __forceinline__ void dma_f32_64(float* tile, const float* base, int32
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Waits until at most N vector-memory loads of this wave are outstanding
+// (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 }  // namespace ra
 

@@ -85,6 +85,63 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Byte address in LDS of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS reads issued as inline assembly, at LDS byte address addr + OFF. The
+// compiler, which cannot tell that the direct global-to-LDS copies in flight
+// target other buffers, would wait for all of them before the equivalent
+// builtins; for these reads it does not know, so the caller waits for the
+// results itself with lds_wait*(). LDS reads complete in issue order, so
+// waiting until at most N are outstanding, with N the number of reads issued
+// after the ones needed, is enough whatever else is in flight.
+template <int OFF>
+__device__ __forceinline__ u32x2 tr_read_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offsets are 16 bits");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS offsets are 16 bits");
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(N) with the registers about to be used tied to it, so
+// that their uses stay after the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2 (&r)[4][2]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1]), "+v"(r[2][0]), "+v"(r[2][1]),
+                 "+v"(r[3][0]), "+v"(r[3][1])
+               : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x2 (&r)[2][2]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0][0]), "+v"(r[0][1]), "+v"(r[1][0]), "+v"(r[1][1]) : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&r)[2]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r[0]), "+v"(r[1]) : "n"(N));
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&r)[4]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
+}
+
 }  // namespace ra
 
 #endif  // RA_LDS_H_
