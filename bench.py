@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--layout", default=None, help="workload 3: contiguous or striped")
+    ap.add_argument("--layout", default=None, help="workloads 3 and 5: contiguous, striped or zigzag")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the library's layout copy with one block) three "
@@ -66,7 +66,9 @@ def calibrate_copy():
 def pair_count(layout, causal, P, Bb, ranks):
     """Visible (query, key) pairs of the given ranks' query blocks, per head:
     a striped block pair (i, j) sees b <= a - [j > i], a contiguous one all
-    (j < i), the lower triangle (j == i) or nothing (j > i)."""
+    (j < i), the lower triangle (j == i) or nothing (j > i); a zigzag one the
+    lower triangle (j == i) or Bb * Bb/2 pairs (j < i: every row sees the
+    first half-block; j > i: the second half of the rows sees every key)."""
     total = 0
     for i in ranks:
         for kstep in range(P):
@@ -75,6 +77,8 @@ def pair_count(layout, causal, P, Bb, ranks):
                 total += Bb * Bb
             elif layout == "striped":
                 total += Bb * (Bb + 1) // 2 if j <= i else Bb * (Bb - 1) // 2
+            elif layout == "zigzag":
+                total += Bb * (Bb + 1) // 2 if j == i else Bb * (Bb // 2)
             elif j < i:
                 total += Bb * Bb
             elif j == i:
@@ -107,6 +111,14 @@ def read_traffic(kernel_tag):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def workload_name(w, layout):
+    """The workload's name with the layout actually run in it."""
+    for other in ("contiguous", "striped", "zigzag"):
+        if f"_{other}_" in w.name:
+            return w.name.replace(f"_{other}_", f"_{layout}_")
+    return w.name.replace("causal_", f"causal_{layout}_", 1) if w.causal else w.name
 
 
 def cpu_baseline(w):
@@ -180,6 +192,9 @@ def main():
             return torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
         return torch.from_numpy(x).to("cuda")
 
+    blocked = layout == "zigzag"  # zigzag blocks are not strided slices: keep blocked copies resident
+    if blocked and w.q_ranks:
+        raise SystemExit("the one-device share is run in the striped layout")
     t = {}
     for n in names:
         pay = syn.make_payload(w.wid, n, shape, w.dtype)
@@ -188,6 +203,12 @@ def main():
             x = np.arange(Bb)
             pos = x * P + rb if layout == "striped" else rb * Bb + x
             pay = np.ascontiguousarray(pay[:, pos])
+        if blocked:
+            # blocked order [P, B, Bb, H, d]: block s holds half-blocks s and 2P-1-s
+            hb = Bb // 2
+            perm = np.concatenate([np.r_[s_ * hb:(s_ + 1) * hb, (2 * P - 1 - s_) * hb:(2 * P - s_) * hb]
+                                   for s_ in range(P)])
+            pay = np.ascontiguousarray(pay[:, perm].reshape(w.batch, P, Bb, w.heads, d).transpose(1, 0, 2, 3, 4))
         t[n] = dev(pay)
         del pay
     torch.cuda.synchronize()
@@ -198,11 +219,15 @@ def main():
     sh = ra._stream_handle(stream)
     copy_stream = torch.cuda.Stream() if w.prefetch else None
     ch = ra._stream_handle(copy_stream) if copy_stream is not None else None
-    if w.q_ranks:
+    if blocked:
+        so = lambda x: ra.seq_blocked(x, block_offset=rb)  # noqa: E731
+        sk = ra.seq_blocked
+    elif w.q_ranks:
         so = lambda x: ra._seq_rank_rows(x, re_ - rb, layout, P)  # noqa: E731
     else:
         so = lambda x: ra.seq_original(x, P, layout, block_offset=rb)  # noqa: E731
-    sk = lambda x: ra.seq_original(x, P, layout)  # noqa: E731
+    if not blocked:
+        sk = lambda x: ra.seq_original(x, P, layout)  # noqa: E731
     o = torch.empty_like(t["q"])
     nr = re_ - rb
     lse = torch.empty((nr, w.batch, w.heads, Bb), dtype=torch.float32, device="cuda")
@@ -284,12 +309,12 @@ def main():
         roof["note"] = "one call of 8 step launches plus the side-stream copies, timed as a whole"
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     out = {
-        "metric": "attention TFLOP/s fwd+bwd (causal striped, d=128) and % of bf16 MFMA peak" if bwd else
-                  f"attention forward TFLOP/s ({w.name})",
+        "metric": f"attention TFLOP/s fwd+bwd (causal {layout}, d=128) and % of bf16 MFMA peak" if bwd else
+                  f"attention forward TFLOP/s ({workload_name(w, layout)})",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "head_dim": d,
+        "config": {"workload": workload_name(w, layout), "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "head_dim": d,
                    "ring_size": P, "block_len": Bb, "layout": layout, "causal": w.causal,
                    "ranks": [rb, re_], "passes": list(w.passes), "prefetch": w.prefetch},
         "frac_of_peak": round(value / peak, 4),

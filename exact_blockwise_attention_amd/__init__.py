@@ -22,13 +22,14 @@ import os
 __all__ = [
     "LAYOUT_CONTIGUOUS", "LAYOUT_STRIPED", "F32", "BF16", "Problem", "Seq", "RaError",
     "library", "library_path", "workspace_bytes", "forward_raw", "backward_raw", "merge_lse_raw",
-    "layout_copy_raw", "status_string", "abi_version", "seq_original", "seq_blocked",
+    "layout_copy_raw", "status_string", "abi_version", "seq_original", "seq_blocked", "LAYOUTS",
     "attention_forward", "attention_backward", "merge_lse", "layout_copy", "EXPORTED_FUNCTIONS",
 ]
 
 LAYOUT_CONTIGUOUS = 0
 LAYOUT_STRIPED = 1
-LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED}
+LAYOUT_ZIGZAG = 2
+LAYOUTS = {"contiguous": LAYOUT_CONTIGUOUS, "striped": LAYOUT_STRIPED, "zigzag": LAYOUT_ZIGZAG}
 F32 = 0
 BF16 = 1
 
@@ -186,6 +187,8 @@ def seq_original(t, ring_size: int, layout: str, block_offset: int = 0) -> Seq:
     if L % ring_size:
         raise ValueError("sequence must split into equal blocks")
     Bb = L // ring_size
+    if layout == "zigzag":
+        raise ValueError("a zigzag block is not a strided slice of the original order: use blocked tensors")
     if layout == "striped":
         s_blk, s_tok = sl, ring_size * sl
     else:
@@ -194,13 +197,24 @@ def seq_original(t, ring_size: int, layout: str, block_offset: int = 0) -> Seq:
     return Seq(ptr, s_blk, sb, s_tok, sh)
 
 
-def seq_blocked(t) -> Seq:
-    """Describe a blocked [P, B, Bb, H, d] tensor."""
+def seq_blocked(t, block_offset: int = 0) -> Seq:
+    """Describe a blocked [P, B, Bb, H, d] tensor (block ``block_offset`` first)."""
     P, B, Bb, H, d = t.shape
     s = t.stride()
     if s[4] != 1:
         raise ValueError("features must be contiguous")
-    return Seq(t.data_ptr(), s[0], s[1], s[2], s[3])
+    return Seq(t.data_ptr() + block_offset * s[0] * t.element_size(), s[0], s[1], s[2], s[3])
+
+
+def _seq_for(t, P, layout, block_offset=0):
+    """Ring-block description of an original-order tensor; for the zigzag
+    layout a blocked copy (made with the library's layout copy) is described
+    instead and returned alongside, so that the caller can keep it alive or
+    copy results back."""
+    if layout == "zigzag":
+        tb = layout_copy(t, P, layout)
+        return seq_blocked(tb, block_offset), tb
+    return seq_original(t, P, layout, block_offset=block_offset), None
 
 
 def make_problem(B, H, d, P, Bb, layout, causal, dtype_code, scale=None) -> Problem:
@@ -235,11 +249,24 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     need = workspace_bytes(pb, rb, re, use_copy, False)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    qs = seq_original(q, P, layout, block_offset=rb) if q.shape[1] == L else _seq_rank_rows(q, nr, layout, P)
-    os_ = seq_original(out, P, layout, block_offset=rb) if out.shape[1] == L else _seq_rank_rows(out, nr, layout, P)
-    forward_raw(pb, rb, re, qs, seq_original(k, P, layout), seq_original(v, P, layout), os_,
+    keep = []
+    if q.shape[1] == L:
+        qs, t_ = _seq_for(q, P, layout, rb)
+        keep.append(t_)
+    else:
+        qs = _seq_rank_rows(q, nr, layout, P)
+    ob = None
+    if out.shape[1] == L:
+        os_, ob = _seq_for(out, P, layout, rb)
+    else:
+        os_ = _seq_rank_rows(out, nr, layout, P)
+    ks, kb = _seq_for(k, P, layout)
+    vs, vb = _seq_for(v, P, layout)
+    forward_raw(pb, rb, re, qs, ks, vs, os_,
                 lse.data_ptr(), workspace.data_ptr() if need else None, need, _stream_handle(None),
                 _stream_handle(copy_stream) if use_copy else None)
+    if ob is not None:  # zigzag: blocked result back to the original order
+        out.copy_(layout_copy(ob, P, layout, inverse=True))
     return out, lse
 
 
@@ -270,10 +297,15 @@ def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "conti
     need = workspace_bytes(pb, rb, re, False, True)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    so = lambda t: seq_original(t, P, layout, block_offset=rb)  # noqa: E731
-    sk = lambda t: seq_original(t, P, layout)  # noqa: E731
-    backward_raw(pb, rb, re, so(q), sk(k), sk(v), so(o), so(do), lse.data_ptr(), so(dq), sk(dk), sk(dv),
+    (qs, _q), (os_, _o), (ds, _d) = (_seq_for(t, P, layout, rb) for t in (q, o, do))
+    (ks, _k), (vs, _v) = (_seq_for(t, P, layout) for t in (k, v))
+    (dqs, dqb), (dks, dkb), (dvs, dvb) = (_seq_for(dq, P, layout, rb), _seq_for(dk, P, layout),
+                                          _seq_for(dv, P, layout))
+    backward_raw(pb, rb, re, qs, ks, vs, os_, ds, lse.data_ptr(), dqs, dks, dvs,
                  workspace.data_ptr(), need, _stream_handle(None))
+    if layout == "zigzag":  # blocked results back to the original order
+        for t, tb in ((dq, dqb), (dk, dkb), (dv, dvb)):
+            t.copy_(layout_copy(tb, P, layout, inverse=True))
     return dq, dk, dv
 
 

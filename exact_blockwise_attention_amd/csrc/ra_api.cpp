@@ -28,7 +28,9 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 ra_status check_problem(const ra_problem* pb, int32_t rb, int32_t re) {
   if (!pb) return RA_ERR_NULL;
   if (pb->batch < 1 || pb->heads < 1 || pb->ring_size < 1 || pb->block_len < 1) return RA_ERR_SHAPE;
-  if (pb->layout != RA_LAYOUT_CONTIGUOUS && pb->layout != RA_LAYOUT_STRIPED) return RA_ERR_SHAPE;
+  if (pb->layout != RA_LAYOUT_CONTIGUOUS && pb->layout != RA_LAYOUT_STRIPED && pb->layout != RA_LAYOUT_ZIGZAG)
+    return RA_ERR_SHAPE;
+  if (pb->layout == RA_LAYOUT_ZIGZAG && pb->block_len % 2) return RA_ERR_SHAPE;  // two half-blocks
   if (pb->causal != 0 && pb->causal != 1) return RA_ERR_SHAPE;
   if (pb->dtype != RA_F32 && pb->dtype != RA_BF16) return RA_ERR_SHAPE;
   if (!(pb->scale == pb->scale) || isinf(pb->scale)) return RA_ERR_SHAPE;  // NaN / inf
@@ -43,6 +45,8 @@ ra_status check_problem(const ra_problem* pb, int32_t rb, int32_t re) {
   if (t3 / 64 > (int64_t)INT32_MAX) return RA_ERR_SHAPE;
   return RA_OK;
 }
+
+constexpr int64_t kMaxTokStride = int64_t(1) << 25;  // elements
 
 ra_status check_seq(const ra_seq* s, int32_t es) {
   if (!s || !s->ptr) return RA_ERR_NULL;
@@ -136,6 +140,8 @@ ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
     if ((st = check_seq(s, es)) != RA_OK) return st;
   if (!lse) return RA_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4) return RA_ERR_ALIGN;
+  // the bf16 forward addresses the rows of a 64-row K/V tile with 32-bit byte offsets
+  if (pb->dtype == RA_BF16 && (k->s_tok > kMaxTokStride || v->s_tok > kMaxTokStride)) return RA_ERR_UNSUPPORTED;
   const int32_t n = rank_end - rank_begin;
   const bool use_copy = copy != nullptr;
   if (use_copy && n != 1) return RA_ERR_SHAPE;

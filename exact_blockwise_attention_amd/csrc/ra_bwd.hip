@@ -35,7 +35,6 @@
 namespace ra {
 namespace {
 
-constexpr int kBandAllKeys = 1 << 30;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 constexpr int kWaves = 8;
@@ -69,17 +68,17 @@ __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int3
 
 // The (rank, query tile) pairs a KV tile meets, in ring order.
 struct QTileIter {
-  int32_t kstep, i, qt, qtiles, band;
-  int32_t j, P, rb, re, layout, causal, kv0;
+  int32_t kstep, i, qt, qtiles;
+  int32_t j, P, rb, re, layout, causal, kv0, Bb;
   __device__ bool step_rank() {
     while (++kstep < P) {
       i = ring_rank(j, kstep, P);
       if (i < rb || i >= re) continue;
-      const BlockRel rel = block_relation(layout, causal, i, j);
-      if (rel.kind == kNone) continue;
-      band = (rel.kind == kAll) ? kBandAllKeys : rel.band;
-      int32_t a_first = (rel.kind == kAll) ? 0 : kv0 - band;  // first row any key can see
-      if (a_first < 0) a_first = 0;
+      const BlockRel rel = block_relation(layout, causal, i, j, Bb);
+      // the first row that sees the tile's first key is the first row that
+      // sees any of its keys
+      const int32_t a_first = first_row_seeing32(rel, kv0, Bb);
+      if (a_first >= Bb) continue;
       qt = a_first / kQm;
       if (qt < qtiles) return true;
     }
@@ -168,6 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   cur.layout = p.layout;
   cur.causal = p.causal;
   cur.kv0 = kv0;
+  cur.Bb = Bb;
   const bool any = cur.step_rank();
   if (any) dma_qtile<D>(p, cur, b, h, lds, f32s, 0, wave, lane);
   wait_dma();  // K, V and the first query tile
@@ -189,16 +189,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     const bool more = nx.next();
     if (more) dma_qtile<D>(p, nx, b, h, lds, f32s, stage ^ 1, wave, lane);  // lands during the compute below
 
-    const int32_t band = cur.band;
+    const BlockRel rel = block_relation(p.layout, p.causal, cur.i, j, Bb);
     const int32_t q0 = cur.qt * kQm;
     const int32_t qw = q0 + 32 * qh;  // first row of this wave
     const __bf16* qs = lds + L::Q + stage * kQm * D;
     const __bf16* os = lds + L::DO + stage * kQm * D;
     const float* lse_s = f32s + stage * kQm;
     const float* dsum_s = f32s + 2 * kQm + stage * kQm;
-    const bool dead = (kw >= Bb) || (qw >= Bb) || (kw - (qw + 31) > band);
+    // row extents grow with the row: the wave's last row sees the most keys,
+    // its first row the fewest
+    const bool dead = (kw >= Bb) || (qw >= Bb) || (row_extent32(rel, qw + 31) <= kw);
     if (!dead) {
-      const bool need_mask = (kw + 31 - qw > band) || (qw + 32 > Bb) || (kw + 32 > Bb);
+      const bool need_mask = (row_extent32(rel, qw) < kw + 32) || (qw + 32 > Bb);
+      // rows a >= a_min see this lane's key (only needed when masking)
+      const int32_t a_min = need_mask ? first_row_seeing32(rel, key, Bb) : 0;
       f32x16 s = {}, dp = {};
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
           float pv = fexp2(fmaf(s[i], c2, -lv[e]));
           if (need_mask) {
             const int32_t a = q0 + qr0 + e;
-            if (key - a > band || a >= Bb || key >= Bb) pv = 0.0f;
+            if (a < a_min || a >= Bb) pv = 0.0f;
           }
           const float dsv = pv * (dp[i] - dd[e]);
           pb[g / 2][4 * (g % 2) + e] = (__bf16)pv;
@@ -398,11 +402,11 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
     const int32_t i = ring_rank(j, kstep, p.P);
     if (i < p.rank_begin || i >= p.rank_begin + p.n_ranks) continue;
     const int32_t ri = i - p.rank_begin;
-    const BlockRel rel = block_relation(p.layout, p.causal, i, j);
+    const BlockRel rel = block_relation(p.layout, p.causal, i, j, (int32_t)p.Bb);
     if (rel.kind == kNone) continue;
-    const int32_t band = (rel.kind == kAll) ? kBandAllKeys : rel.band;
-    int64_t a_first = (rel.kind == kAll) ? 0 : kv0 - band;
-    if (a_first < 0) a_first = 0;
+    const int64_t a_first = first_row_seeing(rel, kv0, p.Bb);  // first row that sees the tile
+    if (a_first >= p.Bb) continue;
+    const int64_t a_min = first_row_seeing(rel, key, p.Bb);  // rows a >= a_min see this lane's key
     const float* qbase = reinterpret_cast<const float*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
     const float* dobase = reinterpret_cast<const float*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch + h * p.dout.s_head;
     const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
@@ -423,7 +427,7 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
       __syncthreads();
       for (int r = 0; r < kF32Rows; ++r) {
         const int64_t a = q0 + r;
-        const bool vis = key < p.Bb && a < p.Bb && key - a <= (int64_t)band;
+        const bool vis = key < p.Bb && a < p.Bb && a >= a_min;
         float s = 0.0f, dpv = 0.0f;
 #pragma unroll
         for (int e = 0; e < D; ++e) {

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
     dma_rows<D, kKvTn, kQWaves>(st, kv_base(p.k, t.j), p.k.s_tok, t.t * kKvTn, Bb, wave, lane);
     dma_rows<D, kKvTn, kQWaves>(st + L::TILE, kv_base(p.v, t.j), p.v.s_tok, t.t * kKvTn, Bb, wave, lane);
   };
-  auto dead = [&](const KvIter& t) { return (aw >= Bb) || (t.t * kKvTn - (aw + 31) > t.band); };
+  // no row of the wave sees the tile's first key (row extents grow with the row)
+  auto dead = [&](const KvIter& t) { return (aw >= Bb) || (row_extent32(t.rel, aw + 31) <= t.t * kKvTn); };
   // S^T = K Q^T and dP^T = V dO^T for keys 32 half .. +31 of a tile
   auto produce = [&](int stage, int half, f32x16* sd) {
     const __bf16* ks = lds + stage * L::STAGE;
@@ -135,17 +136,18 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   // dS^T from the half's scores, then dQ^T += K^T dS^T
   auto consume = [&](const KvIter& t, int stage, auto HALFc, f32x16* sd) __attribute__((always_inline)) {
     constexpr int half = decltype(HALFc)::value;
-    const int32_t band = t.band;
     const int32_t b0 = t.t * kKvTn + 32 * half;
     const uint32_t kb = lds_addr(lds + stage * L::STAGE);
-    const bool need_mask = (b0 + 31 - aw > band) || (b0 + 32 > Bb);
+    // the wave's first row sees the fewest keys; extents never exceed Bb
+    const bool need_mask = row_extent32(t.rel, aw) < b0 + 32;
+    const int32_t ext_a = row_extent32(t.rel, a);
     bf16x8 dsb[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float pv = fexp2(fmaf(sd[0][e], c2, -lse2));
       if (need_mask) {
         const int32_t key = b0 + 8 * (e / 4) + 4 * hf + (e % 4);
-        if (key - a > band || key >= Bb) pv = 0.0f;
+        if (key >= ext_a) pv = 0.0f;
       }
       dsb[e / 8][e % 8] = (__bf16)(pv * (sd[1][e] - dsum));
     }
@@ -278,10 +280,10 @@ __global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
   const float c2 = p.scale_log2;
   for (int32_t kstep = 0; kstep < p.P; ++kstep) {
     const int32_t j = ring_block(i, kstep, p.P);
-    const BlockRel rel = block_relation(p.layout, p.causal, i, j);
+    const BlockRel rel = block_relation(p.layout, p.causal, i, j, Bb);
     const int64_t extent = visible_key_extent(rel, a_hi, p.Bb);
     if (extent <= 0) continue;
-    const int32_t band = (rel.kind == kAll) ? kBandAll : rel.band;
+    const int32_t ext_a = row_extent32(rel, a);  // this row sees keys 0 .. ext_a - 1
     const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + (int64_t)j * p.k.s_blk + b * p.k.s_batch +
                          h * p.k.s_head;
     const float* vbase = reinterpret_cast<const float*>(p.v.ptr) + (int64_t)j * p.v.s_blk + b * p.v.s_batch +
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
           s = fmaf(qv[e], ks[u][e], s);
           dpv = fmaf(ov[e], vs[u][e], dpv);
         }
-        const bool vis = kb - a <= band && kb < Bb;
+        const bool vis = kb < ext_a;
         const float pv = vis ? fexp2(fmaf(s, c2, -lse2)) : 0.0f;
         const float dsv = pv * (dpv - dsum);
 #pragma unroll

@@ -268,12 +268,12 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   // Vector phase of tile t (scores in s): mask, running max, probabilities,
   // row sums. Rows whose keys are all masked keep a zero weight.
   auto softmax = [&](const KvIter& t) __attribute__((always_inline)) {
-    const int32_t band = t.band;
     const int32_t b0 = t.t * kKvTn;
-    if ((b0 + kKvTn - 1 - aw > band) || (b0 + kKvTn > Bb)) {
-      // key b0 + off is visible iff off <= min(band + a - b0, Bb - 1 - b0)
-      const int32_t lim0 = band + a - b0, lim1 = Bb - 1 - b0;
-      const int32_t lim = lim0 < lim1 ? lim0 : lim1;
+    // the wave's first row sees the fewest keys (row extents grow with the
+    // row; they never exceed Bb, which covers the ragged last tile)
+    if (row_extent32(t.rel, aw) < b0 + kKvTn) {
+      // key b0 + off is visible iff off < ext(a) - b0
+      const int32_t lim = row_extent32(t.rel, a) - 1 - b0;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
@@ -477,10 +477,10 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(FwdParams p) {
   const int32_t nsteps = (p.mode == 0) ? p.P : 1;
   for (int32_t kstep = 0; kstep < nsteps; ++kstep) {
     const int32_t j = (p.mode == 0) ? ring_block(i, kstep, p.P) : p.step_block;
-    const BlockRel rel = block_relation(p.layout, p.causal, i, j);
+    const BlockRel rel = block_relation(p.layout, p.causal, i, j, (int32_t)p.Bb);
     const int64_t extent = visible_key_extent(rel, a_hi, p.Bb);
     if (extent <= 0) continue;
-    const int32_t band = (rel.kind == kAll) ? kBandAll : rel.band;
+    const int64_t ext_a = row_extent(rel, a);  // this row sees keys 0 .. ext_a - 1
     const int64_t kblk = (p.mode == 0) ? (int64_t)j : 0;
     const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + kblk * p.k.s_blk + b * p.k.s_batch +
                          h * p.k.s_head;
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(FwdParams p) {
 #pragma unroll
           for (int e = 0; e < D; ++e) dot = fmaf(qv[e], ks[c0 + u][e], dot);
           const int64_t kb = b0 + c0 + u;
-          sc[u] = (kb - a > (int64_t)band || kb >= p.Bb) ? -INFINITY : dot;
+          sc[u] = (kb >= ext_a) ? -INFINITY : dot;
           mx = fmaxf(mx, sc[u]);
         }
         const float m_new = fmaxf(m, mx * c2);

@@ -24,7 +24,6 @@ constexpr int kQWaves = 8;
 constexpr int kQThreads = 64 * kQWaves;
 constexpr int kQTm = 32 * kQWaves;  // query rows per workgroup
 constexpr int kKvTn = 64;           // keys per KV tile
-constexpr int kBandAll = 1 << 30;
 
 // LDS: four stages of (K tile, V tile), each [64][D] swizzled.
 template <int D>
@@ -75,19 +74,21 @@ __device__ __forceinline__ void query_tile_of(int32_t causal, int32_t layout, in
   }
 }
 
-// The (block, tile) pairs a query tile visits, in ring order.
+// The (block, tile) pairs a query tile visits, in ring order. rel is the
+// relation of the current block to the query block (row a sees its keys
+// 0 .. row_extent32(rel, a) - 1).
 struct KvIter {
-  int32_t kstep, nsteps, j, t, ntile, band;
+  int32_t kstep, nsteps, j, t, ntile;
+  BlockRel rel;
   int32_t i, P, layout, causal, a_hi, Bb, single_block;
   // moves to the next block with a visible tile; false when the ring is done
   __device__ bool next_block() {
     while (++kstep < nsteps) {
       j = (single_block >= 0) ? single_block : ring_block(i, kstep, P);
-      const BlockRel rel = block_relation(layout, causal, i, j);
-      const int64_t extent = visible_key_extent(rel, a_hi, Bb);
+      rel = block_relation(layout, causal, i, j, Bb);
+      const int32_t extent = row_extent32(rel, a_hi);
       if (extent <= 0) continue;
-      band = (rel.kind == kAll) ? kBandAll : rel.band;
-      ntile = (int32_t)((extent + kKvTn - 1) / kKvTn);
+      ntile = (extent + kKvTn - 1) / kKvTn;
       t = 0;
       return true;
     }

@@ -26,6 +26,10 @@
  *     Token positions (used by the causal mask) of local row x of block s:
  *       RA_LAYOUT_CONTIGUOUS: t = s * block_len + x
  *       RA_LAYOUT_STRIPED:    t = x * P + s   (ascending order within a block)
+ *       RA_LAYOUT_ZIGZAG:     with h = block_len / 2 (block_len even): t = s*h + x
+ *                             for x < h, t = (2P-1-s)*h + (x-h) for x >= h — the
+ *                             chapter's zigzag variant (two half-blocks placed
+ *                             symmetrically near the start and the end)
  *     Causal: key t' is visible to query t iff t' <= t. Non-causal: all keys.
  *   - scale > 0 is used as given; scale <= 0 selects 1 / sqrt(head_dim).
  *   - lse (log-sum-exp) is the natural log of sum over visible keys of
@@ -60,7 +64,8 @@ extern "C" {
 
 typedef enum {
   RA_LAYOUT_CONTIGUOUS = 0, /* device s owns tokens s*Bb .. s*Bb + Bb - 1 */
-  RA_LAYOUT_STRIPED = 1     /* token t belongs to device t mod P */
+  RA_LAYOUT_STRIPED = 1,    /* token t belongs to device t mod P */
+  RA_LAYOUT_ZIGZAG = 2      /* device s owns half-blocks s and 2P-1-s of 2P */
 } ra_layout;
 
 typedef enum {
@@ -100,7 +105,12 @@ typedef struct {
  * original-order [B, L, H, d] tensor is described without copying by
  *     contiguous: s_blk = block_len*H*d, s_tok = H*d,   s_head = d, s_batch = L*H*d
  *     striped:    s_blk = H*d,           s_tok = P*H*d, s_head = d, s_batch = L*H*d
- * ptr and every stride times the element size must be multiples of 16 bytes. */
+ * A zigzag block is not a strided slice of the original order: pass blocked
+ * tensors ([P][B][block_len][H][d]: s_blk = B*block_len*H*d, s_batch =
+ * block_len*H*d, s_tok = H*d, s_head = d), which ra_layout_copy produces.
+ * ptr and every stride times the element size must be multiples of 16 bytes.
+ * The bf16 forward needs the K and V token strides at most 2^25 elements
+ * (RA_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   void* ptr;
   int64_t s_blk;

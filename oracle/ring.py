@@ -11,7 +11,7 @@ Sources (page title, section):
     sections "Ring Attention: Compute While You Communicate" (ring diagram:
     step k attends KV block (i - k) mod P; device 0 sees KV[0], KV[3], KV[2],
     KV[1]), "The Causal-Mask Problem: Striped Attention" (row r goes to device
-    r mod P) and "Worked Demo: A 4-Device Ring in Discrete Ticks" (tick model
+    r mod P; the zigzag variant's two symmetric half-blocks) and "Worked Demo: A 4-Device Ring in Discrete Ticks" (tick model
     and the per-device work metric).
   * "Ring Attention 論文分析" (blog), sections "リングトポロジーと KV の循環"
     (send to rank+1, receive from rank-1), "リング通信パターン" (N=4 step
@@ -42,12 +42,25 @@ def token_position(layout: str, P: int, block_len: int, block, local):
                 ascending token order, so local row x of block s is token
                 x*P + s (the pages fix only the device of each row; ascending
                 order inside a device is the plain reading).
+    zigzag:     each device holds two half-blocks placed symmetrically near the
+                start and the end of the sequence: with the sequence cut into
+                2P chunks of Bb/2 tokens, device s holds chunk s and chunk
+                2P-1-s. The plain reading of the order: chunk s first, each
+                chunk in ascending token order (needs Bb even).
     Works elementwise on numpy integer arrays.
     """
     if layout == "contiguous":
         return np.asarray(block) * block_len + np.asarray(local)
     if layout == "striped":
         return np.asarray(local) * P + np.asarray(block)
+    if layout == "zigzag":
+        if block_len % 2:
+            raise ValueError("zigzag needs an even block length")
+        half = block_len // 2
+        block, local = np.asarray(block), np.asarray(local)
+        first = block * half + local
+        second = (2 * P - 1 - block) * half + (local - half)
+        return np.where(local < half, first, second)
     raise ValueError(f"unknown layout {layout!r}")
 
 
@@ -75,12 +88,21 @@ def pair_visible(t_query, t_key, causal: bool):
 def block_relation(layout: str, P: int, block_len: int, i: int, j: int, causal: bool = True):
     """How KV block j's keys relate to query block i's rows.
 
-    Returns ("none"|"all"|"band", c): for "band", key b is visible to query a
-    iff b - a <= c (local indices). Derived from the token positions:
+    Returns ("none"|"all"|"band"|"first_half"|"second_half_rows", c): for
+    "band", key b is visible to query a iff b - a <= c (local indices); for
+    "first_half" every query row sees exactly the keys b < c; for
+    "second_half_rows" rows a >= c see every key and rows a < c none. Derived
+    from the token positions:
       contiguous: j > i -> none (the whole block lies in the future and is
                   skipped), j == i -> band with c = 0 (the diagonal block,
                   strictly-upper triangle masked), j < i -> all;
-      striped:    b*P + j <= a*P + i  <=>  b - a <= 0 if j <= i else -1.
+      striped:    b*P + j <= a*P + i  <=>  b - a <= 0 if j <= i else -1;
+      zigzag:     (h = Bb/2; block s holds chunks s and 2P-1-s) a key in the
+                  first half lies in chunk j <= P-1, before chunk 2P-1-i of
+                  the query's second half, and a key in the second half lies in
+                  chunk 2P-1-j >= P, after chunk i of the query's first half.
+                  So j == i -> band 0 (chunk pairs on the diagonal), j < i ->
+                  first_half h, j > i -> second_half_rows h.
     """
     if not causal:
         return ("all", None)
@@ -92,6 +114,11 @@ def block_relation(layout: str, P: int, block_len: int, i: int, j: int, causal: 
         return ("all", None)
     if layout == "striped":
         return ("band", 0 if j <= i else -1)
+    if layout == "zigzag":
+        half = block_len // 2
+        if j == i:
+            return ("band", 0)
+        return ("first_half", half) if j < i else ("second_half_rows", half)
     raise ValueError(f"unknown layout {layout!r}")
 
 
@@ -100,7 +127,7 @@ def unmasked_pairs_per_rank(layout: str, P: int, block_len: int, causal: bool = 
 
     Counts, for every query row of device i and every KV block j, the keys of
     block j whose token position is <= the query's (all keys when not
-    causal). Key positions inside a block are ascending in both layouts, so a
+    causal). Key positions inside a block are ascending in every layout, so a
     sorted search gives the per-row count.
     """
     Bb = block_len

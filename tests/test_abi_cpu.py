@@ -80,12 +80,29 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, 2), ("heads", 0, 2), ("ring_size", 0, 2), ("block_len", 0, 2),
-    ("layout", 2, 2), ("causal", 3, 2), ("dtype", 7, 2), ("head_dim", 96, 3), ("head_dim", 32, 3),
+    ("layout", 3, 2), ("causal", 3, 2), ("dtype", 7, 2), ("head_dim", 96, 3), ("head_dim", 32, 3),
 ])
 def test_invalid_problem_fields(field, value, code):
     pb = problem()
     setattr(pb, field, value)
     assert fwd_status(pb) == code
+
+
+def test_zigzag_needs_an_even_block_length():
+    assert fwd_status(problem(layout="zigzag", Bb=63)) == 2
+    # validation only (nothing is launched): a valid problem has a backward
+    # workspace, an invalid one reports 0 bytes
+    assert ra.workspace_bytes(problem(layout="zigzag", Bb=64), 0, 4, False, True) > 0
+    assert ra.workspace_bytes(problem(layout="zigzag", Bb=63), 0, 4, False, True) == 0
+
+
+def test_forward_token_stride_limit():
+    # the bf16 forward addresses a 64-row K/V tile with 32-bit byte offsets
+    big = fake_seq(s_tok=(1 << 25) + 8)
+    seqs = [fake_seq(), big, fake_seq(), fake_seq()]
+    assert fwd_status(problem(), seqs=seqs) == 3
+    seqs = [fake_seq(), fake_seq(), big, fake_seq()]
+    assert fwd_status(problem(), seqs=seqs) == 3
 
 
 def test_invalid_scale_nan():

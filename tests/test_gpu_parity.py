@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle.
 
 Small cases compare every element; they span several tiles, ragged tails
-(block lengths that are not tile multiples), both layouts, causal and not,
+(block lengths that are not tile multiples), all three layouts, causal and not,
 bf16 and fp32, head_dim 64 and 128, single-rank (double-buffered receive)
 and rank-range launches, and degenerate shapes (one block, one token per
 block). Bars: max |GPU - oracle| <= 2e-2 for bf16 inputs (fp32 accumulation)
@@ -56,6 +56,14 @@ SMALL_FWD = [
     Case(111, 1, 2, 8, 128, 8, True, "striped", "bf16"),        # one token per block
     Case(112, 1, 2, 8, 64, 8, True, "contiguous", "f32"),
     Case(113, 1, 1, 4096, 128, 2, True, "striped", "bf16"),     # many tiles per block
+    # zigzag: half-blocks of 100 rows (tiles straddle the halves), 128 rows,
+    # fp32, one token per half-block, many tiles per block
+    Case(114, 1, 2, 800, 128, 4, True, "zigzag", "bf16"),
+    Case(115, 1, 2, 1024, 64, 4, True, "zigzag", "bf16"),
+    Case(116, 1, 2, 400, 64, 4, True, "zigzag", "f32"),
+    Case(117, 1, 2, 16, 128, 8, True, "zigzag", "bf16"),
+    Case(118, 1, 1, 4096, 128, 2, True, "zigzag", "bf16"),
+    Case(119, 1, 2, 600, 128, 3, False, "zigzag", "bf16"),
 ]
 
 
@@ -79,6 +87,7 @@ STEP_CASES = [
     Case(122, 1, 2, 800, 128, 4, True, "contiguous", "bf16"),
     Case(123, 1, 2, 520, 64, 4, False, "contiguous", "bf16"),
     Case(124, 1, 1, 400, 64, 4, True, "striped", "f32"),
+    Case(125, 1, 2, 800, 128, 4, True, "zigzag", "bf16"),
 ]
 
 
@@ -118,7 +127,7 @@ def test_forward_is_deterministic_and_grid_independent():
 def test_layout_copy_is_bit_exact():
     case = Case(132, 2, 3, 96, 64, 4, True, "striped", "bf16")
     log(f"layout copy {case}")
-    for layout in ("striped", "contiguous"):
+    for layout in ("striped", "contiguous", "zigzag"):
         p = payloads(case, ("q",))["q"]
         x = to_device(p)
         blk = ra.layout_copy(x, case.P, layout)
@@ -187,6 +196,9 @@ SMALL_BWD = [
     Case(146, 1, 2, 400, 64, 4, True, "striped", "f32"),
     Case(147, 1, 1, 210, 128, 3, True, "contiguous", "f32"),
     Case(148, 1, 1, 8, 128, 8, True, "striped", "bf16"),
+    Case(150, 1, 2, 800, 128, 4, True, "zigzag", "bf16"),
+    Case(151, 1, 2, 400, 64, 4, True, "zigzag", "f32"),
+    Case(152, 1, 1, 1000, 64, 5, True, "zigzag", "bf16"),
 ]
 
 
@@ -212,10 +224,11 @@ def test_backward_small(case):
     assert_close("dV", to_f64(dv), dv_r, tol, case)
 
 
-def test_backward_rank_range():
+@pytest.mark.parametrize("layout", ["striped", "zigzag"])
+def test_backward_rank_range(layout):
     """Ranks [1, 3): dQ of their rows, and dK/dV holding only their queries'
     contributions (the oracle's gradient with dO zero outside those rows)."""
-    case = Case(149, 1, 2, 800, 128, 4, True, "striped", "bf16")
+    case = Case(149, 1, 2, 800, 128, 4, True, layout, "bf16")
     log(f"backward rank range [1,3) {case}")
     p = payloads(case, ("q", "k", "v", "do"))
     dev = {n: to_device(x) for n, x in p.items()}

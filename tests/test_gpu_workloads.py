@@ -86,7 +86,7 @@ def test_workload2_bf16_noncausal():
     check_rows(w, "contiguous", o, lse, p, range(w.ring_size), rows, [0, w.heads - 1], TOL["bf16"])
 
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 def test_workload3_bf16_causal(layout):
     w = syn.WORKLOADS[3]
     log(f"workload {w.name} layout={layout}")

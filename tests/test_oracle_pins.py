@@ -216,7 +216,7 @@ def test_bwd_head_subset_equals_full():
 
 # ---------------------------------------------------------------- the method's invariant
 
-@pytest.mark.parametrize("layout", ["contiguous", "striped"])
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_blockwise_ring_equals_full_softmax(layout, causal):
     """Online softmax over KV blocks in ring order, for every block count
@@ -224,7 +224,7 @@ def test_blockwise_ring_equals_full_softmax(layout, causal):
     L = 24
     q, k, v = rnd(50, 1, L, 2, 4), rnd(51, 1, L, 2, 4), rnd(52, 1, L, 2, 4)
     o_full, lse_full = attention_fwd(q, k, v, causal)
-    for P in [p for p in range(1, L + 1) if L % p == 0]:
+    for P in [p for p in range(1, L + 1) if L % p == 0 and (layout != "zigzag" or (L // p) % 2 == 0)]:
         perm = layout_perm(L, P, layout)
         Bb = L // P
         for r in range(P):
@@ -245,6 +245,19 @@ def test_striped_permutation_equivariance():
     o_c, l_c = attention_fwd(q, k, v, True)
     assert np.max(np.abs(o_s[:, inv] - o_c)) < 1e-13
     assert np.max(np.abs(l_s[:, inv] - l_c)) < 1e-13
+
+
+def test_zigzag_permutation_equivariance():
+    """Zigzag causal attention on the blocked rows with their original
+    positions, permuted back, equals contiguous causal attention."""
+    L, P = 48, 4
+    q, k, v = rnd(56, 1, L, 2, 8), rnd(57, 1, L, 2, 8), rnd(58, 1, L, 2, 8)
+    perm = layout_perm(L, P, "zigzag")
+    inv = np.argsort(perm)
+    o_z, l_z = attention_fwd(q[:, perm], k[:, perm], v[:, perm], True, q_pos=perm, k_pos=perm, row_chunk=5)
+    o_c, l_c = attention_fwd(q, k, v, True)
+    assert np.max(np.abs(o_z[:, inv] - o_c)) < 1e-13
+    assert np.max(np.abs(l_z[:, inv] - l_c)) < 1e-13
 
 
 # ---------------------------------------------------------------- LSE merge
@@ -307,21 +320,28 @@ def test_tick_demo_matches_printed_output():
 
 def test_layout_perm_is_the_stated_assignment():
     L, P = 32, 4
-    for layout in ("contiguous", "striped"):
+    for layout in ("contiguous", "striped", "zigzag"):
         perm = layout_perm(L, P, layout)
         assert sorted(perm) == list(range(L))
         Bb = L // P
+        h = Bb // 2
         for s in range(P):
             rows = perm[s * Bb:(s + 1) * Bb]
             if layout == "striped":
                 assert all(t % P == s for t in rows)  # token t -> device t mod P
+            elif layout == "zigzag":
+                # two half-blocks, symmetric: chunk s and chunk 2P-1-s of 2P
+                assert list(rows) == list(range(s * h, (s + 1) * h)) + list(
+                    range((2 * P - 1 - s) * h, (2 * P - s) * h))
             else:
                 assert list(rows) == list(range(s * Bb, (s + 1) * Bb))
             assert list(rows) == sorted(rows)  # ascending inside a device
 
 
 def test_block_relation_matches_brute_force():
-    for layout, P, Bb in itertools.product(("contiguous", "striped"), (1, 2, 3, 5), (1, 4, 7)):
+    cases = list(itertools.product(("contiguous", "striped"), (1, 2, 3, 5), (1, 4, 7)))
+    cases += list(itertools.product(("zigzag",), (1, 2, 3, 5), (2, 4, 6)))
+    for layout, P, Bb in cases:
         for i, j in itertools.product(range(P), range(P)):
             kind, c = oracle.block_relation(layout, P, Bb, i, j)
             a = np.arange(Bb)[:, None]
@@ -331,6 +351,10 @@ def test_block_relation_matches_brute_force():
                 assert not vis.any()
             elif kind == "all":
                 assert vis.all()
+            elif kind == "first_half":
+                assert np.array_equal(vis, np.broadcast_to(b < c, vis.shape))
+            elif kind == "second_half_rows":
+                assert np.array_equal(vis, np.broadcast_to(a >= c, vis.shape))
             else:
                 assert np.array_equal(vis, (b - a) <= c)
         # contiguous rule as stated: later block skipped, own block triangular, earlier block full
@@ -357,6 +381,23 @@ def test_unmasked_pair_counts(layout):
                 rows = perm[r * Bb:(r + 1) * Bb]
                 assert counts[r] == int((perm[None, :] <= rows[:, None]).sum())
     assert oracle.unmasked_pairs_per_rank(layout, 4, 8, causal=False) == [256] * 4
+
+
+def test_zigzag_pair_counts_are_balanced():
+    """Device s's first half-block (chunk s) sees s full chunks and its own
+    triangle, its second (chunk 2P-1-s) sees 2P-1-s full chunks and its own
+    triangle: (2P-1) h^2 + h(h+1) pairs on every device, h = Bb/2."""
+    for P, Bb in ((1, 2), (4, 8), (3, 6), (16, 16), (5, 10)):
+        h = Bb // 2
+        counts = oracle.unmasked_pairs_per_rank("zigzag", P, Bb)
+        assert counts == [(2 * P - 1) * h * h + h * (h + 1)] * P
+        L = P * Bb
+        assert sum(counts) == L * (L + 1) // 2
+        if L <= 64:
+            perm = layout_perm(L, P, "zigzag")
+            for r in range(P):
+                rows = perm[r * Bb:(r + 1) * Bb]
+                assert counts[r] == int((perm[None, :] <= rows[:, None]).sum())
 
 
 # ---------------------------------------------------------------- the pins have teeth
