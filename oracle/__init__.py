@@ -7,10 +7,11 @@ import this package; the product path (the HIP library and its binding)
 never does, and shares no code with it.
 
 Modules:
-  attention -- full-softmax attention forward/backward (the definition),
+  attention -- full-softmax attention forward/backward (the definition,
+               with K/V heads optionally shared by groups of query heads),
                the log-sum-exp merge of two partial results, and the pages'
                online-softmax loop run in ring order (for self-checks).
-  ring      -- ring schedule, token layouts (contiguous / striped), block
+  ring      -- ring schedule, token layouts (contiguous / striped / zigzag), block
                classification, per-device work counts and the pages' tick
                simulation.
 

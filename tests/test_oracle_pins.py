@@ -214,6 +214,120 @@ def test_bwd_head_subset_equals_full():
         assert np.array_equal(a[:, :, [3, 1]], b)
 
 
+# ---------------------------------------------------------------- grouped-query attention
+# K/V with Hk heads shared by H = G * Hk query heads (query head h reads K/V
+# head h // G). torch's enable_gqa attention repeats each K/V head G times
+# consecutively, which is the same assignment.
+
+def _torch_sdpa_gqa(q, k, v, causal, do=None):
+    t = lambda x: torch.tensor(x).permute(0, 2, 1, 3).contiguous().requires_grad_(do is not None)
+    tq, tk, tv = t(q), t(k), t(v)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, enable_gqa=True)
+    back = lambda x: x.permute(0, 2, 1, 3).detach().numpy()
+    if do is None:
+        return back(out)
+    out.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    return back(out), back(tq.grad), back(tk.grad), back(tv.grad)
+
+
+@pytest.mark.parametrize("hk", [1, 2, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_fwd_matches_torch_cpu_f64(causal, hk):
+    q = rnd(300, 2, 45, 6, 8)
+    k, v = rnd(301, 2, 45, hk, 8), rnd(302, 2, 45, hk, 8)
+    o, _ = attention_fwd(q, k, v, causal, row_chunk=16)
+    assert np.max(np.abs(o - _torch_sdpa_gqa(q, k, v, causal))) < 1e-12
+
+
+@pytest.mark.parametrize("hk", [1, 2])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_bwd_matches_torch_autograd_f64(causal, hk):
+    q, do = rnd(303, 1, 33, 4, 8), rnd(304, 1, 33, 4, 8)
+    k, v = rnd(305, 1, 33, hk, 8), rnd(306, 1, 33, hk, 8)
+    _, tdq, tdk, tdv = _torch_sdpa_gqa(q, k, v, causal, do)
+    dq, dk, dv, _, _ = attention_bwd(q, k, v, do, causal, row_chunk=10)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    assert np.max(np.abs(dq - tdq)) < 1e-12
+    assert np.max(np.abs(dk - tdk)) < 1e-12
+    assert np.max(np.abs(dv - tdv)) < 1e-12
+
+
+def test_gqa_bwd_matches_finite_differences():
+    """The gradient of a shared K/V head collects every query head that reads it."""
+    L, d = 5, 2
+    q, do = rnd(310, 1, L, 4, d), rnd(311, 1, L, 4, d)
+    k, v = rnd(312, 1, L, 2, d), rnd(313, 1, L, 2, d)
+    dq, dk, dv, _, _ = attention_bwd(q, k, v, do, True)
+    f = lambda qq, kk, vv: float((attention_fwd(qq, kk, vv, True)[0] * do).sum())
+    h = 1e-6
+    for name, x, g in (("k", k, dk), ("v", v, dv), ("q", q, dq)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args = {"q": q, "k": k, "v": v}
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args[name] = xp
+            fp = f(args["q"], args["k"], args["v"])
+            args[name] = xm
+            fm = f(args["q"], args["k"], args["v"])
+            num[idx] = (fp - fm) / (2 * h)
+        assert np.max(np.abs(num - g)) / np.max(np.abs(g)) < 1e-6, name
+
+
+def test_mqa_zero_keys_give_prefix_means_for_every_head():
+    """One K/V head (multi-query) with K = 0: every query head gets the causal
+    prefix mean of the single V head, and lse = ln(visible count)."""
+    L = 9
+    q, v = rnd(320, 1, L, 5, 4), rnd(321, 1, L, 1, 4)
+    o, lse = attention_fwd(q, np.zeros((1, L, 1, 4)), v, True)
+    means = np.cumsum(v[0, :, 0], axis=0) / np.arange(1, L + 1)[:, None]
+    for h in range(5):
+        assert np.max(np.abs(o[0, :, h] - means)) < 1e-14
+        assert np.max(np.abs(lse[0, :, h] - np.log(np.arange(1, L + 1)))) < 1e-14
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
+def test_gqa_blockwise_ring_equals_full_softmax(layout):
+    L, P = 24, 4
+    q, k, v = rnd(330, 1, L, 4, 4), rnd(331, 1, L, 2, 4), rnd(332, 1, L, 2, 4)
+    of, lf = attention_fwd(q, k, v, True)
+    perm = layout_perm(L, P, layout)
+    Bb = L // P
+    for rank in range(P):
+        ob, lb = blockwise_ring_fwd(q, k, v, P, rank, layout, True)
+        rows = perm[rank * Bb:(rank + 1) * Bb]
+        assert np.max(np.abs(ob - of[:, rows])) < 1e-12
+        assert np.max(np.abs(lb - lf[:, rows])) < 1e-12
+
+
+def test_gqa_sampled_equals_full_and_needs_whole_groups():
+    q, do = rnd(340, 1, 30, 6, 4), rnd(341, 1, 30, 6, 4)
+    k, v = rnd(342, 1, 30, 2, 4), rnd(343, 1, 30, 2, 4)
+    full = attention_bwd(q, k, v, do, True, heads=[3, 4, 5, 0, 1, 2], row_chunk=7)
+    qr, kr = np.array([29, 0, 11]), np.array([0, 17, 29, 4])
+    dq, dk, dv, _, _ = oracle.attention_bwd_sampled(q, k, v, do, True, qr, kr, heads=[3, 4, 5, 0, 1, 2])
+    assert np.max(np.abs(dq - full[0][:, qr])) < 1e-13
+    assert np.max(np.abs(dk - full[1][:, kr])) < 1e-13
+    assert np.max(np.abs(dv - full[2][:, kr])) < 1e-13
+    ref = attention_bwd(q, k, v, do, True)
+    assert np.max(np.abs(full[1] - ref[1][:, :, [1, 0]])) < 1e-13  # groups in order of first appearance
+    with pytest.raises(ValueError):
+        attention_bwd(q, k, v, do, True, heads=[0, 1])
+    with pytest.raises(ValueError):
+        attention_fwd(q, rnd(344, 1, 30, 4, 4), rnd(345, 1, 30, 4, 4), True)
+
+
+def test_planted_interleaved_head_map_is_caught(monkeypatch):
+    """Reading K/V head h mod Hk instead of h // G fails the library pin."""
+    import oracle.attention as oa
+    q, k, v = rnd(350, 1, 12, 4, 4), rnd(351, 1, 12, 2, 4), rnd(352, 1, 12, 2, 4)
+    ref = _torch_sdpa_gqa(q, k, v, True)
+    monkeypatch.setattr(oa, "_kv_head", lambda h, H, Hk: h % Hk)
+    o, _ = oa.attention_fwd(q, k, v, True)
+    assert np.max(np.abs(o - ref)) > 1e-3
+
+
 # ---------------------------------------------------------------- the method's invariant
 
 @pytest.mark.parametrize("layout", ["contiguous", "striped", "zigzag"])
