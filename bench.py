@@ -36,8 +36,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--layout", default=None, help="workloads 3 and 5: contiguous, striped or zigzag")
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--layout", default=None, help="workloads 3, 5 and 6: contiguous, striped or zigzag")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the library's layout copy with one block) three "
@@ -132,22 +132,26 @@ def cpu_baseline(w):
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
     d = w.head_dim
-    if 5 == w.wid:
-        # heads 0 and H-1 of the full 32768-token sequence (the workload's own
-        # tensors), forward + backward; about 10 s on 16 host cores
-        heads = [0, w.heads - 1]
-        shape = syn.workload_shape(w)
+    if "bwd" in w.passes:
+        # of the full 32768-token sequence (the workload's own tensors),
+        # forward + backward: heads 0 and H-1 (about 10 s on 16 host cores),
+        # or with shared K/V heads the query heads of K/V head 0 (about 20 s)
+        G = w.heads // (w.kv_heads or w.heads)
+        heads = [0, w.heads - 1] if G == 1 else list(range(G))
         t = {}
         for n in ("q", "k", "v", "do"):
-            pay = syn.make_payload(w.wid, n, shape, w.dtype)
-            t[n] = syn.to_f64(np.ascontiguousarray(pay[:, :, heads]))
+            pay = syn.make_payload(w.wid, n, syn.workload_shape(w, n), w.dtype)
+            sel = [0] if (G > 1 and n in ("k", "v")) else heads
+            t[n] = syn.to_f64(np.ascontiguousarray(pay[:, :, sel]))
             del pay
         L = w.seq_len
         t0 = time.perf_counter()
         oracle.attention_bwd(t["q"], t["k"], t["v"], t["do"], True)  # runs the forward inside
         dt = time.perf_counter() - t0
         flops = len(heads) * L * (L + 1) // 2 * (4 + 10) * d
-        sample = f"heads 0 and {w.heads - 1} of {w.heads}, all {L} tokens, forward+backward (causal, " \
+        which = f"heads 0 and {w.heads - 1} of {w.heads}" if G == 1 else \
+            f"query heads 0..{G - 1} of {w.heads} (the ones sharing K/V head 0)"
+        sample = f"{which}, all {L} tokens, forward+backward (causal, " \
                  "contiguous order: the oracle's mask is on token positions, so the layout does not change it)"
     else:
         Ls = 4096 if w.causal else 2048
@@ -184,7 +188,6 @@ def main():
     P, Bb, d = w.ring_size, w.block_len, w.head_dim
     ranks = list(range(*w.q_ranks)) if w.q_ranks else list(range(P))
     rb, re_ = ranks[0], ranks[-1] + 1
-    shape = syn.workload_shape(w)
     names = ("q", "k", "v", "do") if "bwd" in w.passes else ("q", "k", "v")
 
     def dev(x):
@@ -197,7 +200,7 @@ def main():
         raise SystemExit("the one-device share is run in the striped layout")
     t = {}
     for n in names:
-        pay = syn.make_payload(w.wid, n, shape, w.dtype)
+        pay = syn.make_payload(w.wid, n, syn.workload_shape(w, n), w.dtype)
         if n == "q" and w.q_ranks:
             # one device's share: only its query block is resident, in local row order
             x = np.arange(Bb)
@@ -208,13 +211,13 @@ def main():
             hb = Bb // 2
             perm = np.concatenate([np.r_[s_ * hb:(s_ + 1) * hb, (2 * P - 1 - s_) * hb:(2 * P - s_) * hb]
                                    for s_ in range(P)])
-            pay = np.ascontiguousarray(pay[:, perm].reshape(w.batch, P, Bb, w.heads, d).transpose(1, 0, 2, 3, 4))
+            pay = np.ascontiguousarray(pay[:, perm].reshape(w.batch, P, Bb, pay.shape[2], d).transpose(1, 0, 2, 3, 4))
         t[n] = dev(pay)
         del pay
     torch.cuda.synchronize()
 
     code = ra.BF16 if w.dtype == "bf16" else ra.F32
-    pb = ra.make_problem(w.batch, w.heads, d, P, Bb, layout, w.causal, code)
+    pb = ra.make_problem(w.batch, w.heads, d, P, Bb, layout, w.causal, code, kv_heads=w.kv_heads)
     stream = torch.cuda.current_stream()
     sh = ra._stream_handle(stream)
     copy_stream = torch.cuda.Stream() if w.prefetch else None
@@ -308,13 +311,15 @@ def main():
     if w.prefetch:
         roof["note"] = "one call of 8 step launches plus the side-stream copies, timed as a whole"
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    gqa_tag = f", {w.heads} query heads on {w.kv_heads} K/V heads" if w.kv_heads else ""
     out = {
-        "metric": f"attention TFLOP/s fwd+bwd (causal {layout}, d=128) and % of bf16 MFMA peak" if bwd else
+        "metric": f"attention TFLOP/s fwd+bwd (causal {layout}{gqa_tag}, d=128) and % of bf16 MFMA peak" if bwd else
                   f"attention forward TFLOP/s ({workload_name(w, layout)})",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": workload_name(w, layout), "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "head_dim": d,
+                   "kv_heads": w.kv_heads or w.heads,
                    "ring_size": P, "block_len": Bb, "layout": layout, "causal": w.causal,
                    "ranks": [rb, re_], "passes": list(w.passes), "prefetch": w.prefetch},
         "frac_of_peak": round(value / peak, 4),

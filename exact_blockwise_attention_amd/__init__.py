@@ -10,7 +10,8 @@ Low level:  Problem, Seq, forward_raw, backward_raw, merge_lse_raw,
             layout_copy_raw, workspace_bytes (same names and meaning as the
             C functions).
 High level: attention_forward / attention_backward take original-order
-            [B, L, H, d] torch tensors and allocate outputs/workspaces with
+            [B, L, H, d] torch tensors (K and V may have fewer heads than Q:
+            grouped-query attention) and allocate outputs/workspaces with
             torch.
 """
 from __future__ import annotations
@@ -53,6 +54,7 @@ class Problem(ctypes.Structure):
         ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("ring_size", ctypes.c_int32), ("block_len", ctypes.c_int64), ("layout", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32),
     ]
 
 
@@ -217,16 +219,18 @@ def _seq_for(t, P, layout, block_offset=0):
     return seq_original(t, P, layout, block_offset=block_offset), None
 
 
-def make_problem(B, H, d, P, Bb, layout, causal, dtype_code, scale=None) -> Problem:
+def make_problem(B, H, d, P, Bb, layout, causal, dtype_code, scale=None, kv_heads=0) -> Problem:
+    """kv_heads: heads of K and V (0: the same as H)."""
     return Problem(B, H, d, P, Bb, LAYOUTS[layout], int(bool(causal)),
-                   float(scale) if scale else 0.0, dtype_code)
+                   float(scale) if scale else 0.0, dtype_code, int(kv_heads))
 
 
 def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causal: bool = False,
                       scale=None, rank_range=None, copy_stream=None, out=None, lse=None, workspace=None):
     """Blockwise ring attention forward on original-order [B, L, H, d] tensors.
 
-    k, v: the whole sequence. q (and ``out``) hold either the whole sequence
+    k, v: the whole sequence, [B, L, Hk, d] with Hk dividing H (query head h
+    reads K/V head h // (H / Hk)). q (and ``out``) hold either the whole sequence
     ([B, L, H, d], only the rows of the ranks in ``rank_range`` are read /
     written) or just those ranks' rows ([B, nr*Bb, H, d], each rank's block
     contiguous in its local row order). Returns (o, lse) with lse fp32
@@ -234,13 +238,14 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     double-buffered receive mode (single rank).
     """
     torch = _torch()
-    B, L, H, d = k.shape
+    B, L, Hk, d = k.shape
+    H = q.shape[2]
     P = ring_size
     Bb = L // P
     rb, re = (0, P) if rank_range is None else rank_range
     nr = re - rb
     code = _dtype_code(q)
-    pb = make_problem(B, H, d, P, Bb, layout, causal, code, scale)
+    pb = make_problem(B, H, d, P, Bb, layout, causal, code, scale, kv_heads=Hk)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -283,14 +288,16 @@ def _seq_rank_rows(t, nr, layout, P):
 
 def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "contiguous",
                        causal: bool = False, scale=None, rank_range=None, workspace=None):
-    """Backward on original-order [B, L, H, d] tensors; returns (dq, dk, dv)."""
+    """Backward on original-order [B, L, H, d] tensors (k, v, dk, dv with
+    Hk heads); returns (dq, dk, dv)."""
     torch = _torch()
-    B, L, H, d = k.shape
+    B, L, Hk, d = k.shape
+    H = q.shape[2]
     P = ring_size
     Bb = L // P
     rb, re = (0, P) if rank_range is None else rank_range
     code = _dtype_code(q)
-    pb = make_problem(B, H, d, P, Bb, layout, causal, code, scale)
+    pb = make_problem(B, H, d, P, Bb, layout, causal, code, scale, kv_heads=Hk)
     dq = torch.zeros_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

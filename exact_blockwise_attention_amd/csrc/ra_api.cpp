@@ -25,9 +25,12 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+int32_t kv_heads_of(const ra_problem* pb) { return pb->kv_heads == 0 ? pb->heads : pb->kv_heads; }
+
 ra_status check_problem(const ra_problem* pb, int32_t rb, int32_t re) {
   if (!pb) return RA_ERR_NULL;
   if (pb->batch < 1 || pb->heads < 1 || pb->ring_size < 1 || pb->block_len < 1) return RA_ERR_SHAPE;
+  if (kv_heads_of(pb) < 1 || pb->heads % kv_heads_of(pb)) return RA_ERR_SHAPE;
   if (pb->layout != RA_LAYOUT_CONTIGUOUS && pb->layout != RA_LAYOUT_STRIPED && pb->layout != RA_LAYOUT_ZIGZAG)
     return RA_ERR_SHAPE;
   if (pb->layout == RA_LAYOUT_ZIGZAG && pb->block_len % 2) return RA_ERR_SHAPE;  // two half-blocks
@@ -71,7 +74,7 @@ FwdWs fwd_ws_layout(const ra_problem* pb, int32_t n_ranks, int32_t copy) {
   FwdWs w{};
   if (!copy) return w;
   const size_t es = elem_bytes(pb->dtype);
-  const size_t blk = (size_t)pb->batch * pb->block_len * pb->heads * pb->head_dim * es;
+  const size_t blk = (size_t)pb->batch * pb->block_len * kv_heads_of(pb) * pb->head_dim * es;
   const size_t rows = (size_t)n_ranks * pb->batch * pb->heads * pb->block_len;
   size_t off = 0;
   for (int b = 0; b < 2; ++b) {
@@ -159,6 +162,8 @@ ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
   p.lse = lse;
   p.B = pb->batch;
   p.H = pb->heads;
+  p.Hk = kv_heads_of(pb);
+  p.G = pb->heads / p.Hk;
   p.D = pb->head_dim;
   p.P = pb->ring_size;
   p.Bb = pb->block_len;
@@ -192,17 +197,17 @@ ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
   RA_HIP(hipEventRecord(ev_start, compute));  // inputs are ready on `compute`
   RA_HIP(hipStreamWaitEvent(copy, ev_start, 0));
 
-  const int64_t dense_tok = (int64_t)pb->heads * pb->head_dim;
+  const int64_t dense_tok = (int64_t)kv_heads_of(pb) * pb->head_dim;
   auto buf_seq = [&](size_t off) {
     return ra::Seq{ws + off, 0, (int64_t)pb->block_len * dense_tok, dense_tok, pb->head_dim};
   };
   auto copy_block = [&](int32_t step) -> hipError_t {
     const int32_t j = ra::ring_block(i, step, P);
     const int32_t bsel = step & 1;
-    hipError_t e = ra::launch_gather_block(to_seq(k), j, ws + w.kbuf[bsel], pb->batch, pb->heads,
+    hipError_t e = ra::launch_gather_block(to_seq(k), j, ws + w.kbuf[bsel], pb->batch, kv_heads_of(pb),
                                            pb->head_dim, pb->block_len, es, copy);
     if (e != hipSuccess) return e;
-    e = ra::launch_gather_block(to_seq(v), j, ws + w.vbuf[bsel], pb->batch, pb->heads,
+    e = ra::launch_gather_block(to_seq(v), j, ws + w.vbuf[bsel], pb->batch, kv_heads_of(pb),
                                 pb->head_dim, pb->block_len, es, copy);
     if (e != hipSuccess) return e;
     return hipEventRecord(ev_copy[bsel], copy);
@@ -264,6 +269,8 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
   p.dsum = reinterpret_cast<float*>(ws + w.dsum);
   p.B = pb->batch;
   p.H = pb->heads;
+  p.Hk = kv_heads_of(pb);
+  p.G = pb->heads / p.Hk;
   p.D = pb->head_dim;
   p.P = pb->ring_size;
   p.Bb = pb->block_len;
@@ -335,7 +342,9 @@ const char* ra_status_string(int32_t status) {
     case RA_OK: return "ok";
     case RA_ERR_NULL: return "a required pointer is NULL";
     case RA_ERR_SHAPE: return "sizes, ranks, strides or layout out of range";
-    case RA_ERR_UNSUPPORTED: return "valid but unsupported configuration (head_dim must be 64 or 128)";
+    case RA_ERR_UNSUPPORTED:
+      return "valid but unsupported configuration (head_dim other than 64 or 128, or a bf16 forward K/V "
+             "token stride above 2^25 elements)";
     case RA_ERR_WORKSPACE: return "workspace missing or too small";
     case RA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case RA_ERR_HIP: return "HIP runtime call failed";
@@ -343,6 +352,6 @@ const char* ra_status_string(int32_t status) {
   }
 }
 
-int32_t ra_abi_version(void) { return 1; }
+int32_t ra_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -7,10 +7,11 @@
 // dK = scale * dS^T Q; the dK/dV partials belong to the KV block's owner.
 //
 // This file holds the dK/dV half: one workgroup owns a tile of 128 keys of KV
-// block j for one (batch, head) and carries its dK/dV accumulators on chip
-// while the block travels the ring: at step k it meets the query block of
-// rank (j + k) mod P. Query tiles the causal/striped mask hides from every
-// key of the tile are skipped. The dQ half (ra_dq.hip) walks the ring from
+// block j for one (batch, K/V head) and carries its dK/dV accumulators on
+// chip while the block travels the ring: at step k it meets the query block
+// of rank (j + k) mod P, once for each query head that reads this K/V head
+// (grouped-query attention sums their contributions). Query tiles the
+// causal/striped mask hides from every key of the tile are skipped. The dQ half (ra_dq.hip) walks the ring from
 // the query side, so neither half needs atomics.
 //
 // bf16 path: 8 waves; wave w owns keys 32(w%4) .. +31 of the tile and query
@@ -66,25 +67,37 @@ __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int3
   }
 }
 
-// The (rank, query tile) pairs a KV tile meets, in ring order.
+// The (rank, query head, query tile) triples a KV tile meets: ranks in ring
+// order, and at each rank the G query heads of its K/V head in turn (gi is
+// the head's index within the group).
 struct QTileIter {
-  int32_t kstep, i, qt, qtiles;
-  int32_t j, P, rb, re, layout, causal, kv0, Bb;
+  int32_t kstep, i, gi, qt, qtiles;
+  int32_t j, P, G, rb, re, layout, causal, kv0, Bb;
+  // the first row of rank i's block that sees the tile's first key, which is
+  // the first row that sees any of its keys (Bb if none does)
+  __device__ int32_t first_row() const {
+    return first_row_seeing32(block_relation(layout, causal, i, j, Bb), kv0, Bb);
+  }
   __device__ bool step_rank() {
     while (++kstep < P) {
       i = ring_rank(j, kstep, P);
       if (i < rb || i >= re) continue;
-      const BlockRel rel = block_relation(layout, causal, i, j, Bb);
-      // the first row that sees the tile's first key is the first row that
-      // sees any of its keys
-      const int32_t a_first = first_row_seeing32(rel, kv0, Bb);
+      const int32_t a_first = first_row();
       if (a_first >= Bb) continue;
       qt = a_first / kQm;
-      if (qt < qtiles) return true;
+      gi = 0;
+      return true;
     }
     return false;
   }
-  __device__ bool next() { return (++qt < qtiles) ? true : step_rank(); }
+  __device__ bool next() {
+    if (++qt < qtiles) return true;
+    if (++gi < G) {
+      qt = first_row() / kQm;
+      return true;
+    }
+    return step_rank();
+  }
 };
 
 // Copies query tile `it` (Q and dO rows, lse and D) into LDS stage `stage`
@@ -123,18 +136,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   const int kg = wave % 4;
   const int qh = wave / 4;
 
-  const int32_t BH = p.B * p.H;
+  const int32_t BHk = p.B * p.Hk;
   const int32_t tiles = (int32_t)((p.Bb + kKn - 1) / kKn);
-  // consecutive logical indices share (batch, head, block) and take its key
-  // tiles in order (early keys are seen by more rows), so the workgroups of
-  // one XCD walk the same query tiles together and share them in L2
-  const int64_t lw = xcd_logical(blockIdx.x, (int64_t)BH * p.P * tiles);
+  // consecutive logical indices share (batch, K/V head, block) and take its
+  // key tiles in order (early keys are seen by more rows), so the workgroups
+  // of one XCD walk the same query tiles together and share them in L2
+  const int64_t lw = xcd_logical(blockIdx.x, (int64_t)BHk * p.P * tiles);
   const int32_t tile = (int32_t)(lw % tiles);
   const int64_t g = lw / tiles;
-  const int32_t bh = (int32_t)(g / p.P);
+  const int32_t bhk = (int32_t)(g / p.P);
   const int32_t j = (int32_t)(g % p.P);
-  const int32_t b = bh / p.H;
-  const int32_t h = bh % p.H;
+  const int32_t b = bhk / p.Hk;
+  const int32_t hk = bhk % p.Hk;
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t kv0 = tile * kKn;
   const int32_t kw = kv0 + 32 * kg;  // first key of this wave
@@ -142,8 +155,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
 
   // K and V of the tile, once
   {
-    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + h * p.k.s_head;
-    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + h * p.v.s_head;
+    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + hk * p.k.s_head;
+    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + hk * p.v.s_head;
     dma_rows<D, kKn, kWaves>(lds + L::K, kb, p.k.s_tok, kv0, Bb, wave, lane);
     dma_rows<D, kKn, kWaves>(lds + L::V, vb, p.v.s_tok, kv0, Bb, wave, lane);
   }
@@ -162,6 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   cur.qtiles = (Bb + kQm - 1) / kQm;
   cur.j = j;
   cur.P = p.P;
+  cur.G = p.G;
   cur.rb = p.rank_begin;
   cur.re = p.rank_begin + p.n_ranks;
   cur.layout = p.layout;
@@ -169,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   cur.kv0 = kv0;
   cur.Bb = Bb;
   const bool any = cur.step_rank();
-  if (any) dma_qtile<D>(p, cur, b, h, lds, f32s, 0, wave, lane);
+  if (any) dma_qtile<D>(p, cur, b, hk * p.G + cur.gi, lds, f32s, 0, wave, lane);
   wait_dma();  // K, V and the first query tile
   // per-lane element offsets: row operands at rows n (+32 key group / +32
   // row half) and columns 16ss + 8hf; transposing reads at rows
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     __syncthreads();  // this query stage is in LDS; the other one is no longer read
     QTileIter nx = cur;
     const bool more = nx.next();
-    if (more) dma_qtile<D>(p, nx, b, h, lds, f32s, stage ^ 1, wave, lane);  // lands during the compute below
+    if (more) dma_qtile<D>(p, nx, b, hk * p.G + nx.gi, lds, f32s, stage ^ 1, wave, lane);  // lands during the compute below
 
     const BlockRel rel = block_relation(p.layout, p.causal, cur.i, j, Bb);
     const int32_t q0 = cur.qt * kQm;
@@ -321,9 +335,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   }
   if (qh == 1 || key >= Bb) return;
   __bf16* dkrow = reinterpret_cast<__bf16*>(p.dk.ptr) + j * p.dk.s_blk + b * p.dk.s_batch +
-                  (int64_t)key * p.dk.s_tok + h * p.dk.s_head;
+                  (int64_t)key * p.dk.s_tok + hk * p.dk.s_head;
   __bf16* dvrow = reinterpret_cast<__bf16*>(p.dv.ptr) + j * p.dv.s_blk + b * p.dv.s_batch +
-                  (int64_t)key * p.dv.s_tok + h * p.dv.s_head;
+                  (int64_t)key * p.dv.s_tok + hk * p.dv.s_head;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -372,18 +386,18 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
   float* lse_s = sm + L::LSE;
   float* dsum_s = sm + L::DSUM;
   const int tid = threadIdx.x;
-  const int32_t BH = p.B * p.H;
+  const int32_t BHk = p.B * p.Hk;
   const int32_t tiles = (int32_t)((p.Bb + kF32Keys - 1) / kF32Keys);
   const int64_t id = blockIdx.x;
-  const int32_t bh = (int32_t)(id % BH);
-  const int32_t b = bh / p.H;
-  const int32_t h = bh % p.H;
+  const int32_t bhk = (int32_t)(id % BHk);
+  const int32_t b = bhk / p.Hk;
+  const int32_t hk = bhk % p.Hk;
   int32_t j, tile;
-  kv_tile_of(p, id / BH, tiles, &j, &tile);
+  kv_tile_of(p, id / BHk, tiles, &j, &tile);
   const int64_t kv0 = (int64_t)tile * kF32Keys;
   const int64_t key = kv0 + tid;
-  const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + h * p.k.s_head;
-  const float* vbase = reinterpret_cast<const float*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + h * p.v.s_head;
+  const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + hk * p.k.s_head;
+  const float* vbase = reinterpret_cast<const float*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + hk * p.v.s_head;
   for (int idx = tid; idx < kF32Keys * D; idx += kF32Keys) {
     const int r = idx / D, e = idx % D;
     const int64_t x = kv0 + r;
@@ -407,46 +421,49 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
     const int64_t a_first = first_row_seeing(rel, kv0, p.Bb);  // first row that sees the tile
     if (a_first >= p.Bb) continue;
     const int64_t a_min = first_row_seeing(rel, key, p.Bb);  // rows a >= a_min see this lane's key
-    const float* qbase = reinterpret_cast<const float*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
-    const float* dobase = reinterpret_cast<const float*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch + h * p.dout.s_head;
-    const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
-    for (int32_t qt = (int32_t)(a_first / kF32Rows); qt < qtiles; ++qt) {
-      const int64_t q0 = (int64_t)qt * kF32Rows;
-      __syncthreads();
-      for (int idx = tid; idx < kF32Rows * D; idx += kF32Keys) {
-        const int r = idx / D, e = idx % D;
-        const int64_t x = q0 + r;
-        qs[r * L::S + e] = (x < p.Bb) ? qbase[x * p.q.s_tok + e] : 0.0f;
-        os[r * L::S + e] = (x < p.Bb) ? dobase[x * p.dout.s_tok + e] : 0.0f;
-      }
-      if (tid < kF32Rows) {
-        const int64_t x = q0 + tid;
-        lse_s[tid] = (x < p.Bb) ? p.lse[srow + x] * kLog2e : 0.0f;
-        dsum_s[tid] = (x < p.Bb) ? p.dsum[srow + x] : 0.0f;
-      }
-      __syncthreads();
-      for (int r = 0; r < kF32Rows; ++r) {
-        const int64_t a = q0 + r;
-        const bool vis = key < p.Bb && a < p.Bb && a >= a_min;
-        float s = 0.0f, dpv = 0.0f;
-#pragma unroll
-        for (int e = 0; e < D; ++e) {
-          s = fmaf(qs[r * L::S + e], ks[tid * L::S + e], s);
-          dpv = fmaf(os[r * L::S + e], vs[tid * L::S + e], dpv);
+    for (int32_t gi = 0; gi < p.G; ++gi) {  // the query heads that read this K/V head
+      const int32_t h = hk * p.G + gi;
+      const float* qbase = reinterpret_cast<const float*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
+      const float* dobase = reinterpret_cast<const float*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch + h * p.dout.s_head;
+      const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
+      for (int32_t qt = (int32_t)(a_first / kF32Rows); qt < qtiles; ++qt) {
+        const int64_t q0 = (int64_t)qt * kF32Rows;
+        __syncthreads();
+        for (int idx = tid; idx < kF32Rows * D; idx += kF32Keys) {
+          const int r = idx / D, e = idx % D;
+          const int64_t x = q0 + r;
+          qs[r * L::S + e] = (x < p.Bb) ? qbase[x * p.q.s_tok + e] : 0.0f;
+          os[r * L::S + e] = (x < p.Bb) ? dobase[x * p.dout.s_tok + e] : 0.0f;
         }
-        const float pv = vis ? fexp2(fmaf(s, c2, -lse_s[r])) : 0.0f;
-        const float dsv = pv * (dpv - dsum_s[r]);
+        if (tid < kF32Rows) {
+          const int64_t x = q0 + tid;
+          lse_s[tid] = (x < p.Bb) ? p.lse[srow + x] * kLog2e : 0.0f;
+          dsum_s[tid] = (x < p.Bb) ? p.dsum[srow + x] : 0.0f;
+        }
+        __syncthreads();
+        for (int r = 0; r < kF32Rows; ++r) {
+          const int64_t a = q0 + r;
+          const bool vis = key < p.Bb && a < p.Bb && a >= a_min;
+          float s = 0.0f, dpv = 0.0f;
 #pragma unroll
-        for (int e = 0; e < D; ++e) {
-          dv[e] = fmaf(pv, os[r * L::S + e], dv[e]);
-          dk[e] = fmaf(dsv, qs[r * L::S + e], dk[e]);
+          for (int e = 0; e < D; ++e) {
+            s = fmaf(qs[r * L::S + e], ks[tid * L::S + e], s);
+            dpv = fmaf(os[r * L::S + e], vs[tid * L::S + e], dpv);
+          }
+          const float pv = vis ? fexp2(fmaf(s, c2, -lse_s[r])) : 0.0f;
+          const float dsv = pv * (dpv - dsum_s[r]);
+#pragma unroll
+          for (int e = 0; e < D; ++e) {
+            dv[e] = fmaf(pv, os[r * L::S + e], dv[e]);
+            dk[e] = fmaf(dsv, qs[r * L::S + e], dk[e]);
+          }
         }
       }
     }
   }
   if (key >= p.Bb) return;
-  float* dkrow = reinterpret_cast<float*>(p.dk.ptr) + j * p.dk.s_blk + b * p.dk.s_batch + key * p.dk.s_tok + h * p.dk.s_head;
-  float* dvrow = reinterpret_cast<float*>(p.dv.ptr) + j * p.dv.s_blk + b * p.dv.s_batch + key * p.dv.s_tok + h * p.dv.s_head;
+  float* dkrow = reinterpret_cast<float*>(p.dk.ptr) + j * p.dk.s_blk + b * p.dk.s_batch + key * p.dk.s_tok + hk * p.dk.s_head;
+  float* dvrow = reinterpret_cast<float*>(p.dv.ptr) + j * p.dv.s_blk + b * p.dv.s_batch + key * p.dv.s_tok + hk * p.dv.s_head;
 #pragma unroll
   for (int e = 0; e < D; ++e) {
     dkrow[e] = dk[e] * p.scale;
@@ -465,13 +482,13 @@ hipError_t launch_dyn(K kernel, int64_t grid, int threads, int bytes, hipStream_
 }  // namespace
 
 hipError_t launch_dkdv_bf16(const BwdParams& p, hipStream_t s) {
-  const int64_t grid = ((p.Bb + kKn - 1) / kKn) * (int64_t)p.P * p.B * p.H;
+  const int64_t grid = ((p.Bb + kKn - 1) / kKn) * (int64_t)p.P * p.B * p.Hk;
   if (p.D == 128) return launch_dyn(dkdv_bf16_kernel<128>, grid, kThreads, BwdLds<128>::BYTES, s, p);
   return launch_dyn(dkdv_bf16_kernel<64>, grid, kThreads, BwdLds<64>::BYTES, s, p);
 }
 
 hipError_t launch_dkdv_f32(const BwdParams& p, hipStream_t s) {
-  const int64_t grid = ((p.Bb + kF32Keys - 1) / kF32Keys) * (int64_t)p.P * p.B * p.H;
+  const int64_t grid = ((p.Bb + kF32Keys - 1) / kF32Keys) * (int64_t)p.P * p.B * p.Hk;
   if (p.D == 128) return launch_dyn(dkdv_f32_kernel<128>, grid, kF32Keys, BwdF32Lds<128>::BYTES, s, p);
   return launch_dyn(dkdv_f32_kernel<64>, grid, kF32Keys, BwdF32Lds<64>::BYTES, s, p);
 }

@@ -49,9 +49,10 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t tiles = (Bb + kQTm - 1) / kQTm;
   int32_t bh, ri, tile;
-  query_work_of(blockIdx.x, BH, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
+  query_work_of(blockIdx.x, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
+  const int32_t hk = h / p.G;  // the K/V head this query head reads
   const int32_t i = p.rank_begin + ri;
   const int32_t a0 = tile * kQTm;
   const int32_t aw = a0 + 32 * wave;
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   c0.a_hi = a_hi;
   c0.Bb = Bb;
   auto kv_base = [&](const Seq& sq, int32_t blk) {
-    return reinterpret_cast<const __bf16*>(sq.ptr) + (int64_t)blk * sq.s_blk + b * sq.s_batch + h * sq.s_head;
+    return reinterpret_cast<const __bf16*>(sq.ptr) + (int64_t)blk * sq.s_blk + b * sq.s_batch + hk * sq.s_head;
   };
   auto dma_tile = [&](const KvIter& t, int stage) {
     __bf16* st = lds + stage * L::STAGE;
@@ -285,9 +286,9 @@ __global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
     if (extent <= 0) continue;
     const int32_t ext_a = row_extent32(rel, a);  // this row sees keys 0 .. ext_a - 1
     const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + (int64_t)j * p.k.s_blk + b * p.k.s_batch +
-                         h * p.k.s_head;
+                         (h / p.G) * p.k.s_head;
     const float* vbase = reinterpret_cast<const float*>(p.v.ptr) + (int64_t)j * p.v.s_blk + b * p.v.s_batch +
-                         h * p.v.s_head;
+                         (h / p.G) * p.v.s_head;
     for (int32_t b0 = 0; b0 < extent; b0 += TN) {
       __syncthreads();
       for (int idx = tid; idx < TN * D; idx += kF32Rows) {

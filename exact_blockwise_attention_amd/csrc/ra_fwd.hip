@@ -103,9 +103,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t tiles = (Bb + kQTm - 1) / kQTm;
   int32_t bh, ri, tile;
-  query_work_of(blockIdx.x, BH, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
+  query_work_of(blockIdx.x, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
+  const int32_t hk = h / p.G;  // the K/V head this query head reads
   const int32_t i = p.rank_begin + ri;
   const int32_t a0 = tile * kQTm;
   const int32_t aw = a0 + 32 * wave;  // first row of this wave
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const int64_t kvblk_mul = (p.mode == 0) ? 1 : 0;  // the single-step buffer holds one block
   auto kv_base = [&](const Seq& sq, int32_t blk, int32_t r_lo) __attribute__((always_inline)) {
     return reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(sq.ptr) + kvblk_mul * blk * sq.s_blk +
-                                         b * sq.s_batch + h * sq.s_head + (int64_t)r_lo * sq.s_tok);
+                                         b * sq.s_batch + hk * sq.s_head + (int64_t)r_lo * sq.s_tok);
   };
   // Requests tile t into stage ST: this wave's CPW row groups of K and of V.
   // Rows at or beyond Bb read row Bb - 1 (finite data; masked later).
@@ -483,9 +484,9 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(FwdParams p) {
     const int64_t ext_a = row_extent(rel, a);  // this row sees keys 0 .. ext_a - 1
     const int64_t kblk = (p.mode == 0) ? (int64_t)j : 0;
     const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + kblk * p.k.s_blk + b * p.k.s_batch +
-                         h * p.k.s_head;
+                         (h / p.G) * p.k.s_head;
     const float* vbase = reinterpret_cast<const float*>(p.v.ptr) + kblk * p.v.s_blk + b * p.v.s_batch +
-                         h * p.v.s_head;
+                         (h / p.G) * p.v.s_head;
     for (int64_t b0 = 0; b0 < extent; b0 += TN) {
       __syncthreads();
       for (int idx = tid; idx < TN * D; idx += kF32Rows) {

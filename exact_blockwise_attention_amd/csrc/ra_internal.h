@@ -25,6 +25,7 @@ struct FwdParams {
   float* st_o;     // step mode: fp32 [n_ranks][B][H][Bb][D] normalised partial O
   float* st_lse;   // step mode: fp32 [n_ranks][B][H][Bb], log2 domain
   int32_t B, H, D, P;
+  int32_t Hk, G;   // K/V heads; query heads per K/V head (H = G * Hk)
   int64_t Bb;
   int32_t layout, causal;
   float scale_log2;  // scale * log2(e)
@@ -38,6 +39,7 @@ struct BwdParams {
   const float* lse;  // [n_ranks][B][H][Bb]
   float* dsum;       // workspace: D = rowsum(dO * O), [n_ranks][B][H][Bb]
   int32_t B, H, D, P;
+  int32_t Hk, G;     // K/V heads; query heads per K/V head (H = G * Hk)
   int64_t Bb;
   int32_t layout, causal;
   float scale, scale_log2;

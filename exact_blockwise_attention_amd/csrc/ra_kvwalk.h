@@ -45,19 +45,23 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t id, int64_t n) {
   return x * q + (x < r ? x : r) + s;
 }
 
-// Query-tile workgroups: consecutive logical indices share (batch, head,
-// rank) and take its query tiles heaviest first, so the workgroups resident
-// on one XCD walk the same KV tiles at about the same time and share them in
-// L2. Heavier ranks come first (contiguous causal work grows with the rank).
-__device__ __forceinline__ void query_work_of(int64_t id, int32_t BH, int32_t n_ranks, int32_t tiles,
-                                              int32_t causal, int32_t layout, int32_t* bh, int32_t* rank_idx,
-                                              int32_t* tile) {
+// Query-tile workgroups: consecutive logical indices share (batch, K/V
+// head, rank) and take its query tiles heaviest first, with the G query
+// heads that read one K/V head innermost, so the workgroups resident on one
+// XCD walk the same KV tiles at about the same time and share them in L2.
+// Heavier ranks come first (contiguous causal work grows with the rank).
+// bh = b * H + h, H = G * (K/V heads). The grid is below 2^31 workgroups.
+__device__ __forceinline__ void query_work_of(int64_t id, int32_t BH, int32_t G, int32_t n_ranks,
+                                              int32_t tiles, int32_t causal, int32_t layout, int32_t* bh,
+                                              int32_t* rank_idx, int32_t* tile) {
   const int64_t n = (int64_t)BH * n_ranks * tiles;
-  const int64_t L = xcd_logical(id, n);
-  const int64_t g = L / tiles;
-  *tile = tiles - 1 - (int32_t)(L % tiles);
-  *bh = (int32_t)(g / n_ranks);
-  const int32_t r = (int32_t)(g % n_ranks);
+  const uint32_t L = (uint32_t)xcd_logical(id, n);
+  const uint32_t gi = L % (uint32_t)G;
+  const uint32_t L2 = L / (uint32_t)G;
+  const uint32_t g = L2 / (uint32_t)tiles;
+  *tile = tiles - 1 - (int32_t)(L2 % (uint32_t)tiles);
+  *bh = (int32_t)(g / (uint32_t)n_ranks) * G + (int32_t)gi;
+  const int32_t r = (int32_t)(g % (uint32_t)n_ranks);
   *rank_idx = (causal && layout == kContiguous) ? n_ranks - 1 - r : r;
 }
 

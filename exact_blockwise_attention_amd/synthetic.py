@@ -49,16 +49,18 @@ class Workload:
     passes: tuple  # ("fwd",) or ("fwd", "bwd")
     q_ranks: tuple | None = None  # None: all ranks
     prefetch: bool = False
+    kv_heads: int = 0  # K/V heads (grouped-query attention); 0: the same as heads
 
     @property
     def block_len(self) -> int:
         return self.seq_len // self.ring_size
 
 
-# The five workloads: a tiny fp32 correctness case, a non-causal bf16 forward,
-# a causal forward in both layouts, one device's share of a 262,144-token
-# 7B-shaped layer (H=32, d=128) with a prefetched side-stream KV receive, and
-# a causal striped forward+backward at 32,768 tokens.
+# The workloads: a tiny fp32 correctness case, a non-causal bf16 forward, a
+# causal forward in every layout, one device's share of a 262,144-token
+# 7B-shaped layer (H=32, d=128) with a prefetched side-stream KV receive, a
+# causal striped forward+backward at 32,768 tokens, and the same with 8 K/V
+# heads shared by the 32 query heads (grouped-query attention).
 WORKLOADS = {
     1: Workload(1, "noncausal_f32_L1024_d64_P4", 1, 1, 1024, 64, 4, False,
                 ("contiguous",), "f32", ("fwd",)),
@@ -71,6 +73,8 @@ WORKLOADS = {
                 q_ranks=(7, 8), prefetch=True),
     5: Workload(5, "causal_striped_bf16_H32_L32768_d128_P8_fwdbwd", 1, 32,
                 32768, 128, 8, True, ("striped",), "bf16", ("fwd", "bwd")),
+    6: Workload(6, "causal_striped_gqa_bf16_H32_KV8_L32768_d128_P8_fwdbwd", 1, 32,
+                32768, 128, 8, True, ("striped",), "bf16", ("fwd", "bwd"), kv_heads=8),
 }
 
 
@@ -172,5 +176,7 @@ def make_tensor(workload_id: int, tensor: str, shape, dtype: str):
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def workload_shape(w: Workload):
-    return (w.batch, w.seq_len, w.heads, w.head_dim)
+def workload_shape(w: Workload, tensor: str = "q"):
+    """[B, L, heads, d] of an input: K and V have the workload's K/V heads."""
+    heads = (w.kv_heads or w.heads) if tensor in ("k", "v") else w.heads
+    return (w.batch, w.seq_len, heads, w.head_dim)

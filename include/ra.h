@@ -85,7 +85,14 @@ typedef enum {
 
 /* The problem: batch B, heads H, head dim d (= value dim), ring of P blocks
  * of block_len tokens each. Supported: head_dim 64 or 128; any block_len >= 1
- * (ragged tiles are masked); causal 0/1; layout matters only when causal. */
+ * (ragged tiles are masked); causal 0/1; layout matters only when causal.
+ * Grouped-query attention (blog, section "比較分析: Ring Attention vs
+ * Sequence Parallelism vs Tensor Parallelism": ring attention works with
+ * GQA/MQA unchanged): K, V, dK and dV have kv_heads heads, and query head h
+ * reads K/V head h / (heads / kv_heads) — consecutive query heads share one
+ * K/V head; dK/dV of a K/V head sum over the query heads that read it.
+ * kv_heads = 0 means kv_heads = heads (multi-head); otherwise it must divide
+ * heads (RA_ERR_SHAPE). lse, O, dQ and D have `heads` heads. */
 typedef struct {
   int32_t batch;
   int32_t heads;
@@ -96,6 +103,7 @@ typedef struct {
   int32_t causal;     /* 0 or 1 */
   float scale;        /* <= 0: 1/sqrt(head_dim) */
   int32_t dtype;      /* ra_dtype */
+  int32_t kv_heads;   /* heads of K, V, dK, dV; 0: same as heads */
 } ra_problem;
 
 /* A sequence tensor seen as ring blocks. Element (blk, b, x, h, e) — block,
@@ -190,7 +198,9 @@ ra_status ra_merge_lse(int64_t rows, int32_t head_dim, const float* o_a, const f
  * Attention"): copy an original-order [B, L, H, d] tensor `src` into blocked
  * order `dst` ([P][B][block_len][H][d], block of rank 0 first) for the given
  * layout, or back when inverse != 0. Pure data movement: bit-exact. Uses the
- * problem's batch, heads, head_dim, ring_size, block_len, layout and dtype. */
+ * problem's batch, heads, head_dim, ring_size, block_len, layout and dtype
+ * (H = heads: to copy the K or V of a grouped-query problem, pass a problem
+ * whose heads is its kv_heads). */
 ra_status ra_layout_copy(const ra_problem* pb, const void* src, void* dst, int32_t inverse,
                          hipStream_t stream);
 

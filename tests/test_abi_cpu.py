@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert ra.abi_version() == 1
+    assert ra.abi_version() == 2
     assert ra.status_string(0) == "ok"
     for code in range(1, 7):
         assert ra.status_string(code) not in ("ok", "unknown status")
@@ -48,10 +48,10 @@ def test_status_strings_and_version():
 
 
 def problem(**kw):
-    base = dict(B=1, H=2, d=64, P=4, Bb=64, layout="striped", causal=True, dtype_code=ra.BF16)
+    base = dict(B=1, H=2, d=64, P=4, Bb=64, layout="striped", causal=True, dtype_code=ra.BF16, kv_heads=0)
     base.update(kw)
     return ra.make_problem(base["B"], base["H"], base["d"], base["P"], base["Bb"], base["layout"],
-                           base["causal"], base["dtype_code"])
+                           base["causal"], base["dtype_code"], kv_heads=base["kv_heads"])
 
 
 def fake_seq(ptr=0x10000, s_blk=128, s_batch=1 << 20, s_tok=512, s_head=64):
@@ -81,11 +81,25 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, 2), ("heads", 0, 2), ("ring_size", 0, 2), ("block_len", 0, 2),
     ("layout", 3, 2), ("causal", 3, 2), ("dtype", 7, 2), ("head_dim", 96, 3), ("head_dim", 32, 3),
+    ("kv_heads", 3, 2), ("kv_heads", -1, 2),
 ])
 def test_invalid_problem_fields(field, value, code):
     pb = problem()
     setattr(pb, field, value)
     assert fwd_status(pb) == code
+
+
+def test_grouped_query_heads():
+    # K/V heads must divide the query heads; the receive buffers of the
+    # single-rank forward hold K/V blocks with the K/V head count
+    pb = problem(d=128, P=8, Bb=4096, H=32, kv_heads=8)
+    blk_kv = 1 * 4096 * 8 * 128 * 2
+    rows = 1 * 32 * 4096
+    assert ra.workspace_bytes(pb, 7, 8, True, False) == 4 * blk_kv + rows * 128 * 4 + rows * 4
+    assert ra.workspace_bytes(pb, 0, 8, False, True) == 8 * rows * 4  # D has one row per query head
+    assert ra.workspace_bytes(problem(H=32, kv_heads=1), 0, 4, False, True) > 0  # multi-query
+    assert ra.workspace_bytes(problem(H=32, kv_heads=12), 0, 4, False, True) == 0
+    assert ra.workspace_bytes(problem(H=4, kv_heads=8), 0, 4, False, True) == 0
 
 
 def test_zigzag_needs_an_even_block_length():

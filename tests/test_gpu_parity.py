@@ -3,8 +3,8 @@
 Small cases compare every element; they span several tiles, ragged tails
 (block lengths that are not tile multiples), all three layouts, causal and not,
 bf16 and fp32, head_dim 64 and 128, single-rank (double-buffered receive)
-and rank-range launches, and degenerate shapes (one block, one token per
-block). Bars: max |GPU - oracle| <= 2e-2 for bf16 inputs (fp32 accumulation)
+and rank-range launches, grouped-query and multi-query K/V heads, and
+degenerate shapes (one block, one token per block). Bars: max |GPU - oracle| <= 2e-2 for bf16 inputs (fp32 accumulation)
 and <= 1e-4 for fp32 inputs, on O, lse, dQ, dK and dV; data movement
 (layout gathers, pre-permuted vs strided inputs) must be bit-exact.
 """
@@ -13,7 +13,8 @@ import pytest
 
 import exact_blockwise_attention_amd as ra
 import oracle
-from gpu_cases import TOL, Case, assert_close, lse_to_original, log, payloads, rank_positions, to_device, to_f64
+from gpu_cases import (TOL, Case, assert_close, assert_output_close, lse_to_original, log, payloads,
+                       rank_positions, to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,7 +39,7 @@ def run_fwd(case, dev, rank_range=None, copy=False):
 def check_fwd(case, o, lse, ref_o, ref_lse, ranks):
     pos, lse_vals = lse_to_original(case, lse, ranks)
     tol = TOL[case.dtype]
-    assert_close("O", to_f64(o)[:, pos], ref_o[:, pos], tol, case)
+    assert_output_close("O", to_f64(o)[:, pos], ref_o[:, pos], case.dtype, case)
     assert_close("lse", lse_vals, ref_lse[:, pos], tol, case)
 
 
@@ -64,6 +65,13 @@ SMALL_FWD = [
     Case(117, 1, 2, 16, 128, 8, True, "zigzag", "bf16"),
     Case(118, 1, 1, 4096, 128, 2, True, "zigzag", "bf16"),
     Case(119, 1, 2, 600, 128, 3, False, "zigzag", "bf16"),
+    # grouped-query (Hk K/V heads shared by H query heads) and multi-query
+    Case(161, 1, 4, 800, 128, 4, True, "striped", "bf16", Hk=2),
+    Case(162, 1, 6, 520, 64, 4, True, "contiguous", "bf16", Hk=1),
+    Case(163, 1, 4, 800, 128, 4, True, "zigzag", "bf16", Hk=1),
+    Case(164, 1, 4, 400, 64, 4, True, "striped", "f32", Hk=2),
+    Case(165, 2, 6, 1024, 128, 2, False, "contiguous", "bf16", Hk=3),
+    Case(166, 1, 8, 2048, 128, 2, True, "striped", "bf16", Hk=2),
 ]
 
 
@@ -88,6 +96,8 @@ STEP_CASES = [
     Case(123, 1, 2, 520, 64, 4, False, "contiguous", "bf16"),
     Case(124, 1, 1, 400, 64, 4, True, "striped", "f32"),
     Case(125, 1, 2, 800, 128, 4, True, "zigzag", "bf16"),
+    Case(126, 1, 4, 800, 128, 4, True, "striped", "bf16", Hk=2),
+    Case(127, 1, 2, 400, 64, 4, True, "contiguous", "f32", Hk=1),
 ]
 
 
@@ -199,6 +209,12 @@ SMALL_BWD = [
     Case(150, 1, 2, 800, 128, 4, True, "zigzag", "bf16"),
     Case(151, 1, 2, 400, 64, 4, True, "zigzag", "f32"),
     Case(152, 1, 1, 1000, 64, 5, True, "zigzag", "bf16"),
+    # grouped-query and multi-query: dK/dV of a K/V head sum over its group
+    Case(153, 1, 4, 800, 128, 4, True, "striped", "bf16", Hk=2),
+    Case(154, 1, 3, 650, 64, 5, True, "contiguous", "bf16", Hk=1),
+    Case(155, 1, 4, 800, 128, 4, True, "zigzag", "bf16", Hk=1),
+    Case(156, 1, 4, 400, 64, 4, True, "striped", "f32", Hk=2),
+    Case(157, 2, 6, 512, 128, 4, False, "contiguous", "bf16", Hk=3),
 ]
 
 
@@ -219,16 +235,16 @@ def test_backward_small(case):
     dq_r, dk_r, dv_r, _, _ = oracle.attention_bwd(f["q"], f["k"], f["v"], f["do"], case.causal)
     dq, dk, dv = run_bwd(case, dev)
     tol = TOL[case.dtype]
-    assert_close("dQ", to_f64(dq), dq_r, tol, case)
-    assert_close("dK", to_f64(dk), dk_r, tol, case)
-    assert_close("dV", to_f64(dv), dv_r, tol, case)
+    assert_output_close("dQ", to_f64(dq), dq_r, case.dtype, case)
+    assert_output_close("dK", to_f64(dk), dk_r, case.dtype, case)
+    assert_output_close("dV", to_f64(dv), dv_r, case.dtype, case)
 
 
-@pytest.mark.parametrize("layout", ["striped", "zigzag"])
-def test_backward_rank_range(layout):
+@pytest.mark.parametrize("layout,hk", [("striped", 0), ("zigzag", 0), ("striped", 1)])
+def test_backward_rank_range(layout, hk):
     """Ranks [1, 3): dQ of their rows, and dK/dV holding only their queries'
     contributions (the oracle's gradient with dO zero outside those rows)."""
-    case = Case(149, 1, 2, 800, 128, 4, True, layout, "bf16")
+    case = Case(149, 1, 2, 800, 128, 4, True, layout, "bf16", Hk=hk)
     log(f"backward rank range [1,3) {case}")
     p = payloads(case, ("q", "k", "v", "do"))
     dev = {n: to_device(x) for n, x in p.items()}
@@ -239,6 +255,6 @@ def test_backward_rank_range(layout):
     dq_r, dk_r, dv_r, _, _ = oracle.attention_bwd(f["q"], f["k"], f["v"], do_masked, case.causal)
     dq, dk, dv = run_bwd(case, dev, rank_range=(1, 3))
     tol = TOL[case.dtype]
-    assert_close("dQ", to_f64(dq)[:, pos], dq_r[:, pos], tol, case)
-    assert_close("dK", to_f64(dk), dk_r, tol, case)
-    assert_close("dV", to_f64(dv), dv_r, tol, case)
+    assert_output_close("dQ", to_f64(dq)[:, pos], dq_r[:, pos], case.dtype, case)
+    assert_output_close("dK", to_f64(dk), dk_r, case.dtype, case)
+    assert_output_close("dV", to_f64(dv), dv_r, case.dtype, case)

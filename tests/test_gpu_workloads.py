@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the five workloads, in the launch
+"""GPU parity at the full sizes of the six workloads, in the launch
 configurations the benchmark times.
 
 Outputs are compared on samples the oracle can compute one by one: every
@@ -13,7 +13,7 @@ import pytest
 import exact_blockwise_attention_amd as ra
 import oracle
 from exact_blockwise_attention_amd import synthetic as syn
-from gpu_cases import TOL, assert_close, log, to_device, to_f64
+from gpu_cases import TOL, assert_close, assert_output_close, log, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +34,7 @@ def sample_rows(n, count, seed):
 
 
 def inputs(w, names=("q", "k", "v")):
-    shape = syn.workload_shape(w)
-    return {n: syn.make_payload(w.wid, n, shape, w.dtype) for n in names}
+    return {n: syn.make_payload(w.wid, n, syn.workload_shape(w, n), w.dtype) for n in names}
 
 
 def heads_f64(x, heads):
@@ -58,7 +57,7 @@ def check_rows(w, layout, o_dev, lse_dev, p, ranks, q_pos_local, heads, tol):
     ri = q_pos_local // Bb
     x = q_pos_local % Bb
     got_lse = np.stack([lse[ri, :, h, x] for h in heads], axis=-1).transpose(1, 0, 2)
-    assert_close(f"O[{layout}]", o, ref_o, tol, w.name)
+    assert_output_close(f"O[{layout}]", o, ref_o, w.dtype, w.name)
     assert_close(f"lse[{layout}]", got_lse, ref_lse, tol, w.name)
 
 
@@ -70,7 +69,7 @@ def test_workload1_fp32_noncausal_full():
     o, lse = ra.attention_forward(dev["q"], dev["k"], dev["v"], w.ring_size, "contiguous", False)
     torch.cuda.synchronize()
     ref_o, ref_lse = oracle.attention_fwd(*(syn.to_f64(p[n]) for n in "qkv"), False)
-    assert_close("O", to_f64(o), ref_o, TOL["f32"], w.name)
+    assert_output_close("O", to_f64(o), ref_o, w.dtype, w.name)
     got_lse = lse.cpu().numpy().transpose(1, 0, 3, 2).reshape(1, -1, 1)
     assert_close("lse", got_lse, ref_lse, TOL["f32"], w.name)
 
@@ -128,7 +127,7 @@ def test_workload4_one_rank_share_with_receive_stream():
     ref_o, ref_lse = oracle.attention_fwd(q[:, rows], k, v, True, q_pos=pos_r[rows])
     got_o = to_f64(o[:, torch.as_tensor(rows, device="cuda")][:, :, heads])
     got_lse = lse.cpu().numpy()[0][:, heads][:, :, rows].transpose(0, 2, 1)
-    assert_close("O", got_o, ref_o, TOL["bf16"], w.name)
+    assert_output_close("O", got_o, ref_o, w.dtype, w.name)
     assert_close("lse", got_lse, ref_lse, TOL["bf16"], w.name)
 
 
@@ -148,7 +147,34 @@ def test_workload5_forward_backward():
     dq_r, dk_r, dv_r, o_r, lse_r = oracle.attention_bwd_sampled(f["q"], f["k"], f["v"], f["do"], True, qrows, krows)
     tol = TOL["bf16"]
     sel = lambda t, rows: to_f64(t[:, torch.as_tensor(rows, device="cuda")][:, :, heads])  # noqa: E731
-    assert_close("O", sel(o, qrows), o_r[:, qrows], tol, w.name)
-    assert_close("dQ", sel(dq, qrows), dq_r, tol, w.name)
-    assert_close("dK", sel(dk, krows), dk_r, tol, w.name)
-    assert_close("dV", sel(dv, krows), dv_r, tol, w.name)
+    assert_output_close("O", sel(o, qrows), o_r[:, qrows], w.dtype, w.name)
+    assert_output_close("dQ", sel(dq, qrows), dq_r, w.dtype, w.name)
+    assert_output_close("dK", sel(dk, krows), dk_r, w.dtype, w.name)
+    assert_output_close("dV", sel(dv, krows), dv_r, w.dtype, w.name)
+
+
+def test_workload6_grouped_query_forward_backward():
+    """32 query heads on 8 K/V heads: two whole groups (query heads 0-3 on
+    K/V head 0, 28-31 on K/V head 7), so that dK/dV of those K/V heads are
+    the sum over their group, as the oracle computes them."""
+    w = syn.WORKLOADS[6]
+    log(f"workload {w.name}")
+    p = inputs(w, ("q", "k", "v", "do"))
+    dev = {n: to_device(x) for n, x in p.items()}
+    P = w.ring_size
+    o, lse = ra.attention_forward(dev["q"], dev["k"], dev["v"], P, "striped", True)
+    dq, dk, dv = ra.attention_backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, P, "striped", True)
+    torch.cuda.synchronize()
+    G = w.heads // w.kv_heads
+    kv_sel = [0, w.kv_heads - 1]
+    q_sel = [g * G + x for g in kv_sel for x in range(G)]
+    qrows = sample_rows(w.seq_len, 256, 61)
+    krows = sample_rows(w.seq_len, 256, 62)
+    f = {n: heads_f64(p[n], kv_sel if n in ("k", "v") else q_sel) for n in ("q", "k", "v", "do")}
+    dq_r, dk_r, dv_r, o_r, lse_r = oracle.attention_bwd_sampled(f["q"], f["k"], f["v"], f["do"], True, qrows, krows)
+    tol = TOL["bf16"]
+    sel = lambda t, rows, hs: to_f64(t[:, torch.as_tensor(rows, device="cuda")][:, :, hs])  # noqa: E731
+    assert_output_close("O", sel(o, qrows, q_sel), o_r[:, qrows], w.dtype, w.name)
+    assert_output_close("dQ", sel(dq, qrows, q_sel), dq_r, w.dtype, w.name)
+    assert_output_close("dK", sel(dk, krows, kv_sel), dk_r, w.dtype, w.name)
+    assert_output_close("dV", sel(dv, krows, kv_sel), dv_r, w.dtype, w.name)
