@@ -121,6 +121,74 @@ def workload_name(w, layout):
     return w.name.replace("causal_", f"causal_{layout}_", 1) if w.causal else w.name
 
 
+def hbm_row(ms, nbytes):
+    """An HBM-bound launch: algorithmic bytes over its time, against 8 TB/s."""
+    gbs = nbytes / ms / 1e6
+    return {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def time_calls(torch, stream, fn, n=5):
+    """Average ms of n back-to-back calls, HIP events on the launch stream
+    (after one untimed call)."""
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def memory_rows(torch, ra, w, q, sh, stream):
+    """The HBM-bound calls on the workload's shapes, timed outside the step:
+    the log-sum-exp merge of two fp32 partial results for every query row
+    (read 2(4d+4), write 4d+4 bytes per row) and the layout gather of Q
+    (read and write every byte once)."""
+    d = w.head_dim
+    rows = w.batch * w.heads * w.seq_len
+    g = torch.Generator(device="cuda").manual_seed(w.wid)
+    oa = torch.randn((rows, d), generator=g, device="cuda")
+    ob = torch.randn((rows, d), generator=g, device="cuda")
+    la = torch.randn((rows,), generator=g, device="cuda")
+    lb = torch.randn((rows,), generator=g, device="cuda")
+    oo, lo = torch.empty_like(oa), torch.empty_like(la)
+    merge_ms = time_calls(torch, stream, lambda: ra.merge_lse_raw(rows, d, oa.data_ptr(), la.data_ptr(), ob.data_ptr(),
+                                                                  lb.data_ptr(), oo.data_ptr(), lo.data_ptr(), sh))
+    del oa, ob, oo
+    B, L, H, _ = q.shape
+    P = w.ring_size
+    blk = torch.empty((P, B, L // P, H, d), dtype=q.dtype, device="cuda")
+    pb = ra.make_problem(B, H, d, P, L // P, "striped", True, ra.BF16 if w.dtype == "bf16" else ra.F32)
+    copy_ms = time_calls(torch, stream, lambda: ra.layout_copy_raw(pb, q.data_ptr(), blk.data_ptr(), False, sh))
+    del blk
+    return {"F7_merge_lse": hbm_row(merge_ms, rows * (3 * 4 * d + 3 * 4)),
+            "F0_layout_copy_striped_q": hbm_row(copy_ms, 2 * q.numel() * q.element_size())}
+
+
+def receive_overlap(torch, ra, w, t, pb, rb, re_, so, sk, o, lse, sh, stream, total_ms):
+    """One device's share with the next KV block copied on a second stream:
+    c = compute per ring step (the same rank's ring in one launch, KV read in
+    place, divided by P), m = the copy per step (the library's striped gather
+    of the whole K, then V, divided by P: per step one K and one V block, read
+    and written once), and how close the overlapped call comes to P max(c, m)."""
+    P = w.ring_size
+    c_all = time_calls(torch, stream, lambda: ra.forward_raw(pb, rb, re_, so(t["q"]), sk(t["k"]), sk(t["v"]), so(o),
+                                                            lse.data_ptr(), None, 0, sh, None), n=2)
+    B, L, Hk, d = t["k"].shape
+    blk = torch.empty((P, B, L // P, Hk, d), dtype=t["k"].dtype, device="cuda")
+    pbk = ra.make_problem(B, Hk, d, P, L // P, "striped", True, ra.BF16)
+    gk = time_calls(torch, stream, lambda: ra.layout_copy_raw(pbk, t["k"].data_ptr(), blk.data_ptr(), False, sh), n=2)
+    gv = time_calls(torch, stream, lambda: ra.layout_copy_raw(pbk, t["v"].data_ptr(), blk.data_ptr(), False, sh), n=2)
+    del blk
+    c, m = c_all / P, (gk + gv) / P
+    step_bytes = 2 * 2 * (t["k"].numel() // P) * t["k"].element_size()
+    return {"c_ms": round(c, 4), "m_ms": round(m, 4), "m_GB/s": round(step_bytes / m / 1e6, 1),
+            "overlapped_ms": round(total_ms, 4), "serial_bound_ms": round(P * (c + m), 4),
+            "overlap_efficiency": round(P * max(c, m) / total_ms, 4)}
+
+
 def cpu_baseline(w):
     """Oracle (float64 numpy) on a bounded sample of the workload."""
     import numpy as np
@@ -310,6 +378,14 @@ def main():
             "frac": round(achieved / peak, 4), "traffic": read_traffic(tag), "launch_ms": round(dom_ms, 4)}
     if w.prefetch:
         roof["note"] = "one call of 8 step launches plus the side-stream copies, timed as a whole"
+    if bwd:
+        B_, H_ = w.batch, w.heads
+        # D = rowsum(dO * O): reads O and dO rows, writes one fp32 per row
+        pre_bytes = len(ranks) * B_ * H_ * Bb * (2 * d_ * t["q"].element_size() + 4)
+        details["memory_rows"] = {"B1_rowsum_dO_O": hbm_row(details["bwd_pre_ms"], pre_bytes),
+                                  **memory_rows(torch, ra, w, t["q"], sh, stream)}
+    if w.prefetch:
+        details["receive_overlap"] = receive_overlap(torch, ra, w, t, pb, rb, re_, so, sk, o, lse, sh, stream, ms)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
     gqa_tag = f", {w.heads} query heads on {w.kv_heads} K/V heads" if w.kv_heads else ""
     out = {
