@@ -92,14 +92,16 @@ FwdWs fwd_ws_layout(const ra_problem* pb, int32_t n_ranks, int32_t copy) {
 }
 
 struct BwdWs {
-  size_t dsum, total;
+  size_t dsum, lse2, total;
 };
 
+// D = rowsum(dO * O) and lse in log2 units, one fp32 per query row each
 BwdWs bwd_ws_layout(const ra_problem* pb, int32_t n_ranks) {
   BwdWs w{};
   const size_t rows = (size_t)n_ranks * pb->batch * pb->heads * pb->block_len;
   w.dsum = 0;
-  w.total = align_up(rows * sizeof(float));
+  w.lse2 = align_up(rows * sizeof(float));
+  w.total = w.lse2 + align_up(rows * sizeof(float));
   return w;
 }
 
@@ -267,6 +269,7 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
   p.dv = to_seq(dv);
   p.lse = lse;
   p.dsum = reinterpret_cast<float*>(ws + w.dsum);
+  p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   p.B = pb->batch;
   p.H = pb->heads;
   p.Hk = kv_heads_of(pb);

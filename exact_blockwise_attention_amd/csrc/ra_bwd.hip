@@ -36,8 +36,6 @@
 namespace ra {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKn = 128;  // keys per workgroup (32 per wave, two waves per key group)
@@ -112,11 +110,13 @@ __device__ __forceinline__ void dma_qtile(const BwdParams& p, const QTileIter& i
   const __bf16* qb = reinterpret_cast<const __bf16*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
   const __bf16* ob = reinterpret_cast<const __bf16*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch +
                      h * p.dout.s_head;
+  // the 4-byte copies go first: issued after the 16-byte ones, they make the
+  // compiler wait for those to land
+  const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
+  if (wave == 0) dma_f32_64(f32s + stage * kQm, p.lse2 + srow, q0, Bb, lane);
+  if (wave == 1) dma_f32_64(f32s + 2 * kQm + stage * kQm, p.dsum + srow, q0, Bb, lane);
   dma_rows<D, kQm, kWaves>(lds + L::Q + stage * kQm * D, qb, p.q.s_tok, q0, Bb, wave, lane);
   dma_rows<D, kQm, kWaves>(lds + L::DO + stage * kQm * D, ob, p.dout.s_tok, q0, Bb, wave, lane);
-  const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
-  if (wave == 0) dma_f32_64(f32s + stage * kQm, p.lse + srow, q0, Bb, lane);
-  if (wave == 1) dma_f32_64(f32s + 2 * kQm + stage * kQm, p.dsum + srow, q0, Bb, lane);
 }
 
 template <int D>
@@ -185,31 +185,48 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   const bool any = cur.step_rank();
   if (any) dma_qtile<D>(p, cur, b, hk * p.G + cur.gi, lds, f32s, 0, wave, lane);
   wait_dma();  // K, V and the first query tile
-  // per-lane element offsets: row operands at rows n (+32 key group / +32
-  // row half) and columns 16ss + 8hf; transposing reads at rows
-  // 4hf + j16/4 (+8) (+32qh + 16kq) and columns 32dt + 16grp + 4(j16%4)
-  int roff[D / 16], toff[2][D / 32];
+  // LDS addresses (bytes) of this lane's reads, as per-lane bases plus
+  // compile-time offsets, so that the walk spends no instructions on them:
+  //   bkv[ss]: K row n of the wave's key group, columns 16ss + 8hf (V: + V_B)
+  //   bq[ss]:  Q row n of the wave's row half, same columns (query stage ST:
+  //            + ST * QST_B; dO: + DO_B)
+  //   bt[h2][dt]: transposing reads of Q / dO at rows 4hf + j16/4 + 8h2
+  //            (+16kq) of the row half, columns 32dt + 16grp + 4(j16%4)
+  //   bl:      lse2 of rows 32qh + 4hf .. of stage 0 (D: + DS_B)
+  constexpr int V_B = 2 * (L::V - L::K);
+  constexpr int QST_B = 2 * kQm * D;
+  constexpr int DO_B = 2 * (L::DO - L::Q);
+  constexpr int DS_B = 4 * 2 * kQm;
+  static_assert(V_B < 65536 && DO_B + 2 * QST_B <= 65536, "LDS read offsets must fit the 16-bit field");
+  const uint32_t lbase = lds_addr(smem_raw);
+  uint32_t bkv[D / 16], bq[D / 16], bt[2][D / 32];
 #pragma unroll
-  for (int ss = 0; ss < D / 16; ++ss) roff[ss] = tile_off<D>(n, 16 * ss + 8 * hf);
+  for (int ss = 0; ss < D / 16; ++ss) {
+    const int c = tile_off<D>(n, 16 * ss + 8 * hf);
+    bkv[ss] = lbase + 2 * (L::K + c + 32 * kg * D);
+    bq[ss] = lbase + 2 * (L::Q + c + 32 * qh * D);
+  }
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
-      toff[h2][dt] = tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
-  int stage = 0;
-  while (any) {
+      bt[h2][dt] = lbase + 2 * (L::Q + 32 * qh * D +
+                                tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4)));
+  const uint32_t bl = lbase + L::F32_OFF + 4 * (32 * qh + 4 * hf);
+
+  // One query tile in stage ST: recompute S and P, dP, dS; dV^T += dO^T P,
+  // dK^T += Q^T dS. The next tile is copied into the other stage meanwhile.
+  // Returns whether there is a next tile.
+  auto step = [&](auto STc) __attribute__((always_inline)) -> bool {
+    constexpr int ST = decltype(STc)::value;
     __syncthreads();  // this query stage is in LDS; the other one is no longer read
     QTileIter nx = cur;
     const bool more = nx.next();
-    if (more) dma_qtile<D>(p, nx, b, hk * p.G + nx.gi, lds, f32s, stage ^ 1, wave, lane);  // lands during the compute below
+    if (more) dma_qtile<D>(p, nx, b, hk * p.G + nx.gi, lds, f32s, ST ^ 1, wave, lane);  // lands during the compute below
 
     const BlockRel rel = block_relation(p.layout, p.causal, cur.i, j, Bb);
     const int32_t q0 = cur.qt * kQm;
     const int32_t qw = q0 + 32 * qh;  // first row of this wave
-    const __bf16* qs = lds + L::Q + stage * kQm * D;
-    const __bf16* os = lds + L::DO + stage * kQm * D;
-    const float* lse_s = f32s + stage * kQm;
-    const float* dsum_s = f32s + 2 * kQm + stage * kQm;
     // row extents grow with the row: the wave's last row sees the most keys,
     // its first row the fewest
     const bool dead = (kw >= Bb) || (qw >= Bb) || (row_extent32(rel, qw + 31) <= kw);
@@ -217,28 +234,39 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       const bool need_mask = (row_extent32(rel, qw) < kw + 32) || (qw + 32 > Bb);
       // rows a >= a_min see this lane's key (only needed when masking)
       const int32_t a_min = need_mask ? first_row_seeing32(rel, key, Bb) : 0;
+      // S = Q K^T and dP = dO V^T over the features: the Q, K, dO and V
+      // fragments of one 16-feature step are read one step ahead of their
+      // MFMAs
       f32x16 s = {}, dp = {};
+      u32x4 rg[2][4];
+      auto rd = [&](u32x4(&r)[4], int ss) __attribute__((always_inline)) {
+        r[0] = lds_read16<ST * QST_B>(bq[ss]);
+        r[1] = lds_read16<0>(bkv[ss]);
+        r[2] = lds_read16<DO_B + ST * QST_B>(bq[ss]);
+        r[3] = lds_read16<V_B>(bkv[ss]);
+      };
+      rd(rg[0], 0);
 #pragma unroll
       for (int ss = 0; ss < D / 16; ++ss) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + roff[ss] + 32 * qh * D);
-        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(lds + L::K + roff[ss] + 32 * kg * D);
-        s = mfma32(qa, kb, s);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(os + roff[ss] + 32 * qh * D);
-        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(lds + L::V + roff[ss] + 32 * kg * D);
-        dp = mfma32(oa, vb, dp);
+        if (ss + 1 < D / 16) {
+          rd(rg[(ss + 1) & 1], ss + 1);
+          lds_wait<4>(rg[ss & 1]);
+        } else {
+          lds_wait<0>(rg[ss & 1]);
+        }
+        s = mfma32(__builtin_bit_cast(bf16x8, rg[ss & 1][0]), __builtin_bit_cast(bf16x8, rg[ss & 1][1]), s);
+        dp = mfma32(__builtin_bit_cast(bf16x8, rg[ss & 1][2]), __builtin_bit_cast(bf16x8, rg[ss & 1][3]), dp);
       }
       // lane (hf, n): key n against rows 8(i/4) + 4hf + i%4 of the wave's 32.
-      // lse and D of rows 8g + 4hf .. +3 are read one group ahead (inline
-      // LDS reads: see lds_read16).
+      // lse2 and D of rows 8g + 4hf .. +3 are read one group ahead.
       bf16x8 pb[2], dsb[2];
-      const uint32_t la = lds_addr(lse_s + 32 * qh + 4 * hf), dla = lds_addr(dsum_s + 32 * qh + 4 * hf);
-      u32x4 ldr[2][2];  // [slot][lse, D]
+      u32x4 ldr[2][2];  // [slot][lse2, D]
       auto ld_rows = [&](u32x4(&r)[2], int g) __attribute__((always_inline)) {
         switch (g) {
-          case 0: r[0] = lds_read16<0>(la); r[1] = lds_read16<0>(dla); break;
-          case 1: r[0] = lds_read16<32>(la); r[1] = lds_read16<32>(dla); break;
-          case 2: r[0] = lds_read16<64>(la); r[1] = lds_read16<64>(dla); break;
-          default: r[0] = lds_read16<96>(la); r[1] = lds_read16<96>(dla); break;
+          case 0: r[0] = lds_read16<ST * 4 * kQm + 0>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 0>(bl); break;
+          case 1: r[0] = lds_read16<ST * 4 * kQm + 32>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 32>(bl); break;
+          case 2: r[0] = lds_read16<ST * 4 * kQm + 64>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 64>(bl); break;
+          default: r[0] = lds_read16<ST * 4 * kQm + 96>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 96>(bl); break;
         }
       };
       ld_rows(ldr[0], 0);
@@ -253,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         const int qr0 = 32 * qh + 8 * g + 4 * hf;  // row within the 64-row tile
         const float4 l4 = __builtin_bit_cast(float4, ldr[g & 1][0]);
         const float4 d4 = __builtin_bit_cast(float4, ldr[g & 1][1]);
-        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};  // lse in log2 units
         const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -270,22 +298,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       }
       // dV^T += dO^T P, dK^T += Q^T dS: contraction over the wave's 32 rows.
       // The transposing reads of (dt, kq) come in groups of 4, one group
-      // ahead of their MFMAs (inline LDS reads: see tr_read_at).
-      const uint32_t oa = lds_addr(os + 32 * qh * D), qa = lds_addr(qs + 32 * qh * D);
+      // ahead of their MFMAs.
       auto tr_group = [&](u32x2(&r)[2][2], int idx) __attribute__((always_inline)) {
         const int dt = idx / 2;
-        const uint32_t o0 = oa + 2 * toff[0][dt], o1 = oa + 2 * toff[1][dt];
-        const uint32_t q0a = qa + 2 * toff[0][dt], q1a = qa + 2 * toff[1][dt];
         if (idx % 2 == 0) {
-          r[0][0] = tr_read_at<0>(o0);
-          r[0][1] = tr_read_at<0>(o1);
-          r[1][0] = tr_read_at<0>(q0a);
-          r[1][1] = tr_read_at<0>(q1a);
+          r[0][0] = tr_read_at<DO_B + ST * QST_B>(bt[0][dt]);
+          r[0][1] = tr_read_at<DO_B + ST * QST_B>(bt[1][dt]);
+          r[1][0] = tr_read_at<ST * QST_B>(bt[0][dt]);
+          r[1][1] = tr_read_at<ST * QST_B>(bt[1][dt]);
         } else {
-          r[0][0] = tr_read_at<16 * D * 2>(o0);
-          r[0][1] = tr_read_at<16 * D * 2>(o1);
-          r[1][0] = tr_read_at<16 * D * 2>(q0a);
-          r[1][1] = tr_read_at<16 * D * 2>(q1a);
+          r[0][0] = tr_read_at<DO_B + ST * QST_B + 16 * D * 2>(bt[0][dt]);
+          r[0][1] = tr_read_at<DO_B + ST * QST_B + 16 * D * 2>(bt[1][dt]);
+          r[1][0] = tr_read_at<ST * QST_B + 16 * D * 2>(bt[0][dt]);
+          r[1][1] = tr_read_at<ST * QST_B + 16 * D * 2>(bt[1][dt]);
         }
       };
       constexpr int NG = 2 * (D / 32);
@@ -306,11 +331,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         dk[dt] = mfma32(qt, dsb[kq], dk[dt]);
       }
     }
-    if (!more) break;
+    if (!more) return false;
     wait_dma();
     cur = nx;
-    stage ^= 1;
-  }
+    return true;
+  };
+  if (any)
+    while (step(ic<0>{}) && step(ic<1>{})) {
+    }
 
   // the two waves of a key group add their partial dK^T, then dV^T
   float* red = reinterpret_cast<float*>(smem_raw);  // [4 key groups][D/32*16 values][64 lanes]
@@ -437,7 +465,7 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
         }
         if (tid < kF32Rows) {
           const int64_t x = q0 + tid;
-          lse_s[tid] = (x < p.Bb) ? p.lse[srow + x] * kLog2e : 0.0f;
+          lse_s[tid] = (x < p.Bb) ? p.lse2[srow + x] : 0.0f;
           dsum_s[tid] = (x < p.Bb) ? p.dsum[srow + x] : 0.0f;
         }
         __syncthreads();

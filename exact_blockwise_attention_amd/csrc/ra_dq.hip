@@ -26,11 +26,6 @@
 namespace ra {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-
-template <int N>
-using ic = std::integral_constant<int, N>;
-
 template <int D>
 __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   using L = KvLds<D>;
@@ -76,7 +71,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
     oreg[ss] = __builtin_bit_cast(bf16x8, vo);
   }
   const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
-  const float lse2 = (a < Bb) ? p.lse[srow + a] * kLog2e : 0.0f;
+  const float lse2 = (a < Bb) ? p.lse2[srow + a] : 0.0f;  // log2 units
   const float dsum = (a < Bb) ? p.dsum[srow + a] : 0.0f;
 
   f32x16 acc[D / 32];  // dQ^T: feature 32dt + 8(i/4) + 4hf + i%4, query n
@@ -214,7 +209,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
       if (!w1) break;
       if (v3) wait_vm<NI>();  // tile c2 (read from the next step on) is in LDS
       else wait_dma();
-      __syncthreads();  // stage sc is free
+      wg_barrier();  // stage sc is free
       c0 = c1;
       c1 = c2;
       c2 = c3;
@@ -276,7 +271,7 @@ __global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
     dq[e] = 0.0f;
   }
   const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
-  const float lse2 = live ? p.lse[srow + a] * kLog2e : 0.0f;
+  const float lse2 = live ? p.lse2[srow + a] : 0.0f;
   const float dsum = live ? p.dsum[srow + a] : 0.0f;
   const float c2 = p.scale_log2;
   for (int32_t kstep = 0; kstep < p.P; ++kstep) {

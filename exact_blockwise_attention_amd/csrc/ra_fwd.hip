@@ -48,9 +48,6 @@ namespace {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a tile max may exceed the reference max
 
-template <int N>
-using ic = std::integral_constant<int, N>;
-
 // LDS of the bf16 forward: NST stages of a K tile and a V tile ([64][D],
 // swizzled), K tiles first.
 template <int D>
@@ -71,10 +68,6 @@ struct FwdDma {
   static constexpr int NI = 2 * CPW;  // instructions per tile per wave (K and V)
   static_assert(CPW >= 1 && (kKvTn / RW) % kQWaves == 0, "tile copies must split over the waves");
 };
-
-// Workgroup barrier without the implicit memory waits of __syncthreads: the
-// kernel waits for exactly the loads it needs before each barrier.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // max over the two half-waves (lanes n and n ^ 32)
 __device__ __forceinline__ float halves_max(float x) {

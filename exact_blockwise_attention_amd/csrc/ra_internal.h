@@ -38,6 +38,7 @@ struct BwdParams {
   Seq q, k, v, o, dout, dq, dk, dv;
   const float* lse;  // [n_ranks][B][H][Bb]
   float* dsum;       // workspace: D = rowsum(dO * O), [n_ranks][B][H][Bb]
+  float* lse2;       // workspace: lse * log2(e) (the exponent base the kernels use), same layout
   int32_t B, H, D, P;
   int32_t Hk, G;     // K/V heads; query heads per K/V head (H = G * Hk)
   int64_t Bb;

@@ -144,6 +144,12 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier without the implicit memory waits of __syncthreads
+// (which drain every copy in flight, also those for later tiles): the kernel
+// waits for exactly the copies it needs before it, and every LDS read before
+// it has been consumed, so none is still pending.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace ra
 
 #endif  // RA_KVWALK_H_

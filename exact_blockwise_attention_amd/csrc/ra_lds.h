@@ -24,7 +24,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ra {
+
+// A compile-time index (an LDS stage, an offset) passed to a generic lambda.
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));

@@ -139,7 +139,10 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p, int32_
     for (int k = 0; k < 8; ++k) acc = fmaf(o8[k], d8[k], acc);
   }
   for (int off = tpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) p.dsum[row] = acc;
+  if (row < rows && part == 0) {
+    p.dsum[row] = acc;
+    p.lse2[row] = p.lse[row] * 1.44269504088896340736f;  // log2(e): the walks use exp2
+  }
 }
 
 inline uint32_t grid_for(int64_t items, int32_t per_block) {

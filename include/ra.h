@@ -172,10 +172,11 @@ ra_status ra_backward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end
                       size_t workspace_bytes, hipStream_t compute);
 
 /* One stage of ra_backward, with the same arguments (ra_backward runs stages
- * 0, 1, 2 in order on `compute`): 0 = D = rowsum(dO * O) into the workspace;
+ * 0, 1, 2 in order on `compute`): 0 = D = rowsum(dO * O), and lse in base-2
+ * units, into the workspace;
  * 1 = the key-side ring walk (recompute S and P, dP, dS; dV and dK);
  * 2 = the query-side ring walk (recompute S, P, dP, dS; dQ). Stages 1 and 2
- * read D, so stage 0 must complete first; lets a caller time or interleave
+ * read the workspace, so stage 0 must complete first; lets a caller time or interleave
  * the stages. Unknown stage: RA_ERR_SHAPE. */
 ra_status ra_backward_stage(int32_t stage, const ra_problem* pb, int32_t rank_begin,
                             int32_t rank_end, const ra_seq* q, const ra_seq* k, const ra_seq* v,

@@ -74,7 +74,7 @@ def test_workspace_sizes():
     expect_fwd = 4 * blk + rows * 128 * 4 + rows * 4  # all multiples of 256 here
     assert ra.workspace_bytes(pb, 7, 8, True, False) == expect_fwd
     rows8 = 8 * rows
-    assert ra.workspace_bytes(pb, 0, 8, False, True) == rows8 * 4  # D = rowsum(dO * O)
+    assert ra.workspace_bytes(pb, 0, 8, False, True) == rows8 * 8  # D = rowsum(dO * O) and lse * log2(e)
     assert ra.workspace_bytes(problem(d=96), 0, 4, False, True) == 0  # invalid problem
 
 
@@ -96,7 +96,7 @@ def test_grouped_query_heads():
     blk_kv = 1 * 4096 * 8 * 128 * 2
     rows = 1 * 32 * 4096
     assert ra.workspace_bytes(pb, 7, 8, True, False) == 4 * blk_kv + rows * 128 * 4 + rows * 4
-    assert ra.workspace_bytes(pb, 0, 8, False, True) == 8 * rows * 4  # D has one row per query head
+    assert ra.workspace_bytes(pb, 0, 8, False, True) == 8 * rows * 8  # D and lse2: one row per query head
     assert ra.workspace_bytes(problem(H=32, kv_heads=1), 0, 4, False, True) > 0  # multi-query
     assert ra.workspace_bytes(problem(H=32, kv_heads=12), 0, 4, False, True) == 0
     assert ra.workspace_bytes(problem(H=4, kv_heads=8), 0, 4, False, True) == 0
