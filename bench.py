@@ -86,6 +86,32 @@ def pair_count(layout, causal, P, Bb, ranks):
     return total
 
 
+def key_extent(layout, causal, i, j, Bb, a):
+    """Keys 0 .. e-1 of block j that local row a of block i sees (the same
+    relations as pair_count)."""
+    if not causal:
+        return Bb
+    if layout == "striped":
+        return max(0, min(Bb, a + 1 - (1 if j > i else 0)))
+    if layout == "zigzag":
+        h = Bb // 2
+        return a + 1 if j == i else (h if j < i else (Bb if a >= h else 0))
+    return Bb if j < i else (a + 1 if j == i else 0)
+
+
+def rank_work(layout, causal, P, Bb, i, rows_per_wg=256, keys_per_tile=64):
+    """Per head: the KV tiles the forward executes for rank i (each
+    256-row query tile walks, in each block, the tiles up to the last key its
+    last row sees) and the KV blocks it visits (blocks with a visible key)."""
+    tiles = 0
+    for a0 in range(0, Bb, rows_per_wg):
+        a_hi = min(a0 + rows_per_wg, Bb) - 1
+        for j in range(P):
+            tiles += -(-key_extent(layout, causal, i, j, Bb, a_hi) // keys_per_tile)
+    blocks = sum(1 for j in range(P) if key_extent(layout, causal, i, j, Bb, Bb - 1) > 0)
+    return tiles, blocks
+
+
 def source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -187,6 +213,32 @@ def receive_overlap(torch, ra, w, t, pb, rb, re_, so, sk, o, lse, sh, stream, to
     return {"c_ms": round(c, 4), "m_ms": round(m, 4), "m_GB/s": round(step_bytes / m / 1e6, 1),
             "overlapped_ms": round(total_ms, 4), "serial_bound_ms": round(P * (c + m), 4),
             "overlap_efficiency": round(P * max(c, m) / total_ms, 4)}
+
+
+def balance_report(torch, ra, w, layout, t, pb, blocked, o, lse, sh, stream):
+    """Each rank's forward launched alone (its query block against the whole
+    ring): kernel time, exact unmasked pairs, executed KV tiles and KV blocks
+    visited, and the max/min ratios. Every device of a ring waits for the
+    slowest one at each step, so the largest rank sets the pace."""
+    P, Bb = w.ring_size, w.block_len
+    per = []
+    for r in range(P):
+        if blocked:
+            q_s, o_s = ra.seq_blocked(t["q"], block_offset=r), ra.seq_blocked(o, block_offset=r)
+            k_s, v_s = ra.seq_blocked(t["k"]), ra.seq_blocked(t["v"])
+        else:
+            q_s, o_s = (ra.seq_original(x, P, layout, block_offset=r) for x in (t["q"], o))
+            k_s, v_s = (ra.seq_original(x, P, layout) for x in (t["k"], t["v"]))
+        ms = time_calls(torch, stream, lambda: ra.forward_raw(pb, r, r + 1, q_s, k_s, v_s, o_s, lse[r].data_ptr(),
+                                                             None, 0, sh, None), n=3)
+        tiles, blocks = rank_work(layout, w.causal, P, Bb, r)
+        bh = w.batch * w.heads
+        per.append({"rank": r, "ms": round(ms, 4), "pairs": pair_count(layout, w.causal, P, Bb, [r]) * bh,
+                    "kv_tiles": tiles * bh, "kv_blocks_visited": blocks})
+    ratio = lambda key: round(max(x[key] for x in per) / max(1e-12, min(x[key] for x in per)), 4)  # noqa: E731
+    return {"per_rank": per, "ms_max_over_min": ratio("ms"), "pairs_max_over_min": ratio("pairs"),
+            "kv_tiles_max_over_min": ratio("kv_tiles"),
+            "slowest_rank_ms_over_mean": round(max(x["ms"] for x in per) / (sum(x["ms"] for x in per) / P), 4)}
 
 
 def cpu_baseline(w):
@@ -384,6 +436,8 @@ def main():
         pre_bytes = len(ranks) * B_ * H_ * Bb * (2 * d_ * t["q"].element_size() + 4)
         details["memory_rows"] = {"B1_rowsum_dO_O": hbm_row(details["bwd_pre_ms"], pre_bytes),
                                   **memory_rows(torch, ra, w, t["q"], sh, stream)}
+    if w.wid == 3:
+        details["balance"] = balance_report(torch, ra, w, layout, t, pb, blocked, o, lse, sh, stream)
     if w.prefetch:
         details["receive_overlap"] = receive_overlap(torch, ra, w, t, pb, rb, re_, so, sk, o, lse, sh, stream, ms)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
