@@ -14,6 +14,9 @@ Modules:
   ring      -- ring schedule, token layouts (contiguous / striped / zigzag), block
                classification, per-device work counts and the pages' tick
                simulation.
+  bpt       -- a Blockwise Parallel Transformer layer: per query block,
+               attention, output projection, residual + layer norm,
+               feedforward network, residual + layer norm.
 
 Every function here is pinned by a CPU test (brute force, closed forms,
 library routines, the invariants the pages state, or values the pages print).
@@ -36,3 +39,4 @@ from .ring import (  # noqa: F401
     block_visit_work,
     ring_timeline,
 )
+from . import bpt  # noqa: F401,E402
