@@ -28,7 +28,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_blockwise_attention_amd/csrc/" + f for f in
-                  ("ra_fwd.hip", "ra_bwd.hip", "ra_dq.hip", "ra_misc.hip", "ra_api.cpp", "ra_schedule.h", "ra_internal.h", "ra_lds.h", "ra_kvwalk.h")]
+                  ("ra_fwd.hip", "ra_bwd.hip", "ra_dq.hip", "ra_misc.hip", "ra_gemm.hip", "ra_api.cpp", "ra_schedule.h",
+                   "ra_internal.h", "ra_lds.h", "ra_kvwalk.h")]
 
 
 def parse():
@@ -36,7 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7],
+                    help="7: the Blockwise Parallel Transformer layer tail (W_o, LN, FFN, LN) at d_model 4096")
     ap.add_argument("--layout", default=None, help="workloads 3, 5 and 6: contiguous, striped or zigzag")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -287,6 +289,83 @@ def cpu_baseline(w):
             "sample": sample, "seconds": round(dt, 3)}
 
 
+def bench_bpt(args):
+    """The BPT layer after attention over a 32768-row sequence, 4096 rows at
+    a time: algorithmic flops 2 d^2 (W_o) + 4 d d_ff (FFN) per row; the
+    products' kernel against the bf16 MFMA peak, layer norm against HBM."""
+    import numpy as np
+    import torch
+
+    import exact_blockwise_attention_amd as ra
+    from exact_blockwise_attention_amd import synthetic as syn
+    w = syn.BPT_WORKLOAD
+    rows, dm, dff, br = w["rows"], w["d_model"], w["d_ff"], w["block_rows"]
+
+    def dev(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
+        return torch.from_numpy(x).to("cuda")
+
+    attn = dev(syn.make_payload(w["wid"], "attn", (rows, dm), "bf16"))
+    x = dev(syn.make_payload(w["wid"], "x", (rows, dm), "bf16"))
+    prm = {k: dev(v) for k, v in syn.bpt_params(w["wid"], dm, dff).items()}
+    out = torch.empty_like(x)
+    pb = ra.BptProblem(rows, dm, dff, br, 0.0)
+    wts = ra.BptWeights(*(prm[n].data_ptr() for n in ra.BPT_WEIGHT_NAMES))
+    need = ra.bpt_workspace_bytes(pb)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    sh = ra._stream_handle(stream)
+    torch.cuda.synchronize()
+    call = lambda: ra.bpt_ffn_raw(pb, attn.data_ptr(), x.data_ptr(), wts, out.data_ptr(), ws.data_ptr(), need, sh)  # noqa: E731
+    for _ in range(args.warmup):
+        call()
+    ms = time_calls(torch, stream, call, n=args.steps)
+    flops = rows * (2 * dm * dm + 4 * dm * dff)
+    value = flops / ms / 1e9
+    # each product shape of one block, and one layer norm, timed alone
+    a_blk = torch.empty((br, dff), dtype=torch.bfloat16, device="cuda").normal_()
+    o32 = torch.empty((br, max(dm, dff)), dtype=torch.float32, device="cuda")
+    shapes = {"W_o": (dm, dm, prm["w_o"], prm["b_o"]), "W_1": (dff, dm, prm["w_1"], prm["b_1"]),
+              "W_2": (dm, dff, prm["w_2"], prm["b_2"])}
+    gem = {}
+    for name, (n, k, wt, bias) in shapes.items():
+        gms = time_calls(torch, stream, lambda: ra.linear_raw(br, n, k, a_blk.data_ptr(), a_blk.stride(0),
+                                                             wt.data_ptr(), k, bias.data_ptr(), None, 0, 0,
+                                                             o32.data_ptr(), o32.stride(0), 1, sh), n=5)
+        gem[name] = {"m": br, "n": n, "k": k, "ms": round(gms, 4), "tflops": round(2 * br * n * k / gms / 1e9, 2)}
+    z = torch.empty((br, dm), dtype=torch.float32, device="cuda").normal_()
+    lms = time_calls(torch, stream, lambda: ra.layer_norm_raw(br, dm, z.data_ptr(), prm["ln1_g"].data_ptr(),
+                                                             prm["ln1_b"].data_ptr(), 0.0, out.data_ptr(), sh), n=5)
+    ln = hbm_row(lms, br * dm * (4 + 2) + 2 * dm * 4)
+    dom = max(gem.values(), key=lambda g: g["ms"])
+    peak = PEAK_BF16_TFLOPS
+    roof = {"bound": "mfma", "kernel": "gemm_bf16_kernel", "achieved": dom["tflops"], "peak": peak,
+            "unit": "TFLOP/s", "frac": round(dom["tflops"] / peak, 4), "traffic": read_traffic("gemm_bf16_kernel"),
+            "launch_ms": dom["ms"], "shape": [dom["m"], dom["n"], dom["k"]]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle.bpt as ob
+        sel = np.arange(16384)  # the first 16384 rows of the tail (rows are independent); about 10 s
+        p64 = {k: syn.to_f64(v) for k, v in syn.bpt_params(w["wid"], dm, dff).items()}
+        a64 = syn.to_f64(syn.make_payload(w["wid"], "attn", (rows, dm), "bf16")[sel])
+        x64 = syn.to_f64(syn.make_payload(w["wid"], "x", (rows, dm), "bf16")[sel])
+        t0 = time.perf_counter()
+        ob.ffn_block(a64, x64, p64)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(len(sel) * (2 * dm * dm + 4 * dm * dff) / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": int(os.cpu_count() or 1), "kind": "oracle", "sample": f"{len(sel)} rows of the tail",
+               "seconds": round(dt, 3)}
+    print(json.dumps({
+        "metric": f"BPT layer tail TFLOP/s ({w['name']})", "value": round(value, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w["name"], "rows": rows, "d_model": dm, "d_ff": dff, "block_rows": br},
+        "frac_of_peak": round(value / peak, 4), "roofline": roof, "cpu_baseline": cpu,
+        "details": {"products": gem, "layer_norm": ln, "workspace_bytes": need},
+        "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -302,6 +381,9 @@ def main():
     ra.library()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.workload == 7:
+        bench_bpt(args)
         return
     w = syn.WORKLOADS[args.workload]
     layout = args.layout or w.layouts[-1]

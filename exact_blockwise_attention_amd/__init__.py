@@ -7,12 +7,13 @@ used only to hold device memory and to name streams. There is no CPU
 fallback: if the library is missing or fails to load, every call raises.
 
 Low level:  Problem, Seq, forward_raw, backward_raw, merge_lse_raw,
-            layout_copy_raw, workspace_bytes (same names and meaning as the
-            C functions).
+            layout_copy_raw, workspace_bytes, linear_raw, layer_norm_raw,
+            bpt_ffn_raw (same names and meaning as the C functions).
 High level: attention_forward / attention_backward take original-order
             [B, L, H, d] torch tensors (K and V may have fewer heads than Q:
             grouped-query attention) and allocate outputs/workspaces with
-            torch.
+            torch; linear, layer_norm, bpt_ffn and bpt_layer cover the
+            Blockwise Parallel Transformer layer around attention.
 """
 from __future__ import annotations
 
@@ -25,6 +26,8 @@ __all__ = [
     "library", "library_path", "workspace_bytes", "forward_raw", "backward_raw", "merge_lse_raw",
     "layout_copy_raw", "status_string", "abi_version", "seq_original", "seq_blocked", "LAYOUTS",
     "attention_forward", "attention_backward", "merge_lse", "layout_copy", "EXPORTED_FUNCTIONS",
+    "BptProblem", "BptWeights", "linear_raw", "layer_norm_raw", "bpt_ffn_raw", "bpt_workspace_bytes",
+    "linear", "layer_norm", "bpt_ffn", "bpt_layer", "BPT_WEIGHT_NAMES",
 ]
 
 LAYOUT_CONTIGUOUS = 0
@@ -39,7 +42,7 @@ library_path = os.path.join(_HERE, "libra.so")
 
 EXPORTED_FUNCTIONS = (
     "ra_workspace_bytes", "ra_forward", "ra_backward", "ra_backward_stage", "ra_merge_lse", "ra_layout_copy",
-    "ra_status_string", "ra_abi_version",
+    "ra_linear", "ra_layer_norm", "ra_bpt_workspace_bytes", "ra_bpt_ffn", "ra_status_string", "ra_abi_version",
 )
 
 
@@ -63,6 +66,18 @@ class Seq(ctypes.Structure):
         ("ptr", ctypes.c_void_p), ("s_blk", ctypes.c_int64), ("s_batch", ctypes.c_int64),
         ("s_tok", ctypes.c_int64), ("s_head", ctypes.c_int64),
     ]
+
+
+class BptProblem(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("block_rows", ctypes.c_int64), ("ln_eps", ctypes.c_float)]
+
+
+BPT_WEIGHT_NAMES = ("w_o", "b_o", "ln1_g", "ln1_b", "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
+
+
+class BptWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in BPT_WEIGHT_NAMES]
 
 
 _lib = None
@@ -92,6 +107,15 @@ def library():
     lib.ra_merge_lse.restype = i32
     lib.ra_layout_copy.argtypes = [P, vp, vp, i32, vp]
     lib.ra_layout_copy.restype = i32
+    lib.ra_linear.argtypes = [i64, i32, i32, vp, i64, vp, i64, vp, vp, i64, i32, vp, i64, i32, vp]
+    lib.ra_linear.restype = i32
+    lib.ra_layer_norm.argtypes = [i64, i32, vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.ra_layer_norm.restype = i32
+    BP, BW = ctypes.POINTER(BptProblem), ctypes.POINTER(BptWeights)
+    lib.ra_bpt_workspace_bytes.argtypes = [BP]
+    lib.ra_bpt_workspace_bytes.restype = sz
+    lib.ra_bpt_ffn.argtypes = [BP, vp, vp, BW, vp, vp, sz, vp]
+    lib.ra_bpt_ffn.restype = i32
     lib.ra_status_string.argtypes = [i32]
     lib.ra_status_string.restype = ctypes.c_char_p
     lib.ra_abi_version.argtypes = []
@@ -151,6 +175,26 @@ def merge_lse_raw(rows, head_dim, o_a, lse_a, o_b, lse_b, o_out, lse_out, stream
 def layout_copy_raw(pb, src, dst, inverse, stream):
     st = library().ra_layout_copy(ctypes.byref(pb), src, dst, int(bool(inverse)), stream)
     _check("ra_layout_copy", st)
+
+
+def linear_raw(m, n, k, a, lda, w, ldw, bias, residual, ldr, gelu, out, ldo, out_f32, stream):
+    st = library().ra_linear(m, n, k, a, lda, w, ldw, bias, residual, ldr, int(bool(gelu)), out, ldo,
+                             int(bool(out_f32)), stream)
+    _check("ra_linear", st)
+
+
+def layer_norm_raw(rows, d, z, gamma, beta, eps, out, stream):
+    st = library().ra_layer_norm(rows, d, z, gamma, beta, float(eps), out, stream)
+    _check("ra_layer_norm", st)
+
+
+def bpt_workspace_bytes(pb: BptProblem) -> int:
+    return int(library().ra_bpt_workspace_bytes(ctypes.byref(pb)))
+
+
+def bpt_ffn_raw(pb, attn, x, wts, out, ws_ptr, ws_bytes, stream):
+    st = library().ra_bpt_ffn(ctypes.byref(pb), attn, x, ctypes.byref(wts), out, ws_ptr, ws_bytes, stream)
+    _check("ra_bpt_ffn", st)
 
 
 # ---------------------------------------------------------------- torch helpers
@@ -346,3 +390,67 @@ def layout_copy(x, ring_size: int, layout: str, inverse: bool = False):
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# ---------------------------------------------------------------- the BPT layer
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def linear(x, w, bias=None, residual=None, gelu=False, out_f32=False, out=None):
+    """x [m, k] bf16, w [n, k] bf16 (a linear layer's [out, in] weight) ->
+    x w^T (+ bias) (+ residual) (then GELU), [m, n] fp32 or bf16."""
+    torch = _torch()
+    m, k = x.shape
+    n = w.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32 if out_f32 else torch.bfloat16, device=x.device)
+    linear_raw(m, n, k, x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), _ptr(bias), _ptr(residual),
+               residual.stride(0) if residual is not None else 0, gelu, out.data_ptr(), out.stride(0), out_f32,
+               _stream_handle(None))
+    return out
+
+
+def layer_norm(z, gamma, beta, eps=1e-5, out=None):
+    """z [rows, d] fp32 -> bf16 layer norm over d."""
+    torch = _torch()
+    rows, d = z.shape
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=z.device)
+    layer_norm_raw(rows, d, z.data_ptr(), gamma.data_ptr(), beta.data_ptr(), eps, out.data_ptr(),
+                   _stream_handle(None))
+    return out
+
+
+def bpt_ffn(attn, x, weights, block_rows, eps=1e-5, out=None, workspace=None):
+    """The BPT layer after attention for rows [rows, d_model] (bf16): output
+    projection, residual + LN1, feedforward network, residual + LN2, one
+    block of ``block_rows`` rows at a time. ``weights``: dict of
+    BPT_WEIGHT_NAMES tensors (weights bf16 [out, in], the rest fp32)."""
+    torch = _torch()
+    rows, dm = x.shape
+    pb = BptProblem(rows, dm, weights["w_1"].shape[0], block_rows, eps)
+    wts = BptWeights(*(weights[n].data_ptr() for n in BPT_WEIGHT_NAMES))
+    need = bpt_workspace_bytes(pb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty_like(x)
+    bpt_ffn_raw(pb, attn.data_ptr(), x.data_ptr(), wts, out.data_ptr(), workspace.data_ptr(), need,
+                _stream_handle(None))
+    return out
+
+
+def bpt_layer(x, weights, n_heads, ring_size, block_rows, causal=False, layout="contiguous"):
+    """The whole layer on x [B, L, d_model] (bf16) with library calls only:
+    Q, K, V projections (ra_linear), ring attention over ``ring_size``
+    blocks (ra_forward), then bpt_ffn. ``weights`` also holds w_q, b_q,
+    w_k, b_k, w_v, b_v."""
+    B, L, dm = x.shape
+    x2 = x.reshape(B * L, dm)
+    q, k, v = (linear(x2, weights[f"w_{n}"], weights[f"b_{n}"]).reshape(B, L, n_heads, dm // n_heads)
+               for n in "qkv")
+    attn, _ = attention_forward(q, k, v, ring_size, layout, causal)
+    return bpt_ffn(attn.reshape(B * L, dm), x2, weights, block_rows).reshape(B, L, dm)
+

@@ -105,6 +105,26 @@ BwdWs bwd_ws_layout(const ra_problem* pb, int32_t n_ranks) {
   return w;
 }
 
+struct BptWs {
+  size_t y, h, u, total;  // y (then z): fp32 [br][dm]; h: bf16 [br][dm]; u: bf16 [br][dff]
+};
+
+bool bpt_problem_ok(const ra_bpt_problem* pb) {
+  return pb && pb->rows >= 1 && pb->d_model >= 128 && pb->d_model % 128 == 0 && pb->d_model <= 8192 &&
+         pb->d_ff >= 128 && pb->d_ff % 128 == 0 && pb->block_rows >= 1 && pb->block_rows <= (int64_t)1 << 24 &&
+         pb->ln_eps == pb->ln_eps && !isinf(pb->ln_eps);
+}
+
+BptWs bpt_ws_layout(const ra_bpt_problem* pb) {
+  BptWs w{};
+  const size_t br = (size_t)(pb->block_rows < pb->rows ? pb->block_rows : pb->rows);
+  w.y = 0;
+  w.h = align_up(br * pb->d_model * sizeof(float));
+  w.u = w.h + align_up(br * pb->d_model * 2);
+  w.total = w.u + align_up(br * (size_t)pb->d_ff * 2);
+  return w;
+}
+
 #define RA_HIP(call)                         \
   do {                                       \
     if ((call) != hipSuccess) {              \
@@ -337,6 +357,110 @@ ra_status ra_layout_copy(const ra_problem* pb, const void* src, void* dst, int32
   RA_HIP(ra::launch_layout_copy(src, dst, pb->batch, pb->heads, pb->head_dim, pb->ring_size,
                                 pb->block_len, pb->layout, inverse ? 1 : 0, elem_bytes(pb->dtype),
                                 stream));
+  return RA_OK;
+}
+
+ra_status ra_linear(int64_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* w,
+                    int64_t ldw, const float* bias, const void* residual, int64_t ldr, int32_t gelu,
+                    void* out, int64_t ldo, int32_t out_f32, hipStream_t stream) {
+  if (!a || !w || !out) return RA_ERR_NULL;
+  if (m < 1 || n < 128 || n % 128 || k < 64 || k % 64) return RA_ERR_SHAPE;
+  if (lda < k || ldw < k || ldo < n || (residual && ldr < n)) return RA_ERR_SHAPE;
+  if ((m + 255) / 256 * (n / 128) > (int64_t)INT32_MAX) return RA_ERR_SHAPE;
+  const void* ptrs[4] = {a, w, out, residual};
+  for (const void* ptr : ptrs)
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return RA_ERR_ALIGN;
+  if (lda % 8 || ldw % 8 || (residual && ldr % 8) || ldo % 8) return RA_ERR_ALIGN;
+  if (bias && reinterpret_cast<uintptr_t>(bias) % 4) return RA_ERR_ALIGN;
+  ra::GemmParams p{};
+  p.a = reinterpret_cast<const __bf16*>(a);
+  p.lda = lda;
+  p.w = reinterpret_cast<const __bf16*>(w);
+  p.ldw = ldw;
+  p.bias = bias;
+  p.res = reinterpret_cast<const __bf16*>(residual);
+  p.ldr = ldr;
+  p.out = out;
+  p.ldo = ldo;
+  p.M = m;
+  p.N = n;
+  p.K = k;
+  p.gelu = gelu ? 1 : 0;
+  p.out_f32 = out_f32 ? 1 : 0;
+  RA_HIP(ra::launch_gemm_bf16(p, stream));
+  return RA_OK;
+}
+
+ra_status ra_layer_norm(int64_t rows, int32_t d, const float* z, const float* gamma, const float* beta,
+                        float eps, void* out, hipStream_t stream) {
+  if (!z || !gamma || !beta || !out) return RA_ERR_NULL;
+  if (rows < 0 || rows > (int64_t)INT32_MAX || d < 1 || d > 8192) return RA_ERR_SHAPE;
+  if (!(eps == eps) || isinf(eps)) return RA_ERR_SHAPE;
+  const void* ptrs[4] = {z, gamma, beta, out};
+  for (const void* ptr : ptrs)
+    if (reinterpret_cast<uintptr_t>(ptr) % 4) return RA_ERR_ALIGN;
+  RA_HIP(ra::launch_layer_norm(z, rows, d, gamma, beta, eps > 0.0f ? eps : 1e-5f,
+                               reinterpret_cast<__bf16*>(out), stream));
+  return RA_OK;
+}
+
+size_t ra_bpt_workspace_bytes(const ra_bpt_problem* pb) {
+  if (!bpt_problem_ok(pb)) return 0;
+  return bpt_ws_layout(pb).total;
+}
+
+ra_status ra_bpt_ffn(const ra_bpt_problem* pb, const void* attn, const void* x, const ra_bpt_weights* wts,
+                     void* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!pb || !attn || !x || !wts || !out) return RA_ERR_NULL;
+  if (!bpt_problem_ok(pb)) return RA_ERR_SHAPE;
+  const void* wptrs[10] = {wts->w_o, wts->b_o, wts->ln1_g, wts->ln1_b, wts->w_1,
+                           wts->b_1, wts->w_2, wts->b_2, wts->ln2_g, wts->ln2_b};
+  for (const void* ptr : wptrs)
+    if (!ptr) return RA_ERR_NULL;
+  const void* big[6] = {attn, x, out, wts->w_o, wts->w_1, wts->w_2};
+  for (const void* ptr : big)
+    if (reinterpret_cast<uintptr_t>(ptr) % 16) return RA_ERR_ALIGN;
+  for (int i : {1, 2, 3, 5, 7, 8, 9})
+    if (reinterpret_cast<uintptr_t>(wptrs[i]) % 4) return RA_ERR_ALIGN;
+  const BptWs w = bpt_ws_layout(pb);
+  if (!workspace || workspace_bytes < w.total) return RA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return RA_ERR_ALIGN;
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* yz = reinterpret_cast<float*>(ws + w.y);
+  __bf16* h = reinterpret_cast<__bf16*>(ws + w.h);
+  __bf16* u = reinterpret_cast<__bf16*>(ws + w.u);
+  const int64_t dm = pb->d_model, dff = pb->d_ff;
+  const float eps = pb->ln_eps > 0.0f ? pb->ln_eps : 1e-5f;
+  auto gemm = [&](int64_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* wt, const float* bias,
+                  const void* res, int64_t ldr, int32_t gelu, void* o, int64_t ldo, int32_t f32) {
+    ra::GemmParams p{};
+    p.a = reinterpret_cast<const __bf16*>(a);
+    p.lda = lda;
+    p.w = reinterpret_cast<const __bf16*>(wt);
+    p.ldw = k;
+    p.bias = bias;
+    p.res = reinterpret_cast<const __bf16*>(res);
+    p.ldr = ldr;
+    p.out = o;
+    p.ldo = ldo;
+    p.M = m;
+    p.N = n;
+    p.K = k;
+    p.gelu = gelu;
+    p.out_f32 = f32;
+    return ra::launch_gemm_bf16(p, stream);
+  };
+  for (int64_t r0 = 0; r0 < pb->rows; r0 += pb->block_rows) {
+    const int64_t br = (pb->rows - r0 < pb->block_rows) ? pb->rows - r0 : pb->block_rows;
+    const __bf16* ab = reinterpret_cast<const __bf16*>(attn) + r0 * dm;
+    const __bf16* xb = reinterpret_cast<const __bf16*>(x) + r0 * dm;
+    __bf16* ob = reinterpret_cast<__bf16*>(out) + r0 * dm;
+    RA_HIP(gemm(br, (int32_t)dm, (int32_t)dm, ab, dm, wts->w_o, wts->b_o, xb, dm, 0, yz, dm, 1));
+    RA_HIP(ra::launch_layer_norm(yz, br, (int32_t)dm, wts->ln1_g, wts->ln1_b, eps, h, stream));
+    RA_HIP(gemm(br, (int32_t)dff, (int32_t)dm, h, dm, wts->w_1, wts->b_1, nullptr, 0, 1, u, dff, 0));
+    RA_HIP(gemm(br, (int32_t)dm, (int32_t)dff, u, dff, wts->w_2, wts->b_2, h, dm, 0, yz, dm, 1));
+    RA_HIP(ra::launch_layer_norm(yz, br, (int32_t)dm, wts->ln2_g, wts->ln2_b, eps, ob, stream));
+  }
   return RA_OK;
 }
 

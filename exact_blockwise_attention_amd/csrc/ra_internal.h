@@ -47,6 +47,26 @@ struct BwdParams {
   int32_t rank_begin, n_ranks;
 };
 
+// Dense product with fused epilogue: out[m][n] = sum_k a[m][k] w[n][k]
+// (+ bias[n]) (+ res[m][n]) (then GELU), fp32 or bf16 out.
+struct GemmParams {
+  const __bf16* a;
+  int64_t lda;
+  const __bf16* w;
+  int64_t ldw;
+  const float* bias;  // [N] or null
+  const __bf16* res;  // [M][ldr] or null
+  int64_t ldr;
+  void* out;
+  int64_t ldo;
+  int64_t M;
+  int32_t N, K;
+  int32_t gelu, out_f32;
+};
+
+hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s);
+hipError_t launch_layer_norm(const float* in, int64_t rows, int32_t d, const float* gamma, const float* beta,
+                             float eps, __bf16* out, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int32_t bf16, hipStream_t s);

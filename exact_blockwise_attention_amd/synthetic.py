@@ -12,6 +12,12 @@ layout, is cut into chunks of 2**22 elements; chunk c is drawn with
 ``numpy.random.Generator(PCG64(SeedSequence([workload_id, tensor_id, c])))``
 with tensor ids Q=0, K=1, V=2, dO=3. Chunks are independent, so they are drawn
 (and rounded) on several host threads.
+
+The Blockwise Parallel Transformer layer adds its input x, an attention
+output, and its parameters (ids from 10 on). Weights [out, in] are the N(0, 1)
+draws scaled by 1/sqrt(in) and rounded to bfloat16, biases 0.02 N(0, 1), layer
+norm gains 1 + 0.1 N(0, 1) and offsets 0.1 N(0, 1), all fp32 apart from the
+weights: a scale that keeps activations of order one through the layer.
 """
 from __future__ import annotations
 
@@ -23,7 +29,9 @@ import numpy as np
 
 CHUNK = 1 << 22
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "x": 10, "attn": 11,
+              "w_q": 12, "b_q": 13, "w_k": 14, "b_k": 15, "w_v": 16, "b_v": 17, "w_o": 18, "b_o": 19,
+              "ln1_g": 20, "ln1_b": 21, "w_1": 22, "b_1": 23, "w_2": 24, "b_2": 25, "ln2_g": 26, "ln2_b": 27}
 
 
 @dataclass(frozen=True)
@@ -180,3 +188,28 @@ def workload_shape(w: Workload, tensor: str = "q"):
     """[B, L, heads, d] of an input: K and V have the workload's K/V heads."""
     heads = (w.kv_heads or w.heads) if tensor in ("k", "v") else w.heads
     return (w.batch, w.seq_len, heads, w.head_dim)
+
+
+def bpt_params(workload_id: int, d_model: int, d_ff: int) -> dict:
+    """Parameters of a BPT layer: weights as bfloat16 bit patterns [out, in],
+    the rest float32 (see the module docstring for the scales)."""
+    shapes = {"q": (d_model, d_model), "k": (d_model, d_model), "v": (d_model, d_model),
+              "o": (d_model, d_model), "1": (d_ff, d_model), "2": (d_model, d_ff)}
+    p = {}
+    for n, (o, i) in shapes.items():
+        w = normal_f32(workload_id, f"w_{n}", (o, i)) * np.float32(1.0 / np.sqrt(i))
+        p[f"w_{n}"] = f32_to_bf16_bits(w)
+        p[f"b_{n}"] = normal_f32(workload_id, f"b_{n}", (o,)) * np.float32(0.02)
+    for n in ("ln1", "ln2"):
+        p[f"{n}_g"] = np.float32(1.0) + normal_f32(workload_id, f"{n}_g", (d_model,)) * np.float32(0.1)
+        p[f"{n}_b"] = normal_f32(workload_id, f"{n}_b", (d_model,)) * np.float32(0.1)
+    return p
+
+
+
+# The Blockwise Parallel Transformer layer tail at the pages' 7B layer shape
+# (hidden 4096 = 32 heads of 128, feedforward 4 x 4096), over a 32768-token
+# sequence finished 4096 rows (one ring block of the forward+backward
+# workload) at a time.
+BPT_WORKLOAD = {"wid": 7, "name": "bpt_ffn_bf16_rows32768_d4096_ff16384_block4096", "rows": 32768,
+                "d_model": 4096, "d_ff": 16384, "block_rows": 4096, "n_heads": 32}

@@ -205,6 +205,67 @@ ra_status ra_merge_lse(int64_t rows, int32_t head_dim, const float* o_a, const f
 ra_status ra_layout_copy(const ra_problem* pb, const void* src, void* dst, int32_t inverse,
                          hipStream_t stream);
 
+/* ---- The Blockwise Parallel Transformer layer around attention ("Ring
+ * Attention 論文分析" (blog), section "BPT の Feedforward 融合": each query
+ * block goes through attention, the output projection, residual + layer
+ * norm, the feedforward network and residual + layer norm before the next
+ * block starts, so intermediate results never exist for the whole sequence).
+ * The Q/K/V projections are ra_linear calls and attention is ra_forward. */
+
+/* A linear layer with fused epilogue: out[r][c] = sum_i a[r][i] w[c][i],
+ * then + bias[c] (fp32, or NULL), then + residual[r][c] (bf16, row stride
+ * ldr, or NULL), then the exact GELU 0.5 v (1 + erf(v / sqrt 2)) if gelu != 0.
+ * a: bf16 [m][k] (row stride lda); w: bf16 [n][k] (row stride ldw), the
+ * [out][in] weight of the layer; out: fp32 if out_f32 != 0 else bf16 (round
+ * to nearest even), row stride ldo. fp32 accumulation. Requires m >= 1,
+ * n % 128 == 0, k % 64 == 0, 16-byte aligned pointers and row strides
+ * (RA_ERR_SHAPE / RA_ERR_ALIGN otherwise). */
+ra_status ra_linear(int64_t m, int32_t n, int32_t k, const void* a, int64_t lda, const void* w,
+                    int64_t ldw, const float* bias, const void* residual, int64_t ldr, int32_t gelu,
+                    void* out, int64_t ldo, int32_t out_f32, hipStream_t stream);
+
+/* Row layer normalisation: out[r] = (z[r] - mean) / sqrt(var + eps) * gamma
+ * + beta, mean and biased variance over the d entries of the row. z: fp32
+ * [rows][d]; gamma, beta: fp32 [d]; out: bf16 [rows][d]. eps <= 0 selects
+ * 1e-5. d in 1..8192. */
+ra_status ra_layer_norm(int64_t rows, int32_t d, const float* z, const float* gamma, const float* beta,
+                        float eps, void* out, hipStream_t stream);
+
+typedef struct {
+  int64_t rows;       /* rows of the sequence (all blocks) */
+  int32_t d_model;    /* multiple of 128, at most 8192 */
+  int32_t d_ff;       /* multiple of 128 */
+  int64_t block_rows; /* rows finished at a time; the workspace holds one block */
+  float ln_eps;       /* <= 0: 1e-5 */
+} ra_bpt_problem;
+
+/* Weights in bf16 as [out][in], biases and normalisation gains/offsets in fp32. */
+typedef struct {
+  const void* w_o;    /* [d_model][d_model] */
+  const float* b_o;   /* [d_model] */
+  const float* ln1_g; /* [d_model] */
+  const float* ln1_b;
+  const void* w_1;    /* [d_ff][d_model] */
+  const float* b_1;   /* [d_ff] */
+  const void* w_2;    /* [d_model][d_ff] */
+  const float* b_2;   /* [d_model] */
+  const float* ln2_g;
+  const float* ln2_b;
+} ra_bpt_weights;
+
+/* Workspace of ra_bpt_ffn: block_rows * (6 d_model + 2 d_ff) bytes (rounded
+ * up per buffer); 0 for an invalid problem. */
+size_t ra_bpt_workspace_bytes(const ra_bpt_problem* pb);
+
+/* The layer after attention, block_rows rows at a time:
+ *   y = attn W_o^T + b_o + x        h = LN1(y)
+ *   u = GELU(h W_1^T + b_1)         z = u W_2^T + b_2 + h      out = LN2(z)
+ * attn (the heads side by side), x and out: bf16 [rows][d_model],
+ * contiguous. y and z are fp32; h and u are bf16 (the next product's
+ * operands). */
+ra_status ra_bpt_ffn(const ra_bpt_problem* pb, const void* attn, const void* x, const ra_bpt_weights* wts,
+                     void* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* ra_status_string(int32_t status);
 

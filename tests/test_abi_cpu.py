@@ -196,3 +196,40 @@ def test_merge_and_layout_copy_validation():
     assert lib.ra_layout_copy(ctypes.byref(pb), None, p, 0, None) == 1
     assert lib.ra_layout_copy(ctypes.byref(pb), p + 4, p, 0, None) == 5
     assert lib.ra_layout_copy(None, p, p, 0, None) == 1
+
+
+def test_linear_and_layer_norm_validation():
+    """Argument checks only: every call here fails validation, so nothing is
+    launched."""
+    lib = ra.library()
+    p = 0x10000
+    # n must be a multiple of 128, k of 64; m >= 1
+    assert lib.ra_linear(64, 100, 64, p, 64, p, 64, None, None, 0, 0, p, 128, 1, None) == 2
+    assert lib.ra_linear(64, 128, 96, p, 96, p, 96, None, None, 0, 0, p, 128, 1, None) == 2
+    assert lib.ra_linear(0, 128, 64, p, 64, p, 64, None, None, 0, 0, p, 128, 1, None) == 2
+    assert lib.ra_linear(64, 128, 64, p, 32, p, 64, None, None, 0, 0, p, 128, 1, None) == 2  # lda < k
+    assert lib.ra_linear(64, 128, 64, None, 64, p, 64, None, None, 0, 0, p, 128, 1, None) == 1
+    assert lib.ra_linear(64, 128, 64, p + 2, 64, p, 64, None, None, 0, 0, p, 128, 1, None) == 5
+    assert lib.ra_linear(64, 128, 64, p, 68, p, 64, None, None, 0, 0, p, 128, 1, None) == 5  # row stride
+    assert lib.ra_layer_norm(4, 8193, p, p, p, 0.0, p, None) == 2
+    assert lib.ra_layer_norm(4, 0, p, p, p, 0.0, p, None) == 2
+    assert lib.ra_layer_norm(4, 64, None, p, p, 0.0, p, None) == 1
+    assert lib.ra_layer_norm(4, 64, p, p, p, float("nan"), p, None) == 2
+
+
+def test_bpt_validation_and_workspace():
+    br, dm, dff = 1024, 4096, 16384
+    pb = ra.BptProblem(32768, dm, dff, br, 0.0)
+    assert ra.bpt_workspace_bytes(pb) == br * dm * 4 + br * dm * 2 + br * dff * 2
+    assert ra.bpt_workspace_bytes(ra.BptProblem(100, dm, dff, br, 0.0)) == 100 * (dm * 4 + dm * 2 + dff * 2)
+    for bad in (ra.BptProblem(32768, 4000, dff, br, 0.0), ra.BptProblem(32768, dm, 1000, br, 0.0),
+                ra.BptProblem(0, dm, dff, br, 0.0), ra.BptProblem(32768, 16384, dff, br, 0.0)):
+        assert ra.bpt_workspace_bytes(bad) == 0
+    lib = ra.library()
+    w = ra.BptWeights(*([0x10000] * 10))
+    p = 0x20000
+    assert lib.ra_bpt_ffn(ctypes.byref(pb), p, p, ctypes.byref(w), p, None, 0, None) == 4  # no workspace
+    w0 = ra.BptWeights(*([0x10000] * 9 + [0]))
+    assert lib.ra_bpt_ffn(ctypes.byref(pb), p, p, ctypes.byref(w0), p, p, 1 << 40, None) == 1
+    assert lib.ra_bpt_ffn(ctypes.byref(ra.BptProblem(32768, 4000, dff, br, 0.0)), p, p, ctypes.byref(w), p, p,
+                          1 << 40, None) == 2
