@@ -42,6 +42,18 @@ def _run(cmd):
     return r
 
 
+def _check_launch_stubs(lib):
+    """Fail the build when a kernel's host launch stub is undefined in the
+    library: hipcc drops it without a diagnostic when the host pass cannot
+    instantiate a kernel template, and the library then fails only at load."""
+    r = subprocess.run(["nm", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        return  # no nm: nothing to check with
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if " U " in ln and "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError(f"{lib}: undefined kernel launch stubs: {missing}")
+
+
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     out_dir = os.path.join(HERE, "_build")
@@ -60,6 +72,7 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    _check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -10,10 +10,11 @@
 // bias[n], then residual[m][n] (bf16), then applies the exact GELU, and stores
 // fp32 or bf16 (rounded to nearest even).
 //
-// Tiling: a workgroup owns a 256 x 128 tile of C; its 8 waves each own 64 x 64
-// (2 x 2 MFMA tiles). K advances 64 at a time through three LDS stages (a
-// 256 x 64 A tile and a 128 x 64 W tile each, 48 KB), copied straight from
-// global memory into LDS two steps ahead of their use. LDS rows are 128
+// Tiling: a workgroup owns a 256 x BN tile of C (BN = 256 when N allows,
+// else 128); its 8 waves each own 64 x BN/2 (2 x BN/64 MFMA tiles). K advances
+// 64 at a time through LDS stages of a 256 x 64 A tile and a BN x 64 W tile
+// (two stages of 64 KB for BN = 256, three of 48 KB for BN = 128), copied
+// straight from global memory into LDS ahead of their use. LDS rows are 128
 // bytes; the 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7), so that the
 // 16 lanes of a read phase, on 16 consecutive rows at one chunk, hit all 64
 // banks once.
@@ -28,21 +29,52 @@
 namespace ra {
 namespace {
 
-constexpr int kBM = 256, kBN = 128, kBK = 64;
+constexpr int kBM = 256, kBK = 64;
 constexpr int kGWaves = 8;
 constexpr int kGThreads = 64 * kGWaves;
-constexpr int kNSt = 3;
-constexpr int kATileB = kBM * kBK * 2;             // 32 KB
-constexpr int kWTileB = kBN * kBK * 2;             // 16 KB
-constexpr int kStageB = kATileB + kWTileB;         // 48 KB
-constexpr int kGemmLds = kNSt * kStageB;           // 144 KB
-constexpr int kACopies = kATileB / 1024 / kGWaves;  // 1 KB copies per wave per stage
-constexpr int kWCopies = kWTileB / 1024 / kGWaves;
-constexpr int kGNI = kACopies + kWCopies;
+constexpr int kATileB = kBM * kBK * 2;  // 32 KB
+
+template <int BN>
+struct GemmCfg {
+  static constexpr int NST = BN == 256 ? 2 : 3;
+  static constexpr int WTILE_B = BN * kBK * 2;
+  static constexpr int STAGE_B = kATileB + WTILE_B;
+  static constexpr int LDS = NST * STAGE_B;
+  static constexpr int ACOPIES = kATileB / 1024 / kGWaves;  // 1 KB copies per wave per stage
+  static constexpr int WCOPIES = WTILE_B / 1024 / kGWaves;
+  static constexpr int NI = ACOPIES + WCOPIES;
+  static constexpr int NT = BN / 64;  // MFMA column tiles per wave
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
 
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
+// One K step's copies of this wave into the stage at `stage`: 1 KB (8 rows of
+// 64 elements) per copy, A rows first, then W rows behind the A tile.
+template <int AC, int WC>
+__device__ __forceinline__ void copy_stage(const __bf16* const (&asrc)[AC], const __bf16* const (&wsrc)[WC], int32_t k0,
+                                           unsigned char* stage, int wave) {
+#pragma unroll
+  for (int c = 0; c < AC; ++c)
+    __builtin_amdgcn_global_load_lds(asrc[c] + k0, (__attribute__((address_space(3))) void*)(stage + (wave + kGWaves * c) * 1024),
+                                     16, 0, 0);
+#pragma unroll
+  for (int c = 0; c < WC; ++c)
+    __builtin_amdgcn_global_load_lds(wsrc[c] + k0,
+                                     (__attribute__((address_space(3))) void*)(stage + kATileB + (wave + kGWaves * c) * 1024),
+                                     16, 0, 0);
+}
+
+template <int BN>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_kernel(GemmParams p) {
+  using C = GemmCfg<BN>;
+  constexpr int kBN = BN;
+  constexpr int kNSt = C::NST;
+  constexpr int kStageB = C::STAGE_B;
+  constexpr int kACopies = C::ACOPIES;
+  constexpr int kWCopies = C::WCOPIES;
+  constexpr int kGNI = C::NI;
+  constexpr int NT = C::NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -52,7 +84,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_kernel(GemmParams p) {
 
   // tile order: consecutive workgroups (one XCD) share a row band of A and
   // walk the W column tiles, so a band is read from HBM about once
-  const int32_t ntn = p.N / kBN;
+  const int32_t ntn = (p.N + kBN - 1) / kBN;
   const int64_t ntm = (p.M + kBM - 1) / kBM;
   const int64_t lw = xcd_logical(blockIdx.x, ntm * ntn);
   const int64_t m0 = (lw / ntn) * kBM;
@@ -73,68 +105,72 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
   for (int c = 0; c < kWCopies; ++c) {
     const int row = (wave + kGWaves * c) * 8 + lane / 8;
-    wsrc[c] = p.w + (int64_t)(n0 + row) * p.ldw + 8 * ((lane % 8) ^ gswz(row));
+    int32_t gr = n0 + row;
+    if (gr > p.N - 1) gr = p.N - 1;  // a ragged last column tile reads a valid row
+    wsrc[c] = p.w + (int64_t)gr * p.ldw + 8 * ((lane % 8) ^ gswz(row));
   }
+  // the copy builtin sits in a function: written directly in a lambda of a
+  // kernel template, it makes the host compilation drop the launch stub
   auto copy = [&](int kt, int st) __attribute__((always_inline)) {
-    unsigned char* sa = smem_raw + st * kStageB;
-    unsigned char* sw = sa + kATileB;
-#pragma unroll
-    for (int c = 0; c < kACopies; ++c)
-      __builtin_amdgcn_global_load_lds(asrc[c] + kt * kBK,
-                                       (__attribute__((address_space(3))) void*)(sa + (wave + kGWaves * c) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int c = 0; c < kWCopies; ++c)
-      __builtin_amdgcn_global_load_lds(wsrc[c] + kt * kBK,
-                                       (__attribute__((address_space(3))) void*)(sw + (wave + kGWaves * c) * 1024), 16, 0, 0);
+    copy_stage<kACopies, kWCopies>(asrc, wsrc, kt * kBK, smem_raw + st * kStageB, wave);
   };
 
   // LDS byte addresses of this lane's operand reads in stage 0 for k-step ks:
-  // A row 64wm + n (+32 for the second row tile), W row 64wn + n (+32),
-  // logical chunk 2ks + hf
+  // A row 64wm + n (+32 for the second row tile), W row (BN/2) wn + n (+32j),
+  // logical chunk 2ks + hf (rows 32 apart share the swizzle)
   uint32_t ra_[4], rw_[4];
   const uint32_t base = lds_addr(smem_raw);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const int ar = 64 * wm + n, wr = 64 * wn + n;
+    const int ar = 64 * wm + n, wr = (kBN / 2) * wn + n;
     ra_[ks] = base + ar * 128 + 16 * ((2 * ks + hf) ^ gswz(ar));
     rw_[ks] = base + kATileB + wr * 128 + 16 * ((2 * ks + hf) ^ gswz(wr));
   }
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][NT];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
+  // copies run DIST = NST - 1 steps ahead of the compute
+  constexpr int DIST = kNSt - 1;
   const int32_t nk = p.K / kBK;
-  copy(0, 0);
-  if (nk > 1) copy(1, 1);
+#pragma unroll
+  for (int d = 0; d < DIST; ++d)
+    if (d < nk) copy(d, d);
   for (int32_t kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) wait_vm<kGNI>();  // step kt has landed; kt + 1 may still be in flight
+    // step kt has landed; the copies of steps kt+1 .. kt+DIST-1 may stay in flight
+    if (DIST > 1 && kt + DIST - 1 < nk) wait_vm<(DIST - 1) * kGNI>();
     else wait_vm<0>();
-    wg_barrier();  // every wave's part of step kt is in LDS; stage (kt + 2) % 3 is free
-    if (kt + 2 < nk) copy(kt + 2, (kt + 2) % kNSt);
+    wg_barrier();  // every wave's part of step kt is in LDS; the stage of step kt-1 is free
+    if (kt + DIST < nk) copy(kt + DIST, (kt + DIST) % kNSt);
     const uint32_t so = (uint32_t)((kt % kNSt) * kStageB);
-    u32x4 fr[2][4];  // [slot][A0, A1, W0, W1]
-    auto rd = [&](u32x4(&r)[4], int ks) __attribute__((always_inline)) {
-      r[0] = lds_read16<0>(ra_[ks] + so);
-      r[1] = lds_read16<32 * 128>(ra_[ks] + so);
-      r[2] = lds_read16<0>(rw_[ks] + so);
-      r[3] = lds_read16<32 * 128>(rw_[ks] + so);
+    u32x4 fr[2][2 + NT];  // [slot][A0, A1, W0 .. W(NT-1)]
+    auto rd = [&](u32x4(&r)[2 + NT], int ks) __attribute__((always_inline)) {
+      const uint32_t a = ra_[ks] + so, w = rw_[ks] + so;
+      r[0] = lds_read16<0>(a);
+      r[1] = lds_read16<32 * 128>(a);
+      r[2] = lds_read16<0>(w);
+      r[3] = lds_read16<32 * 128>(w);
+      if constexpr (NT == 4) {
+        r[4] = lds_read16<64 * 128>(w);
+        r[5] = lds_read16<96 * 128>(w);
+      }
     };
     rd(fr[0], 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks + 1 < 4) {
         rd(fr[(ks + 1) & 1], ks + 1);
-        lds_wait<4>(fr[ks & 1]);
+        lds_wait<2 + NT>(fr[ks & 1]);
       } else {
         lds_wait<0>(fr[ks & 1]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NT; ++j)
           acc[i][j] = mfma32(__builtin_bit_cast(bf16x8, fr[ks & 1][i]), __builtin_bit_cast(bf16x8, fr[ks & 1][2 + j]),
                              acc[i][j]);
     }
@@ -143,8 +179,9 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_kernel(GemmParams p) {
   // epilogue: lane (hf, n) of tile (i, j) holds rows 8(e/4) + 4hf + e%4 of
   // column n
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int32_t col = n0 + 64 * wn + 32 * j + n;
+  for (int j = 0; j < NT; ++j) {
+    const int32_t col = n0 + (kBN / 2) * wn + 32 * j + n;
+    if (col >= p.N) continue;
     const float bj = p.bias ? p.bias[col] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -215,11 +252,19 @@ __global__ __launch_bounds__(kLnThreads) void layer_norm_kernel(const float* in,
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmParams& p, hipStream_t s) {
-  const int64_t grid = ((p.M + kBM - 1) / kBM) * (p.N / kBN);
+  const bool wide = p.N % 256 == 0;
+  const int bn = wide ? 256 : 128;
+  const int64_t grid = ((p.M + kBM - 1) / kBM) * ((p.N + bn - 1) / bn);
   if (grid <= 0) return hipSuccess;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kGemmLds);
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3((uint32_t)grid), dim3(kGThreads), kGemmLds, s, p);
+  if (wide) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<256>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, GemmCfg<256>::LDS);
+    hipLaunchKernelGGL(gemm_bf16_kernel<256>, dim3((uint32_t)grid), dim3(kGThreads), GemmCfg<256>::LDS, s, p);
+  } else {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_kernel<128>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, GemmCfg<128>::LDS);
+    hipLaunchKernelGGL(gemm_bf16_kernel<128>, dim3((uint32_t)grid), dim3(kGThreads), GemmCfg<128>::LDS, s, p);
+  }
   return hipGetLastError();
 }
 

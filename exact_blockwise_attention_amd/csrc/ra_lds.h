@@ -148,6 +148,14 @@ __device__ __forceinline__ void lds_wait(u32x4 (&r)[4]) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]) : "n"(N));
 }
 
+template <int N>
+__device__ __forceinline__ void lds_wait(u32x4 (&r)[6]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%6)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5])
+               : "n"(N));
+}
+
 }  // namespace ra
 
 #endif  // RA_LDS_H_
