@@ -185,6 +185,7 @@ def memory_rows(torch, ra, w, q, sh, stream):
     merge_ms = time_calls(torch, stream, lambda: ra.merge_lse_raw(rows, d, oa.data_ptr(), la.data_ptr(), ob.data_ptr(),
                                                                   lb.data_ptr(), oo.data_ptr(), lo.data_ptr(), sh))
     del oa, ob, oo
+    q = q.reshape(w.batch, w.seq_len, w.heads, d)  # blocked (zigzag) copies hold the same bytes
     B, L, H, _ = q.shape
     P = w.ring_size
     blk = torch.empty((P, B, L // P, H, d), dtype=q.dtype, device="cuda")
