@@ -11,19 +11,14 @@
 // chip while the block travels the ring: at step k it meets the query block
 // of rank (j + k) mod P, once for each query head that reads this K/V head
 // (grouped-query attention sums their contributions). Query tiles the
-// causal/striped mask hides from every key of the tile are skipped. The dQ half (ra_dq.hip) walks the ring from
-// the query side, so neither half needs atomics.
+// causal / striped / zigzag mask hides from every key of the tile are
+// skipped. The dQ half (ra_dq.hip) walks the ring from the query side, so
+// neither half needs atomics.
 //
-// bf16 path: 8 waves; wave w owns keys 32(w%4) .. +31 of the tile and query
-// rows 32(w/4) .. +31 of each 64-row query tile (the two waves sharing keys
-// add their dK/dV partials at the end). K and V of the tile and a double
-// buffer of Q/dO tiles sit row-major in swizzled LDS, copied there directly
-// from global memory; the next query tile is copied while the current one is
-// computed. S = Q K^T and
-// dP = dO V^T come out with lane (h, n) holding key n against 16 query rows —
-// the operand layout dV^T += dO^T P and dK^T += Q^T dS need (contraction over
-// query rows, whose order inside an MFMA is free); the dO^T and Q^T operands
-// come from transposing LDS reads.
+// S = Q K^T and dP = dO V^T come out with lane (h, n) holding key n against
+// 16 query rows: the operand layout dV^T += dO^T P and dK^T += Q^T dS need
+// (contraction over query rows, whose order inside an MFMA is free); the
+// dO^T and Q^T operands come from transposing LDS reads.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -36,22 +31,8 @@
 namespace ra {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kKn = 128;  // keys per workgroup (32 per wave, two waves per key group)
-constexpr int kQm = 64;   // query rows per visited tile (32 per wave)
-
-template <int D>
-struct BwdLds {
-  static constexpr int K = 0;                  // [128][D] swizzled
-  static constexpr int V = K + kKn * D;        // [128][D] swizzled
-  static constexpr int Q = V + kKn * D;        // [2 stages][64][D] swizzled
-  static constexpr int DO = Q + 2 * kQm * D;   // [2 stages][64][D] swizzled
-  static constexpr int BF16_ELEMS = DO + 2 * kQm * D;
-  static constexpr int F32_OFF = BF16_ELEMS * 2;       // bytes
-  static constexpr int BYTES = F32_OFF + 4 * kQm * 4;  // lse2[2][64], dsum[2][64]
-  static_assert(4 * ((D / 32) * 16) * 64 * 4 <= F32_OFF, "the dK (then dV) exchange must fit in the tile area");
-};
+constexpr int kKn = 128;  // keys per workgroup (32 per wave)
+constexpr int kQm = 64;   // query rows per visited tile
 
 // Heaviest KV tiles first: early keys are seen by more query rows.
 __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int32_t tiles, int32_t* j,
@@ -65,82 +46,105 @@ __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int3
   }
 }
 
-// The (rank, query head, query tile) triples a KV tile meets: ranks in ring
-// order, and at each rank the G query heads of its K/V head in turn (gi is
-// the head's index within the group).
-struct QTileIter {
-  int32_t kstep, i, gi, qt, qtiles;
-  int32_t j, P, G, rb, re, layout, causal, kv0, Bb;
-  // the first row of rank i's block that sees the tile's first key, which is
-  // the first row that sees any of its keys (Bb if none does)
-  __device__ int32_t first_row() const {
-    return first_row_seeing32(block_relation(layout, causal, i, j, Bb), kv0, Bb);
-  }
-  __device__ bool step_rank() {
-    while (++kstep < P) {
-      i = ring_rank(j, kstep, P);
-      if (i < rb || i >= re) continue;
-      const int32_t a_first = first_row();
-      if (a_first >= Bb) continue;
-      qt = a_first / kQm;
-      gi = 0;
-      return true;
-    }
-    return false;
-  }
-  __device__ bool next() {
-    if (++qt < qtiles) return true;
-    if (++gi < G) {
-      qt = first_row() / kQm;
-      return true;
-    }
-    return step_rank();
-  }
+// ---------------------------------------------------------------- bf16 path
+// 4 waves of 32 keys each, every wave taking all 64 rows
+// of each query tile. A wave holds its K and V rows in registers for the
+// whole walk (the B operands of S = Q K^T and dP = dO V^T), so only Q, dO,
+// lse and D go through LDS, in a ring of four stages copied two tiles ahead.
+// With a single wave per SIMD the matrix and vector work overlap inside the
+// wave: each step computes S, dP, P and dS of its tile while it finishes the
+// tile before it, whose dV^T += dO^T P and dK^T += Q^T dS products are
+// issued between the S / dP products and the exponentials.
+//
+// The copies are bounds-checked buffer loads whose range ends at the last
+// row of the block, so rows past it arrive as zeros (Q = dO = lse = D = 0,
+// hence dS = 0 and a zero dO row: they add nothing). Every step copies
+// exactly one tile (the tile two steps ahead, or the last one again once
+// the walk has no more), and every wave issues the same number of copies per
+// tile (waves 2 and 3 copy a spare lse row), so a fixed count of outstanding
+// copies tells each wave that its current tile has landed.
+constexpr int kWaves = 4;          // waves
+constexpr int kThreads = 64 * kWaves;   // threads
+constexpr int kNst = 4;        // query-tile stages
+constexpr int kRawRsrcWord3 = 0x00020000;  // untyped 32-bit data, bounds-checked raw buffer
+
+template <int D>
+struct BwdLds {
+  static constexpr int QST_B = kQm * D * 2;         // one stage of Q (or dO), bytes
+  static constexpr int Q_B = 0;                     // Q stages
+  static constexpr int DO_B = kNst * QST_B;        // dO stages
+  static constexpr int F32_B = 2 * kNst * QST_B;   // lse2[4][64], then dsum[4][64], then 2 spare rows
+  static constexpr int DS_B = kNst * kQm * 4;      // dsum after lse2
+  static constexpr int SPARE_B = F32_B + 2 * DS_B;  // [2][64] floats, written by waves 2 and 3
+  static constexpr int BYTES = SPARE_B + 2 * kQm * 4;
+  static_assert(BYTES <= 160 * 1024, "LDS");
+  static_assert(32 * D * 2 + 16 * D * 2 < 65536, "DS offsets are 16 bits");
 };
 
-// Copies query tile `it` (Q and dO rows, lse and D) into LDS stage `stage`
-// (asynchronous; wait_dma() and a barrier make it visible).
-template <int D>
-__device__ __forceinline__ void dma_qtile(const BwdParams& p, const QTileIter& it, int32_t b, int32_t h,
-                                          __bf16* lds, float* f32s, int stage, int wave, int lane) {
-  using L = BwdLds<D>;
-  const int32_t ri = it.i - p.rank_begin;
-  const int32_t q0 = it.qt * kQm;
-  const int32_t Bb = (int32_t)p.Bb;
-  const __bf16* qb = reinterpret_cast<const __bf16*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head;
-  const __bf16* ob = reinterpret_cast<const __bf16*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch +
-                     h * p.dout.s_head;
-  // the 4-byte copies go first: issued after the 16-byte ones, they make the
-  // compiler wait for those to land
-  const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;
-  if (wave == 0) dma_f32_64(f32s + stage * kQm, p.lse2 + srow, q0, Bb, lane);
-  if (wave == 1) dma_f32_64(f32s + 2 * kQm + stage * kQm, p.dsum + srow, q0, Bb, lane);
-  dma_rows<D, kQm, kWaves>(lds + L::Q + stage * kQm * D, qb, p.q.s_tok, q0, Bb, wave, lane);
-  dma_rows<D, kQm, kWaves>(lds + L::DO + stage * kQm * D, ob, p.dout.s_tok, q0, Bb, wave, lane);
+// s_waitcnt lgkmcnt(N) with the registers of one read group tied to it.
+template <int N, int A, int B>
+__device__ __forceinline__ void lds_wait_grp(u32x4 (&r)[A], u32x2 (&t)[B]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  if constexpr (A == 4 && B == 4) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
+                 : "n"(N));
+  } else if constexpr (A == 2 && B == 4) {
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(r[0]), "+v"(r[1]), "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3])
+                 : "n"(N));
+  } else {
+    static_assert(A == 0, "read group shape");
+  }
 }
+
+template <int N>
+__device__ __forceinline__ void lds_wait_grp2(u32x4 (&r)[2], u32x4 (&t)[2]) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(t[0]), "+v"(t[1]) : "n"(N));
+}
+
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(ic<I>{}), ...);
+}
+
+// f(ic<0>{}), ..., f(ic<N-1>{}).
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
+
+// One query tile as its copies see it: the first byte of its Q and dO rows
+// and of its lse2 and D entries, and how many of its rows lie in the block.
+struct QTileSrc {
+  const unsigned char *q, *o;
+  const float *l, *d;
+  int32_t rows;
+};
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   using L = BwdLds<D>;
+  constexpr int NSS = D / 16;          // 16-feature steps of the S / dP products
+  constexpr int NDT = D / 32;          // 32-feature tiles of dK^T / dV^T
+  constexpr int RW = 1024 / (2 * D);   // rows per 1 KB copy
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int NCP = kQm / RW / kWaves;  // row copies per wave per tensor
+  constexpr int NCOPY = 2 * NCP + 1;   // copies per wave per tile
+  static_assert(2 * NDT == NSS, "one pair of dV products per feature step");
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  __bf16* lds = reinterpret_cast<__bf16*>(smem_raw);
-  float* f32s = reinterpret_cast<float*>(smem_raw + L::F32_OFF);  // lse2[2][64], dsum[2][64]
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int n = lane % 32;
   const int hf = lane / 32;
   const int grp = (lane / 16) % 2;
   const int j16 = lane % 16;
-  const int kg = wave % 4;
-  const int qh = wave / 4;
 
   const int32_t BHk = p.B * p.Hk;
   const int32_t tiles = (int32_t)((p.Bb + kKn - 1) / kKn);
-  // consecutive logical indices share (batch, K/V head, block) and take its
-  // key tiles in order (early keys are seen by more rows), so the workgroups
-  // of one XCD walk the same query tiles together and share them in L2
   const int64_t lw = xcd_logical(blockIdx.x, (int64_t)BHk * p.P * tiles);
   const int32_t tile = (int32_t)(lw % tiles);
   const int64_t g = lw / tiles;
@@ -150,237 +154,462 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   const int32_t hk = bhk % p.Hk;
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t kv0 = tile * kKn;
-  const int32_t kw = kv0 + 32 * kg;  // first key of this wave
-  const int32_t key = kw + n;        // this lane's key
+  const int32_t kw = kv0 + 32 * wave;  // first key of this wave
+  const int32_t key = kw + n;          // this lane's key
+  const int32_t qtiles = (Bb + kQm - 1) / kQm;
 
-  // K and V of the tile, once
-  {
-    const __bf16* kb = reinterpret_cast<const __bf16*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + hk * p.k.s_head;
-    const __bf16* vb = reinterpret_cast<const __bf16*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + hk * p.v.s_head;
-    dma_rows<D, kKn, kWaves>(lds + L::K, kb, p.k.s_tok, kv0, Bb, wave, lane);
-    dma_rows<D, kKn, kWaves>(lds + L::V, vb, p.v.s_tok, kv0, Bb, wave, lane);
+  f32x16 dk[NDT], dv[NDT];  // dK^T, dV^T: [dt][i] = feature 32dt + 8(i/4) + 4hf + i%4, key n
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
   }
 
-  f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: [dt][i] = feature 32dt + 8(i/4) + 4hf + i%4, key n
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    f32x16 z = {};
-    dk[dt] = z;
-    dv[dt] = z;
-  }
-  const float c2 = p.scale_log2;
-
-  QTileIter cur;
-  cur.kstep = -1;
-  cur.qtiles = (Bb + kQm - 1) / kQm;
-  cur.j = j;
-  cur.P = p.P;
-  cur.G = p.G;
-  cur.rb = p.rank_begin;
-  cur.re = p.rank_begin + p.n_ranks;
-  cur.layout = p.layout;
-  cur.causal = p.causal;
-  cur.kv0 = kv0;
-  cur.Bb = Bb;
-  const bool any = cur.step_rank();
-  if (any) dma_qtile<D>(p, cur, b, hk * p.G + cur.gi, lds, f32s, 0, wave, lane);
-  wait_dma();  // K, V and the first query tile
-  // LDS addresses (bytes) of this lane's reads, as per-lane bases plus
-  // compile-time offsets, so that the walk spends no instructions on them:
-  //   bkv[ss]: K row n of the wave's key group, columns 16ss + 8hf (V: + V_B)
-  //   bq[ss]:  Q row n of the wave's row half, same columns (query stage ST:
-  //            + ST * QST_B; dO: + DO_B)
-  //   bt[h2][dt]: transposing reads of Q / dO at rows 4hf + j16/4 + 8h2
-  //            (+16kq) of the row half, columns 32dt + 16grp + 4(j16%4)
-  //   bl:      lse2 of rows 32qh + 4hf .. of stage 0 (D: + DS_B)
-  constexpr int V_B = 2 * (L::V - L::K);
-  constexpr int QST_B = 2 * kQm * D;
-  constexpr int DO_B = 2 * (L::DO - L::Q);
-  constexpr int DS_B = 4 * 2 * kQm;
-  static_assert(V_B < 65536 && DO_B + 2 * QST_B <= 65536, "LDS read offsets must fit the 16-bit field");
-  const uint32_t lbase = lds_addr(smem_raw);
-  uint32_t bkv[D / 16], bq[D / 16], bt[2][D / 32];
-#pragma unroll
-  for (int ss = 0; ss < D / 16; ++ss) {
-    const int c = tile_off<D>(n, 16 * ss + 8 * hf);
-    bkv[ss] = lbase + 2 * (L::K + c + 32 * kg * D);
-    bq[ss] = lbase + 2 * (L::Q + c + 32 * qh * D);
-  }
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      bt[h2][dt] = lbase + 2 * (L::Q + 32 * qh * D +
-                                tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4)));
-  const uint32_t bl = lbase + L::F32_OFF + 4 * (32 * qh + 4 * hf);
-
-  // One query tile in stage ST: recompute S and P, dP, dS; dV^T += dO^T P,
-  // dK^T += Q^T dS. The next tile is copied into the other stage meanwhile.
-  // Returns whether there is a next tile.
-  auto step = [&](auto STc) __attribute__((always_inline)) -> bool {
-    constexpr int ST = decltype(STc)::value;
-    __syncthreads();  // this query stage is in LDS; the other one is no longer read
-    QTileIter nx = cur;
-    const bool more = nx.next();
-    if (more) dma_qtile<D>(p, nx, b, hk * p.G + nx.gi, lds, f32s, ST ^ 1, wave, lane);  // lands during the compute below
-
-    const BlockRel rel = block_relation(p.layout, p.causal, cur.i, j, Bb);
-    const int32_t q0 = cur.qt * kQm;
-    const int32_t qw = q0 + 32 * qh;  // first row of this wave
-    // row extents grow with the row: the wave's last row sees the most keys,
-    // its first row the fewest
-    const bool dead = (kw >= Bb) || (qw >= Bb) || (row_extent32(rel, qw + 31) <= kw);
-    if (!dead) {
-      const bool need_mask = (row_extent32(rel, qw) < kw + 32) || (qw + 32 > Bb);
-      // rows a >= a_min see this lane's key (only needed when masking)
-      const int32_t a_min = need_mask ? first_row_seeing32(rel, key, Bb) : 0;
-      // S = Q K^T and dP = dO V^T over the features: the Q, K, dO and V
-      // fragments of one 16-feature step are read one step ahead of their
-      // MFMAs
-      f32x16 s = {}, dp = {};
-      u32x4 rg[2][4];
-      auto rd = [&](u32x4(&r)[4], int ss) __attribute__((always_inline)) {
-        r[0] = lds_read16<ST * QST_B>(bq[ss]);
-        r[1] = lds_read16<0>(bkv[ss]);
-        r[2] = lds_read16<DO_B + ST * QST_B>(bq[ss]);
-        r[3] = lds_read16<V_B>(bkv[ss]);
-      };
-      rd(rg[0], 0);
-#pragma unroll
-      for (int ss = 0; ss < D / 16; ++ss) {
-        if (ss + 1 < D / 16) {
-          rd(rg[(ss + 1) & 1], ss + 1);
-          lds_wait<4>(rg[ss & 1]);
-        } else {
-          lds_wait<0>(rg[ss & 1]);
-        }
-        s = mfma32(__builtin_bit_cast(bf16x8, rg[ss & 1][0]), __builtin_bit_cast(bf16x8, rg[ss & 1][1]), s);
-        dp = mfma32(__builtin_bit_cast(bf16x8, rg[ss & 1][2]), __builtin_bit_cast(bf16x8, rg[ss & 1][3]), dp);
+  // The walk, in two passes over the ranks (ring order) and, at each rank,
+  // the G query heads of this K/V head: first the query tiles in which some
+  // row does not see some key of the tile (the causal diagonal), then the
+  // tiles every row of which sees every key. Row extents grow with the row,
+  // so at each rank the first kind is a run of tiles [wq_first, wq_full)
+  // and the second the rest up to the last tile; each pass runs its own copy
+  // of the step, and only the first masks. (wk, wi, wgi, wqt) is the tile
+  // to copy next; per rank: its relation to block j, the pass's tile range,
+  // and (per lane) the first row that sees this lane's key.
+  int32_t wpass = 0, wk = -1, wi = 0, wgi = 0, wqt = 0, wq_lo = 0, wq_hi = 0;
+  BlockRel wrel = make_rel(kNone, 0, Bb);
+  int32_t wfrs = Bb;
+  const int32_t klast = kv0 + kKn - 1 < Bb ? kv0 + kKn - 1 : Bb - 1;
+  auto next_rank = [&]() -> bool {
+    for (;;) {
+      while (++wk < p.P) {
+        wi = ring_rank(j, wk, p.P);
+        if (wi < p.rank_begin || wi >= p.rank_begin + p.n_ranks) continue;
+        wrel = block_relation(p.layout, p.causal, wi, j, Bb);
+        const int32_t a_first = first_row_seeing32(wrel, kv0, Bb);
+        if (a_first >= Bb) continue;
+        const int32_t q_first = a_first / kQm;
+        int32_t q_full = (first_row_seeing32(wrel, klast, Bb) + kQm - 1) / kQm;
+        q_full = q_full < qtiles ? q_full : qtiles;
+        wq_lo = wpass == 0 ? q_first : (q_full > q_first ? q_full : q_first);
+        wq_hi = wpass == 0 ? q_full : qtiles;
+        if (wq_lo >= wq_hi) continue;
+        wqt = wq_lo;
+        wgi = 0;
+        wfrs = first_row_seeing32(wrel, key, Bb);
+        return true;
       }
-      // lane (hf, n): key n against rows 8(i/4) + 4hf + i%4 of the wave's 32.
-      // lse2 and D of rows 8g + 4hf .. +3 are read one group ahead.
-      bf16x8 pb[2], dsb[2];
-      u32x4 ldr[2][2];  // [slot][lse2, D]
-      auto ld_rows = [&](u32x4(&r)[2], int g) __attribute__((always_inline)) {
-        switch (g) {
-          case 0: r[0] = lds_read16<ST * 4 * kQm + 0>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 0>(bl); break;
-          case 1: r[0] = lds_read16<ST * 4 * kQm + 32>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 32>(bl); break;
-          case 2: r[0] = lds_read16<ST * 4 * kQm + 64>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 64>(bl); break;
-          default: r[0] = lds_read16<ST * 4 * kQm + 96>(bl); r[1] = lds_read16<DS_B + ST * 4 * kQm + 96>(bl); break;
-        }
-      };
-      ld_rows(ldr[0], 0);
+      if (wpass == 1) return false;
+      wpass = 1;
+      wk = -1;
+    }
+  };
+  // 0: no more tiles; 1: the next tile of the same head; 2: another head or rank
+  auto next_tile = [&]() -> int {
+    if (++wqt < wq_hi) return 1;
+    if (++wgi < p.G) {
+      wqt = wq_lo;
+      return 2;
+    }
+    return next_rank() ? 2 : 0;
+  };
+  auto src_of_walk = [&]() {
+    const int32_t ri = wi - p.rank_begin;
+    const int32_t h = hk * p.G + wgi;
+    const int32_t q0 = wqt * kQm;
+    QTileSrc s;
+    s.q = reinterpret_cast<const unsigned char*>(p.q.ptr) +
+          2 * (ri * p.q.s_blk + b * p.q.s_batch + h * p.q.s_head + q0 * p.q.s_tok);
+    s.o = reinterpret_cast<const unsigned char*>(p.dout.ptr) +
+          2 * (ri * p.dout.s_blk + b * p.dout.s_batch + h * p.dout.s_head + q0 * p.dout.s_tok);
+    const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb + q0;
+    s.l = p.lse2 + srow;
+    s.d = p.dsum + srow;
+    s.rows = Bb - q0 < kQm ? Bb - q0 : kQm;
+    return s;
+  };
+  // the tile after `s` in the same head: 64 rows on
+  auto src_next_row_tile = [&](QTileSrc& s) {
+    s.q += (int64_t)kQm * 2 * p.q.s_tok;
+    s.o += (int64_t)kQm * 2 * p.dout.s_tok;
+    s.l += kQm;
+    s.d += kQm;
+    const int32_t left = Bb - wqt * kQm;
+    s.rows = left < kQm ? left : kQm;
+  };
+  // the first row of the walk's tile (less 4hf) that sees this lane's key
+  auto lo_of_walk = [&]() { return wfrs - wqt * kQm - 4 * hf; };
+
+  if (next_rank()) {
+    // K and V of this lane's key (row Bb - 1 past the block: finite, and its
+    // results are not stored) as the B operands of the feature steps:
+    // kreg[ss] = K[key][16ss + 8hf .. +7]
+    bf16x8 kreg[NSS], vreg[NSS];
+    {
+      const int32_t kr = key < Bb ? key : Bb - 1;
+      const __bf16* kp = reinterpret_cast<const __bf16*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch +
+                         (int64_t)kr * p.k.s_tok + hk * p.k.s_head + 8 * hf;
+      const __bf16* vp = reinterpret_cast<const __bf16*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch +
+                         (int64_t)kr * p.v.s_tok + hk * p.v.s_head + 8 * hf;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (g + 1 < 4) {
-          ld_rows(ldr[(g + 1) & 1], g + 1);
-          lds_wait<2>(ldr[g & 1]);
-        } else {
-          lds_wait<0>(ldr[g & 1]);
-        }
-        const int qr0 = 32 * qh + 8 * g + 4 * hf;  // row within the 64-row tile
-        const float4 l4 = __builtin_bit_cast(float4, ldr[g & 1][0]);
-        const float4 d4 = __builtin_bit_cast(float4, ldr[g & 1][1]);
+      for (int ss = 0; ss < NSS; ++ss) {
+        kreg[ss] = *reinterpret_cast<const bf16x8*>(kp + 16 * ss);
+        vreg[ss] = *reinterpret_cast<const bf16x8*>(vp + 16 * ss);
+      }
+    }
+    // The first step finishes a "previous" tile of zero probabilities read
+    // from stage 3: zero that stage's Q and dO, so that no stale LDS bits (a
+    // NaN pattern) reach the accumulators.
+    {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      constexpr int N16 = L::QST_B / 16;
+#pragma unroll
+      for (int k = 0; k < N16 / kThreads; ++k) {
+        reinterpret_cast<u32x4*>(smem_raw + L::Q_B + 3 * L::QST_B)[tid + k * kThreads] = z;
+        reinterpret_cast<u32x4*>(smem_raw + L::DO_B + 3 * L::QST_B)[tid + k * kThreads] = z;
+      }
+    }
+
+    // This lane's byte offsets in the row copies: copy k of the wave covers
+    // tile rows (wave + 4k) RW .. +RW-1; the lane fetches the logical chunk
+    // that belongs at its place in the swizzled row (the swizzle repeats
+    // every 16 rows, and 4 RW is a multiple of 16).
+    const int32_t crow = wave * RW + lane / CPR;
+    const int32_t cchunk = (lane % CPR) ^ chunk_swz<D>(crow);
+    const int32_t sq2 = (int32_t)(2 * p.q.s_tok), so2 = (int32_t)(2 * p.dout.s_tok);
+    const int32_t vq = crow * sq2 + 16 * cchunk, vo = crow * so2 + 16 * cchunk;
+    auto dma = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(wave == 1 ? s.d : s.l), (short)0, 4 * s.rows, kRawRsrcWord3);
+      const int32_t foff = wave < 2 ? L::F32_B + (wave * kNst + stage) * kQm * 4 : L::SPARE_B + (wave - 2) * kQm * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(smem_raw + foff), 4,
+                                              4 * lane, 0, 0, 0);
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)s.q, (short)0, sq2 * s.rows,
+                                                                          kRawRsrcWord3);
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)s.o, (short)0, so2 * s.rows,
+                                                                          kRawRsrcWord3);
+#pragma unroll
+      for (int k = 0; k < NCP; ++k) {
+        const int qc = wave + kWaves * k;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rq, (__attribute__((address_space(3))) void*)(smem_raw + L::Q_B + stage * L::QST_B + qc * 1024), 16,
+            vq + k * kWaves * RW * sq2, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < NCP; ++k) {
+        const int qc = wave + kWaves * k;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ro, (__attribute__((address_space(3))) void*)(smem_raw + L::DO_B + stage * L::QST_B + qc * 1024), 16,
+            vo + k * kWaves * RW * so2, 0, 0, 0);
+      }
+    };
+
+    // tiles t (current), t + 1 and t + 2 (the walk's position): whether they
+    // exist, and the pass and mask data of t and t + 1
+    QTileSrc src = src_of_walk();
+    int32_t cpass = wpass, npass = 1;
+    int32_t clo = lo_of_walk(), nlo = 0;
+    dma(src, 0);
+    bool v1 = next_tile() != 0;
+    if (v1) {
+      src = src_of_walk();
+      npass = wpass;
+      nlo = lo_of_walk();
+    }
+    dma(src, 1);
+    bool v2 = v1 && next_tile() != 0;
+    if (v2) src = src_of_walk();
+    // the K / V registers are in (the compiler waits for them here, once)
+#pragma unroll
+    for (int ss = 0; ss < NSS; ++ss) asm volatile("" : "+v"(kreg[ss]), "+v"(vreg[ss]));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zeroed stage
+
+    const float c2 = p.scale_log2;
+    // LDS byte addresses of this lane's reads. Current tile (stage st):
+    //   cq / co[ss]: Q / dO row n, columns 16ss + 8hf (row block rb: + 32 rows)
+    //   cl: lse2 of rows 4hf .. +3 (+ 8gg + 32rb; D: + DS_B)
+    // previous tile (stage st - 1), transposing reads:
+    //   pq / po[h2][dt]: Q / dO rows 4hf + j16/4 + 8h2 (chunk kc: + 16 rows),
+    //   columns 32dt + 16grp + 4(j16%4)
+    const uint32_t lbase = lds_addr(smem_raw);
+    uint32_t cq[NSS], co[NSS], pq[2][NDT], po[2][NDT];
+#pragma unroll
+    for (int ss = 0; ss < NSS; ++ss) {
+      const uint32_t c = 2 * tile_off<D>(n, 16 * ss + 8 * hf);
+      cq[ss] = lbase + L::Q_B + c;
+      co[ss] = lbase + L::DO_B + c;
+    }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint32_t c = 2 * tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
+        pq[h2][dt] = lbase + L::Q_B + 3 * L::QST_B + c;
+        po[h2][dt] = lbase + L::DO_B + 3 * L::QST_B + c;
+      }
+    uint32_t cl = lbase + L::F32_B + 4 * (4 * hf);
+
+    // P and dS of the previous tile (B operands of its dV / dK products, one
+    // per 16-row chunk kc: rows 16kc + 8(x/4) + 4hf + x%4 for element x)
+    bf16x8 pbp[4], dsp[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      pbp[kc] = bf16x8{};
+      dsp[kc] = bf16x8{};
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS of the previous tile, chunks (dt,
+    // kc) = (X/2, 2(X%2) + 0 / 1): the transposing reads and the products
+    auto rd_prev = [&](u32x2* t, const uint32_t(&base)[2][NDT], auto Xc) __attribute__((always_inline)) {
+      constexpr int X = decltype(Xc)::value;
+      constexpr int dt = X / 2, k0 = 2 * (X % 2);
+      t[0] = tr_read_at<k0 * 16 * D * 2>(base[0][dt]);
+      t[1] = tr_read_at<k0 * 16 * D * 2>(base[1][dt]);
+      t[2] = tr_read_at<(k0 + 1) * 16 * D * 2>(base[0][dt]);
+      t[3] = tr_read_at<(k0 + 1) * 16 * D * 2>(base[1][dt]);
+    };
+    auto mm_prev = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto Xc) __attribute__((always_inline)) {
+      constexpr int X = decltype(Xc)::value;
+      constexpr int dt = X / 2, k0 = 2 * (X % 2);
+      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3)), bop[k0], acc[dt]);
+      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3)), bop[k0 + 1], acc[dt]);
+    };
+
+    int32_t st = 0;
+    bool v0 = true;
+    auto step = [&](auto MASKc) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(MASKc)::value != 0;
+      wait_vm<NCOPY>();  // the current tile has landed (the next one may still be in flight)
+      wg_barrier();      // every wave's share of it is in LDS; stage st + 2 is read by nobody
+      dma(src, (st + 2) & 3);
+
+      // The step in three phases, each a stretch of straight-line code that
+      // mixes matrix products with the reads and vector work they do not
+      // depend on:
+      //   1. S and dP of row block 0 (A operands: Q / dO rows n), and dV^T of
+      //      the previous tile;
+      //   2. S and dP of row block 1 (rows 32 + n), and P / dS of row block 0;
+      //   3. dK^T of the previous tile, and P / dS of row block 1.
+      // Reads are issued one group ahead of their use. P and dS of element i
+      // of row block rb belong to row 32rb + 8(i/4) + 4hf + i%4.
+      f32x16 sacc[2], dacc[2];
+      bf16x8 pbc[4], dsc[4];
+      const f32x16 zacc = {};
+      // keeps the conversions of chunk kc where they are, between the
+      // products (they would otherwise sink to the next step, which uses them)
+      auto pin = [&](int kc) __attribute__((always_inline)) {
+        asm volatile("" : "+v"(pbc[kc]), "+v"(dsc[kc]));
+      };
+      // P and dS of elements 4gg + e0, +1 of row block rb, lse2 / D of the
+      // group's rows in lr
+      auto p_ds = [&](int rb, int gg, int e0, const u32x4(&lr)[2]) __attribute__((always_inline)) {
+        const float4 l4 = __builtin_bit_cast(float4, lr[0]);
+        const float4 d4 = __builtin_bit_cast(float4, lr[1]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};  // lse in log2 units
         const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          float pv = fexp2(fmaf(s[i], c2, -lv[e]));
-          if (need_mask) {
-            const int32_t a = q0 + qr0 + e;
-            if (a < a_min || a >= Bb) pv = 0.0f;
+        for (int e = e0; e < e0 + 2; ++e) {
+          const int i = 4 * gg + e;
+          float pv = fexp2(fmaf(sacc[rb][i], c2, -lv[e]));
+          if constexpr (MASK) {
+            if (32 * rb + 8 * gg + e < clo) pv = 0.0f;
           }
-          const float dsv = pv * (dp[i] - dd[e]);
-          pb[g / 2][4 * (g % 2) + e] = (__bf16)pv;
-          dsb[g / 2][4 * (g % 2) + e] = (__bf16)dsv;
-        }
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS: contraction over the wave's 32 rows.
-      // The transposing reads of (dt, kq) come in groups of 4, one group
-      // ahead of their MFMAs.
-      auto tr_group = [&](u32x2(&r)[2][2], int idx) __attribute__((always_inline)) {
-        const int dt = idx / 2;
-        if (idx % 2 == 0) {
-          r[0][0] = tr_read_at<DO_B + ST * QST_B>(bt[0][dt]);
-          r[0][1] = tr_read_at<DO_B + ST * QST_B>(bt[1][dt]);
-          r[1][0] = tr_read_at<ST * QST_B>(bt[0][dt]);
-          r[1][1] = tr_read_at<ST * QST_B>(bt[1][dt]);
-        } else {
-          r[0][0] = tr_read_at<DO_B + ST * QST_B + 16 * D * 2>(bt[0][dt]);
-          r[0][1] = tr_read_at<DO_B + ST * QST_B + 16 * D * 2>(bt[1][dt]);
-          r[1][0] = tr_read_at<ST * QST_B + 16 * D * 2>(bt[0][dt]);
-          r[1][1] = tr_read_at<ST * QST_B + 16 * D * 2>(bt[1][dt]);
+          const float dsv = pv * (dacc[rb][i] - dd[e]);
+          pbc[2 * rb + gg / 2][4 * (gg % 2) + e] = (__bf16)pv;
+          dsc[2 * rb + gg / 2][4 * (gg % 2) + e] = (__bf16)dsv;
         }
       };
-      constexpr int NG = 2 * (D / 32);
-      u32x2 trg[2][2][2];
-      tr_group(trg[0], 0);
-#pragma unroll
-      for (int idx = 0; idx < NG; ++idx) {
-        if (idx + 1 < NG) {
-          tr_group(trg[(idx + 1) & 1], idx + 1);
-          lds_wait<4>(trg[idx & 1]);
-        } else {
-          lds_wait<0>(trg[idx & 1]);
-        }
-        const int dt = idx / 2, kq = idx % 2;
-        const bf16x8 ot = __builtin_bit_cast(bf16x8, __builtin_shufflevector(trg[idx & 1][0][0], trg[idx & 1][0][1], 0, 1, 2, 3));
-        const bf16x8 qt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(trg[idx & 1][1][0], trg[idx & 1][1][1], 0, 1, 2, 3));
-        dv[dt] = mfma32(ot, pb[kq], dv[dt]);
-        dk[dt] = mfma32(qt, dsb[kq], dk[dt]);
+      // Phase 1
+      {
+        u32x4 ra[2][4];
+        u32x2 ta[2][4];
+        auto rd = [&](auto SSc) __attribute__((always_inline)) {
+          constexpr int SS = decltype(SSc)::value;
+          constexpr int sl = SS & 1;
+          ra[sl][0] = lds_read16<0>(cq[SS]);
+          ra[sl][1] = lds_read16<0>(co[SS]);
+          rd_prev(ta[sl], po, SSc);
+        };
+        rd(ic<0>{});
+        unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
+          constexpr int SS = decltype(SSc)::value;
+          constexpr int sl = SS & 1;
+          if constexpr (SS + 1 < NSS) {
+            rd(ic<SS + 1>{});
+            lds_wait_grp<6>(ra[sl], ta[sl]);
+          } else {
+            lds_wait_grp<0>(ra[sl], ta[sl]);
+          }
+          sacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sacc[0]);
+          mm_prev(dv, ta[sl], pbp, SSc);
+          dacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dacc[0]);
+        });
       }
-    }
-    if (!more) return false;
-    wait_dma();
-    cur = nx;
-    return true;
-  };
-  if (any)
-    while (step(ic<0>{}) && step(ic<1>{})) {
-    }
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase 2 (the lse2 / D rows of group gg of row block 0 come with the
+      // reads of feature step 2gg)
+      {
+        u32x4 ra[2][2];
+        u32x4 rl[2][2];
+        auto rd = [&](auto SSc) __attribute__((always_inline)) {
+          constexpr int SS = decltype(SSc)::value;
+          constexpr int sl = SS & 1;
+          ra[sl][0] = lds_read16<32 * D * 2>(cq[SS]);
+          ra[sl][1] = lds_read16<32 * D * 2>(co[SS]);
+          if constexpr (SS % 2 == 0) {
+            rl[(SS / 2) & 1][0] = lds_read16<(SS / 2) * 32>(cl);
+            rl[(SS / 2) & 1][1] = lds_read16<L::DS_B + (SS / 2) * 32>(cl);
+          }
+        };
+        rd(ic<0>{});
+        unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
+          constexpr int SS = decltype(SSc)::value;
+          constexpr int sl = SS & 1;
+          constexpr int gg = (SS / 2) % 4;
+          if constexpr (SS + 1 < NSS) {
+            rd(ic<SS + 1>{});
+            // outstanding after this step's group: the next group's reads
+            constexpr int nxt = ((SS + 1) % 2 == 0) ? 4 : 2;
+            if constexpr (SS % 2 == 0) lds_wait_grp2<nxt>(ra[sl], rl[(SS / 2) & 1]);
+            else lds_wait<nxt>(ra[sl]);
+          } else {
+            lds_wait<0>(ra[sl]);
+          }
+          sacc[1] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sacc[1]);
+          if constexpr (NSS == 8) p_ds(0, gg, 2 * (SS % 2), rl[(SS / 2) & 1]);
+          dacc[1] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dacc[1]);
+          if constexpr (NSS == 8 && SS % 4 == 3) pin(gg / 2);
+        });
+        if constexpr (NSS != 8) {
+          // d = 64: four feature steps; P / dS of row block 0 after them
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            u32x4 lr[2];
+            lr[0] = lds_read16<0>(cl + gg * 32);
+            lr[1] = lds_read16<L::DS_B>(cl + gg * 32);
+            lds_wait<0>(lr);
+            p_ds(0, gg, 0, lr);
+            p_ds(0, gg, 2, lr);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Phase 3: dK^T chunks X < 2 NDT of the previous tile; P / dS of row
+      // block 1 (group gg = X/2, elements 2(X%2), +1 for 8 chunks; d = 64:
+      // a whole group per chunk)
+      {
+        u32x2 tq[2][4];
+        u32x4 rl[2][2];
+        constexpr int NX = 2 * NDT;
+        constexpr int GPX = 8 / NX;  // element pairs per chunk
+        auto rd = [&](auto Xc) __attribute__((always_inline)) {
+          constexpr int X = decltype(Xc)::value;
+          constexpr int sl = X & 1;
+          rd_prev(tq[sl], pq, Xc);
+          constexpr int g0 = X * GPX / 2;  // first group of this chunk
+          if constexpr ((X * GPX) % 2 == 0) {
+            rl[g0 & 1][0] = lds_read16<g0 * 32 + 32 * 4>(cl);
+            rl[g0 & 1][1] = lds_read16<L::DS_B + g0 * 32 + 32 * 4>(cl);
+          }
+        };
+        rd(ic<0>{});
+        unroll<NX>([&](auto Xc) __attribute__((always_inline)) {
+          constexpr int X = decltype(Xc)::value;
+          constexpr int sl = X & 1;
+          constexpr int g0 = X * GPX / 2;
+          constexpr bool lnext = (X + 1 < NX) && (((X + 1) * GPX) % 2 == 0);
+          if constexpr (X + 1 < NX) {
+            rd(ic<X + 1>{});
+            constexpr int nxt = lnext ? 6 : 4;
+            lds_wait_grp<nxt>(rl[g0 & 1], tq[sl]);
+          } else {
+            lds_wait_grp<0>(rl[g0 & 1], tq[sl]);
+          }
+          mm_prev(dk, tq[sl], dsp, Xc);
+#pragma unroll
+          for (int k = 0; k < GPX; ++k) {
+            const int pr = X * GPX + k;  // element pair of row block 1
+            p_ds(1, pr / 2, 2 * (pr % 2), rl[(pr / 2) & 1]);
+          }
+          if constexpr (((X + 1) * GPX) % 2 == 0) {
+            constexpr int gl = ((X + 1) * GPX) / 2 - 1;  // group just finished
+            if constexpr (gl % 2 == 1) pin(2 + gl / 2);
+          }
+        });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        pbp[kc] = pbc[kc];
+        dsp[kc] = dsc[kc];
+      }
 
-  // the two waves of a key group add their partial dK^T, then dV^T
-  float* red = reinterpret_cast<float*>(smem_raw);  // [4 key groups][D/32*16 values][64 lanes]
-  constexpr int NV = (D / 32) * 16;
+      // move on: t + 1 becomes current, the walk's tile becomes t + 1, and
+      // the read addresses move one stage (the previous tile is now this one)
+      v0 = v1;
+      cpass = npass;
+      clo = nlo;
+      v1 = v2;
+      if (v2) {
+        npass = wpass;
+        nlo = lo_of_walk();
+        const int nt = next_tile();
+        v2 = nt != 0;
+        if (nt == 1) src_next_row_tile(src);
+        else if (nt == 2) src = src_of_walk();
+      }
+      const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::QST_B : L::QST_B;
+      const int32_t dp = st == 0 ? -(kNst - 1) * L::QST_B : L::QST_B;
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    f32x16* acc = which == 0 ? dk : dv;
-    __syncthreads();  // the LDS area is free
-    if (qh == 1) {
+      for (int ss = 0; ss < NSS; ++ss) {
+        cq[ss] += dc;
+        co[ss] += dc;
+      }
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) red[(kg * NV + dt * 16 + i) * 64 + lane] = acc[dt][i];
+        for (int dt = 0; dt < NDT; ++dt) {
+          pq[h2][dt] += dp;
+          po[h2][dt] += dp;
+        }
+      cl += st == kNst - 1 ? -(kNst - 1) * kQm * 4 : kQm * 4;
+      st = (st + 1) & (kNst - 1);
+    };
+    while (v0 && cpass == 0) step(ic<1>{});
+    while (v0) step(ic<0>{});
+
+    // the last tile's dV / dK products
+    {
+      u32x2 t[4];
+      unroll<2 * NDT>([&](auto Xc) __attribute__((always_inline)) {
+        rd_prev(t, po, Xc);
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
+        mm_prev(dv, t, pbp, Xc);
+        rd_prev(t, pq, Xc);
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
+        mm_prev(dk, t, dsp, Xc);
+      });
     }
-    __syncthreads();
-    if (qh == 0) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] += red[(kg * NV + dt * 16 + i) * 64 + lane];
-    }
+    wait_vm<0>();  // the repeated copies of the last steps
   }
-  if (qh == 1 || key >= Bb) return;
+
+  if (key >= Bb) return;
   __bf16* dkrow = reinterpret_cast<__bf16*>(p.dk.ptr) + j * p.dk.s_blk + b * p.dk.s_batch +
                   (int64_t)key * p.dk.s_tok + hk * p.dk.s_head;
   __bf16* dvrow = reinterpret_cast<__bf16*>(p.dv.ptr) + j * p.dv.s_blk + b * p.dv.s_batch +
                   (int64_t)key * p.dv.s_tok + hk * p.dv.s_head;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      bf16x4 wk, wv;
+      bf16x4 wk4, wv4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        wk[e] = (__bf16)(dk[dt][4 * g4 + e] * p.scale);
-        wv[e] = (__bf16)dv[dt][4 * g4 + e];
+        wk4[e] = (__bf16)(dk[dt][4 * g4 + e] * p.scale);
+        wv4[e] = (__bf16)dv[dt][4 * g4 + e];
       }
-      *reinterpret_cast<bf16x4*>(dkrow + 32 * dt + 8 * g4 + 4 * hf) = wk;
-      *reinterpret_cast<bf16x4*>(dvrow + 32 * dt + 8 * g4 + 4 * hf) = wv;
+      *reinterpret_cast<bf16x4*>(dkrow + 32 * dt + 8 * g4 + 4 * hf) = wk4;
+      *reinterpret_cast<bf16x4*>(dvrow + 32 * dt + 8 * g4 + 4 * hf) = wv4;
     }
 }
-
 
 // ---------------------------------------------------------------- fp32 path
 // Plain VALU kernel for float32: one lane per key (64 keys per workgroup),
