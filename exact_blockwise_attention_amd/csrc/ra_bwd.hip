@@ -302,25 +302,41 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       }
     };
 
-    // tiles t (current), t + 1 and t + 2 (the walk's position): whether they
-    // exist, and the pass and mask data of t and t + 1
+    // Tiles t (current) to t + 3 (the walk's position): whether they exist,
+    // and the pass and mask data of t, t + 1 and t + 2. Tiles t + 1 and t + 2
+    // are in flight while tile t is computed; the copy of t + 3 starts once
+    // every wave is done with the stage of t - 1.
     QTileSrc src = src_of_walk();
-    int32_t cpass = wpass, npass = 1;
-    int32_t clo = lo_of_walk(), nlo = 0;
+    int32_t pass0 = wpass, pass1 = 1, pass2 = 1;
+    int32_t lo0 = lo_of_walk(), lo1 = 0, lo2 = 0;
+    // moves the walk on and its copy source with it (the source stays on the
+    // last tile once the walk is over: copies then repeat it)
+    auto advance = [&]() -> bool {
+      const int nt = next_tile();
+      if (nt == 1) src_next_row_tile(src);
+      else if (nt == 2) src = src_of_walk();
+      return nt != 0;
+    };
     dma(src, 0);
-    bool v1 = next_tile() != 0;
+    bool v1 = advance();
     if (v1) {
-      src = src_of_walk();
-      npass = wpass;
-      nlo = lo_of_walk();
+      pass1 = wpass;
+      lo1 = lo_of_walk();
     }
     dma(src, 1);
-    bool v2 = v1 && next_tile() != 0;
-    if (v2) src = src_of_walk();
+    bool v2 = v1 && advance();
+    if (v2) {
+      pass2 = wpass;
+      lo2 = lo_of_walk();
+    }
+    dma(src, 2);
+    bool v3 = v2 && advance();
     // the K / V registers are in (the compiler waits for them here, once)
 #pragma unroll
     for (int ss = 0; ss < NSS; ++ss) asm volatile("" : "+v"(kreg[ss]), "+v"(vreg[ss]));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zeroed stage
+    wait_vm<2 * NCOPY>();  // tile 0 has landed
+    wg_barrier();
 
     const float c2 = p.scale_log2;
     // LDS byte addresses of this lane's reads. Current tile (stage st):
@@ -356,30 +372,50 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       dsp[kc] = bf16x8{};
     }
 
-    // dV^T += dO^T P and dK^T += Q^T dS of the previous tile, chunks (dt,
-    // kc) = (X/2, 2(X%2) + 0 / 1): the transposing reads and the products
-    auto rd_prev = [&](u32x2* t, const uint32_t(&base)[2][NDT], auto Xc) __attribute__((always_inline)) {
-      constexpr int X = decltype(Xc)::value;
-      constexpr int dt = X / 2, k0 = 2 * (X % 2);
-      t[0] = tr_read_at<k0 * 16 * D * 2>(base[0][dt]);
-      t[1] = tr_read_at<k0 * 16 * D * 2>(base[1][dt]);
-      t[2] = tr_read_at<(k0 + 1) * 16 * D * 2>(base[0][dt]);
-      t[3] = tr_read_at<(k0 + 1) * 16 * D * 2>(base[1][dt]);
+    // dV^T += dO^T P and dK^T += Q^T dS of the previous tile come in 4 NDT
+    // products, (feature tile dt, row chunk kc); product pair X (X < 2 NDT)
+    // is (X % NDT, X / NDT) and ((X + 1) % NDT, 2 + X / NDT): two different
+    // accumulators. The two transposing reads of one product:
+    auto rd_chunk = [&](u32x2* t, const uint32_t(&base)[2][NDT], auto DTc, auto KCc) __attribute__((always_inline)) {
+      constexpr int dt = decltype(DTc)::value, kc = decltype(KCc)::value;
+      t[0] = tr_read_at<kc * 16 * D * 2>(base[0][dt]);
+      t[1] = tr_read_at<kc * 16 * D * 2>(base[1][dt]);
     };
-    auto mm_prev = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto Xc) __attribute__((always_inline)) {
+    auto rd_pair = [&](u32x2* t, const uint32_t(&base)[2][NDT], auto Xc) __attribute__((always_inline)) {
       constexpr int X = decltype(Xc)::value;
-      constexpr int dt = X / 2, k0 = 2 * (X % 2);
-      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3)), bop[k0], acc[dt]);
-      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3)), bop[k0 + 1], acc[dt]);
+      rd_chunk(t, base, ic<X % NDT>{}, ic<X / NDT>{});
+      rd_chunk(t + 2, base, ic<(X + 1) % NDT>{}, ic<2 + X / NDT>{});
     };
+    auto mm_chunk = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto DTc, auto KCc) __attribute__((always_inline)) {
+      constexpr int dt = decltype(DTc)::value, kc = decltype(KCc)::value;
+      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3)), bop[kc], acc[dt]);
+    };
+    auto mm_first = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto Xc) __attribute__((always_inline)) {
+      constexpr int X = decltype(Xc)::value;
+      mm_chunk(acc, t, bop, ic<X % NDT>{}, ic<X / NDT>{});
+    };
+    auto mm_second = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto Xc) __attribute__((always_inline)) {
+      constexpr int X = decltype(Xc)::value;
+      mm_chunk(acc, t + 2, bop, ic<(X + 1) % NDT>{}, ic<2 + X / NDT>{});
+    };
+
+    // the first read group of phase 1 (Q / dO row block 0 at feature step
+    // 0, and the dO^T pair 0 of the previous tile), issued ahead of the step
+    u32x4 ra0[2];
+    u32x2 ta0[4];
+    auto rd1 = [&](u32x4* r, u32x2* t, auto SSc) __attribute__((always_inline)) {
+      constexpr int SS = decltype(SSc)::value;
+      r[0] = lds_read16<0>(cq[SS]);
+      r[1] = lds_read16<0>(co[SS]);
+      rd_pair(t, po, SSc);
+    };
+    rd1(ra0, ta0, ic<0>{});
 
     int32_t st = 0;
     bool v0 = true;
     auto step = [&](auto MASKc) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(MASKc)::value != 0;
-      wait_vm<NCOPY>();  // the current tile has landed (the next one may still be in flight)
-      wg_barrier();      // every wave's share of it is in LDS; stage st + 2 is read by nobody
-      dma(src, (st + 2) & 3);
+      const int32_t clo = lo0;
 
       // The step in three phases, each a stretch of straight-line code that
       // mixes matrix products with the reads and vector work they do not
@@ -419,27 +455,24 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       };
       // Phase 1
       {
-        u32x4 ra[2][4];
+        u32x4 ra[2][2];
         u32x2 ta[2][4];
-        auto rd = [&](auto SSc) __attribute__((always_inline)) {
-          constexpr int SS = decltype(SSc)::value;
-          constexpr int sl = SS & 1;
-          ra[sl][0] = lds_read16<0>(cq[SS]);
-          ra[sl][1] = lds_read16<0>(co[SS]);
-          rd_prev(ta[sl], po, SSc);
-        };
-        rd(ic<0>{});
+#pragma unroll
+        for (int k = 0; k < 2; ++k) ra[0][k] = ra0[k];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ta[0][k] = ta0[k];
         unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
           constexpr int SS = decltype(SSc)::value;
           constexpr int sl = SS & 1;
           if constexpr (SS + 1 < NSS) {
-            rd(ic<SS + 1>{});
+            rd1(ra[sl ^ 1], ta[sl ^ 1], ic<SS + 1>{});
             lds_wait_grp<6>(ra[sl], ta[sl]);
           } else {
             lds_wait_grp<0>(ra[sl], ta[sl]);
           }
+          mm_first(dv, ta[sl], pbp, SSc);
           sacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sacc[0]);
-          mm_prev(dv, ta[sl], pbp, SSc);
+          mm_second(dv, ta[sl], pbp, SSc);
           dacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dacc[0]);
         });
       }
@@ -492,19 +525,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      // Phase 3: dK^T chunks X < 2 NDT of the previous tile; P / dS of row
-      // block 1 (group gg = X/2, elements 2(X%2), +1 for 8 chunks; d = 64:
-      // a whole group per chunk)
+      // Phase 3: dK^T product pairs X < 2 NDT of the previous tile; P / dS
+      // of row block 1 (group gg = X/2, elements 2(X%2), +1 for 8 pairs;
+      // d = 64: a whole group per pair)
       {
         u32x2 tq[2][4];
         u32x4 rl[2][2];
         constexpr int NX = 2 * NDT;
-        constexpr int GPX = 8 / NX;  // element pairs per chunk
+        constexpr int GPX = 8 / NX;  // element pairs per product pair
         auto rd = [&](auto Xc) __attribute__((always_inline)) {
           constexpr int X = decltype(Xc)::value;
           constexpr int sl = X & 1;
-          rd_prev(tq[sl], pq, Xc);
-          constexpr int g0 = X * GPX / 2;  // first group of this chunk
+          rd_pair(tq[sl], pq, Xc);
+          constexpr int g0 = X * GPX / 2;  // first group of this pair
           if constexpr ((X * GPX) % 2 == 0) {
             rl[g0 & 1][0] = lds_read16<g0 * 32 + 32 * 4>(cl);
             rl[g0 & 1][1] = lds_read16<L::DS_B + g0 * 32 + 32 * 4>(cl);
@@ -518,17 +551,17 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
           constexpr bool lnext = (X + 1 < NX) && (((X + 1) * GPX) % 2 == 0);
           if constexpr (X + 1 < NX) {
             rd(ic<X + 1>{});
-            constexpr int nxt = lnext ? 6 : 4;
-            lds_wait_grp<nxt>(rl[g0 & 1], tq[sl]);
+            lds_wait_grp<lnext ? 6 : 4>(rl[g0 & 1], tq[sl]);
           } else {
             lds_wait_grp<0>(rl[g0 & 1], tq[sl]);
           }
-          mm_prev(dk, tq[sl], dsp, Xc);
+          mm_first(dk, tq[sl], dsp, Xc);
 #pragma unroll
           for (int k = 0; k < GPX; ++k) {
             const int pr = X * GPX + k;  // element pair of row block 1
             p_ds(1, pr / 2, 2 * (pr % 2), rl[(pr / 2) & 1]);
           }
+          mm_second(dk, tq[sl], dsp, Xc);
           if constexpr (((X + 1) * GPX) % 2 == 0) {
             constexpr int gl = ((X + 1) * GPX) / 2 - 1;  // group just finished
             if constexpr (gl % 2 == 1) pin(2 + gl / 2);
@@ -542,20 +575,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         dsp[kc] = dsc[kc];
       }
 
-      // move on: t + 1 becomes current, the walk's tile becomes t + 1, and
-      // the read addresses move one stage (the previous tile is now this one)
-      v0 = v1;
-      cpass = npass;
-      clo = nlo;
-      v1 = v2;
-      if (v2) {
-        npass = wpass;
-        nlo = lo_of_walk();
-        const int nt = next_tile();
-        v2 = nt != 0;
-        if (nt == 1) src_next_row_tile(src);
-        else if (nt == 2) src = src_of_walk();
-      }
+      // Tile t + 1 has landed (t + 2 may still be in flight); past the
+      // barrier no wave reads the stage of t - 1, which takes tile t + 3.
+      wait_vm<NCOPY>();
+      wg_barrier();
+      dma(src, (st + 3) & 3);
+      // the read addresses move one stage (the previous tile is now t), and
+      // the first read group of the next step goes out
       const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::QST_B : L::QST_B;
       const int32_t dp = st == 0 ? -(kNst - 1) * L::QST_B : L::QST_B;
 #pragma unroll
@@ -572,20 +598,38 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         }
       cl += st == kNst - 1 ? -(kNst - 1) * kQm * 4 : kQm * 4;
       st = (st + 1) & (kNst - 1);
+      rd1(ra0, ta0, ic<0>{});
+      // t + 1 becomes current
+      v0 = v1;
+      v1 = v2;
+      v2 = v3;
+      pass0 = pass1;
+      pass1 = pass2;
+      lo0 = lo1;
+      lo1 = lo2;
+      if (v3) {
+        pass2 = wpass;
+        lo2 = lo_of_walk();
+        v3 = advance();
+      }
     };
-    while (v0 && cpass == 0) step(ic<1>{});
+    while (v0 && pass0 == 0) step(ic<1>{});
     while (v0) step(ic<0>{});
 
     // the last tile's dV / dK products
     {
       u32x2 t[4];
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ra0[0]), "+v"(ra0[1]), "+v"(ta0[0]), "+v"(ta0[1]), "+v"(ta0[2]),
+                   "+v"(ta0[3]));
       unroll<2 * NDT>([&](auto Xc) __attribute__((always_inline)) {
-        rd_prev(t, po, Xc);
+        rd_pair(t, po, Xc);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
-        mm_prev(dv, t, pbp, Xc);
-        rd_prev(t, pq, Xc);
+        mm_first(dv, t, pbp, Xc);
+        mm_second(dv, t, pbp, Xc);
+        rd_pair(t, pq, Xc);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
-        mm_prev(dk, t, dsp, Xc);
+        mm_first(dk, t, dsp, Xc);
+        mm_second(dk, t, dsp, Xc);
       });
     }
     wait_vm<0>();  // the repeated copies of the last steps
