@@ -93,7 +93,8 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
     for (int dt = 0; dt < D / 32; ++dt)
       toff[h2][dt] = tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
 
-  KvIter c0;
+  KvPassIter c0;
+  c0.pass = 0;
   c0.kstep = -1;
   c0.nsteps = p.P;
   c0.single_block = -1;
@@ -101,18 +102,19 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   c0.P = p.P;
   c0.layout = p.layout;
   c0.causal = p.causal;
+  c0.a_lo = a0;
   c0.a_hi = a_hi;
   c0.Bb = Bb;
   auto kv_base = [&](const Seq& sq, int32_t blk) {
     return reinterpret_cast<const __bf16*>(sq.ptr) + (int64_t)blk * sq.s_blk + b * sq.s_batch + hk * sq.s_head;
   };
-  auto dma_tile = [&](const KvIter& t, int stage) {
+  auto dma_tile = [&](const KvPassIter& t, int stage) {
     __bf16* st = lds + stage * L::STAGE;
     dma_rows<D, kKvTn, kQWaves>(st, kv_base(p.k, t.j), p.k.s_tok, t.t * kKvTn, Bb, wave, lane);
     dma_rows<D, kKvTn, kQWaves>(st + L::TILE, kv_base(p.v, t.j), p.v.s_tok, t.t * kKvTn, Bb, wave, lane);
   };
   // no row of the wave sees the tile's first key (row extents grow with the row)
-  auto dead = [&](const KvIter& t) { return (aw >= Bb) || (row_extent32(t.rel, aw + 31) <= t.t * kKvTn); };
+  auto dead = [&](const KvPassIter& t) { return (aw >= Bb) || (row_extent32(t.rel, aw + 31) <= t.t * kKvTn); };
   // S^T = K Q^T and dP^T = V dO^T for keys 32 half .. +31 of a tile
   auto produce = [&](int stage, int half, f32x16* sd) {
     const __bf16* ks = lds + stage * L::STAGE;
@@ -129,19 +131,21 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
     }
   };
   const float c2 = p.scale_log2;
-  // dS^T from the half's scores, then dQ^T += K^T dS^T
-  auto consume = [&](const KvIter& t, int stage, auto HALFc, f32x16* sd) __attribute__((always_inline)) {
+  // dS^T from the half's scores, then dQ^T += K^T dS^T (MASK: the tile is
+  // one of the walk's first pass, which some rows see only in part)
+  auto consume = [&](const KvPassIter& t, int stage, auto HALFc, f32x16* sd, auto MASKc) __attribute__((always_inline)) {
     constexpr int half = decltype(HALFc)::value;
+    constexpr bool MASK = decltype(MASKc)::value != 0;
     const int32_t b0 = t.t * kKvTn + 32 * half;
     const uint32_t kb = lds_addr(lds + stage * L::STAGE);
     // the wave's first row sees the fewest keys; extents never exceed Bb
-    const bool need_mask = row_extent32(t.rel, aw) < b0 + 32;
-    const int32_t ext_a = row_extent32(t.rel, a);
+    const bool need_mask = MASK && row_extent32(t.rel, aw) < b0 + 32;
+    const int32_t ext_a = MASK ? row_extent32(t.rel, a) : 0;
     bf16x8 dsb[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       float pv = fexp2(fmaf(sd[0][e], c2, -lse2));
-      if (need_mask) {
+      if (MASK && need_mask) {
         const int32_t key = b0 + 8 * (e / 4) + 4 * hf + (e % 4);
         if (key >= ext_a) pv = 0.0f;
       }
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   // copies per K/V tile per wave (K and V), for the counted waits below
   constexpr int NI = 2 * (kKvTn / (1024 / (2 * D))) / kQWaves;
   if (c0.next_block()) {
-    KvIter c1 = c0, c2;
+    KvPassIter c1 = c0, c2;
     const bool v1 = c1.next();
     bool v2 = false;
     if (v1) {
@@ -188,25 +192,27 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
     if (!da) produce(0, 0, sa);
     int sc = 0;
     bool w1 = v1, w2 = v2;
-    // the MFMA pipe gets the next half's products before the current half's
-    // exponentials are computed; a ring of four stages holds the tile, the
-    // next one and two more in flight
-    while (true) {
-      KvIter c3 = c2;
+    // One tile (c0) per call; false once the walk is done. The MFMA pipe
+    // gets the next half's products before the current half's exponentials
+    // are computed; a ring of four stages holds the tile, the next one and
+    // two more in flight. The walk's first pass (tiles some rows see only in
+    // part) runs the masking copy of the step, the second pass the other.
+    auto step = [&](auto MASKc) __attribute__((always_inline)) -> bool {
+      KvPassIter c3 = c2;
       const bool v3 = w2 && c3.next();
       const int s1 = (sc + 1) & 3;
       if (v3) dma_tile(c3, (sc + 3) & 3);  // the stage the previous tile freed
       if (!da) {
         produce(sc, 1, sb);
-        consume(c0, sc, ic<0>{}, sa);
+        consume(c0, sc, ic<0>{}, sa, MASKc);
       }
       bool db = true;
       if (w1) {
         db = dead(c1);
         if (!db) produce(s1, 0, sa);
       }
-      if (!da) consume(c0, sc, ic<1>{}, sb);
-      if (!w1) break;
+      if (!da) consume(c0, sc, ic<1>{}, sb, MASKc);
+      if (!w1) return false;
       if (v3) wait_vm<NI>();  // tile c2 (read from the next step on) is in LDS
       else wait_dma();
       wg_barrier();  // stage sc is free
@@ -217,7 +223,11 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
       w2 = v3;
       da = db;
       sc = s1;
-    }
+      return true;
+    };
+    bool more = true;
+    while (more && c0.pass == 0) more = step(ic<1>{});
+    while (more) more = step(ic<0>{});
   }
 
   if (a >= Bb) return;

@@ -101,6 +101,39 @@ struct KvIter {
   __device__ bool next() { return (++t < ntile) ? true : next_block(); }
 };
 
+// The same tiles in two passes over the ring: first, in each block, the
+// tiles that some row of the query tile sees only in part (the causal
+// diagonal, and a last tile cut by the block's end), then the tiles that
+// every row sees whole (key tile t < ext(a_lo) / 64: row extents grow with
+// the row). A kernel runs its masking code in the first pass only.
+struct KvPassIter {
+  int32_t pass, kstep, nsteps, j, t, t_hi, t_lo;
+  BlockRel rel;
+  int32_t i, P, layout, causal, a_lo, a_hi, Bb, single_block;
+  __device__ bool next_block() {
+    for (;;) {
+      while (++kstep < nsteps) {
+        j = (single_block >= 0) ? single_block : ring_block(i, kstep, P);
+        rel = block_relation(layout, causal, i, j, Bb);
+        const int32_t extent = row_extent32(rel, a_hi);
+        if (extent <= 0) continue;
+        const int32_t ntile = (extent + kKvTn - 1) / kKvTn;
+        int32_t t_full = row_extent32(rel, a_lo) / kKvTn;
+        t_full = t_full < ntile ? t_full : ntile;
+        t_lo = pass == 0 ? t_full : 0;
+        t_hi = pass == 0 ? ntile : t_full;
+        if (t_lo >= t_hi) continue;
+        t = t_lo;
+        return true;
+      }
+      if (pass == 1) return false;
+      pass = 1;
+      kstep = -1;
+    }
+  }
+  __device__ bool next() { return (++t < t_hi) ? true : next_block(); }
+};
+
 // Direct global -> LDS copy (global_load_lds_dwordx4: lane l of a wave
 // writes its 16 bytes at the wave's LDS base + 16 l) of rows
 // [r_lo, r_lo + ROWS) of a strided [rows][D] tensor into a swizzled LDS tile,
