@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   // 4hf + j16/4 (+8) (+16kk) and columns 32dt + 16grp + 4(j16%4)
   uint32_t koff[D / 16], voff[2][D / 32];
 #pragma unroll
-  for (int ss = 0; ss < D / 16; ++ss) koff[ss] = 2 * tile_off<D>(n, 16 * ss + 8 * hf);
+  for (int ss = 0; ss < D / 16; ++ss) koff[ss] = lds_addr(smem_raw) + 2 * tile_off<D>(n, 16 * ss + 8 * hf);
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -208,19 +208,28 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   bf16x8 pb[4];   // its probabilities, B operand of the P V product
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T = K Q^T for the 64 keys in stage ST
+  // S^T = K Q^T for the 64 keys in stage ST: the two 32-key halves take
+  // turns on the MFMA pipe, and the K fragments of feature step ss + 1 are
+  // requested before the products of step ss
   auto scores = [&](auto STc) __attribute__((always_inline)) {
     constexpr int ST = decltype(STc)::value;
-    const unsigned char* ks = smem_raw + ST * L::TILE_B;
+    constexpr int NSS = D / 16;
+    u32x4 kf[2][2];  // [slot][half]
+    kf[0][0] = lds_read16<ST * L::TILE_B>(koff[0]);
+    kf[0][1] = lds_read16<ST * L::TILE_B + 32 * D * 2>(koff[0]);
+    const f32x16 z = {};
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      f32x16 z = {};
-      s[t2] = z;
-#pragma unroll
-      for (int ss = 0; ss < D / 16; ++ss) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff[ss] + t2 * 32 * D * 2);
-        s[t2] = mfma32(kf, qreg[ss], s[t2]);
+    for (int ss = 0; ss < NSS; ++ss) {
+      if (ss + 1 < NSS) {
+        kf[(ss + 1) & 1][0] = lds_read16<ST * L::TILE_B>(koff[ss + 1]);
+        kf[(ss + 1) & 1][1] = lds_read16<ST * L::TILE_B + 32 * D * 2>(koff[ss + 1]);
+        lds_wait<2>(kf[ss & 1]);
+      } else {
+        lds_wait<0>(kf[ss & 1]);
       }
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+        s[t2] = mfma32(__builtin_bit_cast(bf16x8, kf[ss & 1][t2]), qreg[ss], ss == 0 ? z : s[t2]);
     }
   };
   // Matrix phase: scores of the tile in stage SK (if any) and O^T += V^T P^T
