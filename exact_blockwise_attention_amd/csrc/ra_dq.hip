@@ -115,19 +115,34 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   };
   // no row of the wave sees the tile's first key (row extents grow with the row)
   auto dead = [&](const KvPassIter& t) { return (aw >= Bb) || (row_extent32(t.rel, aw + 31) <= t.t * kKvTn); };
-  // S^T = K Q^T and dP^T = V dO^T for keys 32 half .. +31 of a tile
-  auto produce = [&](int stage, int half, f32x16* sd) {
-    const __bf16* ks = lds + stage * L::STAGE;
-    const __bf16* vs = ks + L::TILE;
-    f32x16 z = {};
-    sd[0] = z;
-    sd[1] = z;
+  // S^T = K Q^T and dP^T = V dO^T for keys 32 half .. +31 of a tile; the K
+  // and V fragments of feature step ss + 1 are requested before the
+  // products of step ss
+  const uint32_t lbase = lds_addr(smem_raw);
+  auto produce = [&](int stage, auto HALFc, f32x16* sd) __attribute__((always_inline)) {
+    constexpr int half = decltype(HALFc)::value;
+    constexpr int NSS = D / 16;
+    constexpr int KO = 32 * half * D * 2, VO = L::TILE * 2 + KO;  // bytes
+    const uint32_t sb = lbase + stage * L::STAGE * 2;
+    u32x4 f[2][2];  // [slot][K, V]
+    {
+      const uint32_t ad = sb + 2 * koff[0];
+      f[0][0] = lds_read16<KO>(ad);
+      f[0][1] = lds_read16<VO>(ad);
+    }
+    const f32x16 z = {};
 #pragma unroll
-    for (int ss = 0; ss < D / 16; ++ss) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + koff[ss] + 32 * half * D);
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vs + koff[ss] + 32 * half * D);
-      sd[0] = mfma32(kf, qreg[ss], sd[0]);
-      sd[1] = mfma32(vf, oreg[ss], sd[1]);
+    for (int ss = 0; ss < NSS; ++ss) {
+      if (ss + 1 < NSS) {
+        const uint32_t ad = sb + 2 * koff[ss + 1];
+        f[(ss + 1) & 1][0] = lds_read16<KO>(ad);
+        f[(ss + 1) & 1][1] = lds_read16<VO>(ad);
+        lds_wait<2>(f[ss & 1]);
+      } else {
+        lds_wait<0>(f[ss & 1]);
+      }
+      sd[0] = mfma32(__builtin_bit_cast(bf16x8, f[ss & 1][0]), qreg[ss], ss == 0 ? z : sd[0]);
+      sd[1] = mfma32(__builtin_bit_cast(bf16x8, f[ss & 1][1]), oreg[ss], ss == 0 ? z : sd[1]);
     }
   };
   const float c2 = p.scale_log2;
@@ -189,7 +204,7 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
     __syncthreads();
     f32x16 sa[2], sb[2];  // scores of half 0 / half 1 of a tile
     bool da = dead(c0);
-    if (!da) produce(0, 0, sa);
+    if (!da) produce(0, ic<0>{}, sa);
     int sc = 0;
     bool w1 = v1, w2 = v2;
     // One tile (c0) per call; false once the walk is done. The MFMA pipe
@@ -203,13 +218,13 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
       const int s1 = (sc + 1) & 3;
       if (v3) dma_tile(c3, (sc + 3) & 3);  // the stage the previous tile freed
       if (!da) {
-        produce(sc, 1, sb);
+        produce(sc, ic<1>{}, sb);
         consume(c0, sc, ic<0>{}, sa, MASKc);
       }
       bool db = true;
       if (w1) {
         db = dead(c1);
-        if (!db) produce(s1, 0, sa);
+        if (!db) produce(s1, ic<0>{}, sa);
       }
       if (!da) consume(c0, sc, ic<1>{}, sb, MASKc);
       if (!w1) return false;
