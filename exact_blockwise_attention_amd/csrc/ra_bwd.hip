@@ -276,15 +276,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     const int32_t cchunk = (lane % CPR) ^ chunk_swz<D>(crow);
     const int32_t sq2 = (int32_t)(2 * p.q.s_tok), so2 = (int32_t)(2 * p.dout.s_tok);
     const int32_t vq = crow * sq2 + 16 * cchunk, vo = crow * so2 + 16 * cchunk;
-    auto dma = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
+    // the copies of one tile in two parts, lse2 / D and Q first, then dO
+    // (a step spreads them over its phases)
+    auto dma_q = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(wave == 1 ? s.d : s.l), (short)0, 4 * s.rows, kRawRsrcWord3);
       const int32_t foff = wave < 2 ? L::F32_B + (wave * kNst + stage) * kQm * 4 : L::SPARE_B + (wave - 2) * kQm * 4;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(smem_raw + foff), 4,
                                               4 * lane, 0, 0, 0);
       const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)s.q, (short)0, sq2 * s.rows,
-                                                                          kRawRsrcWord3);
-      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)s.o, (short)0, so2 * s.rows,
                                                                           kRawRsrcWord3);
 #pragma unroll
       for (int k = 0; k < NCP; ++k) {
@@ -293,6 +293,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
             rq, (__attribute__((address_space(3))) void*)(smem_raw + L::Q_B + stage * L::QST_B + qc * 1024), 16,
             vq + k * kWaves * RW * sq2, 0, 0, 0);
       }
+    };
+    auto dma_o = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)s.o, (short)0, so2 * s.rows,
+                                                                          kRawRsrcWord3);
 #pragma unroll
       for (int k = 0; k < NCP; ++k) {
         const int qc = wave + kWaves * k;
@@ -301,14 +305,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
             vo + k * kWaves * RW * so2, 0, 0, 0);
       }
     };
+    auto dma = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
+      dma_q(s, stage);
+      dma_o(s, stage);
+    };
 
-    // Tiles t (current) to t + 3 (the walk's position): whether they exist,
-    // and the pass and mask data of t, t + 1 and t + 2. Tiles t + 1 and t + 2
-    // are in flight while tile t is computed; the copy of t + 3 starts once
-    // every wave is done with the stage of t - 1.
+    // Tiles t (current), t + 1 and t + 2 (the walk's position): whether they
+    // exist, and the pass and mask data of t and t + 1. Tile t + 1 is in
+    // flight or has landed while tile t is computed; the step copies tile
+    // t + 2 into the stage of t - 2, which no wave reads any more.
     QTileSrc src = src_of_walk();
-    int32_t pass0 = wpass, pass1 = 1, pass2 = 1;
-    int32_t lo0 = lo_of_walk(), lo1 = 0, lo2 = 0;
+    int32_t pass0 = wpass, pass1 = 1;
+    int32_t lo0 = lo_of_walk(), lo1 = 0;
     // moves the walk on and its copy source with it (the source stays on the
     // last tile once the walk is over: copies then repeat it)
     auto advance = [&]() -> bool {
@@ -325,17 +333,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     }
     dma(src, 1);
     bool v2 = v1 && advance();
-    if (v2) {
-      pass2 = wpass;
-      lo2 = lo_of_walk();
-    }
-    dma(src, 2);
-    bool v3 = v2 && advance();
     // the K / V registers are in (the compiler waits for them here, once)
 #pragma unroll
     for (int ss = 0; ss < NSS; ++ss) asm volatile("" : "+v"(kreg[ss]), "+v"(vreg[ss]));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zeroed stage
-    wait_vm<2 * NCOPY>();  // tile 0 has landed
+    wait_vm<NCOPY>();  // tile 0 has landed
     wg_barrier();
 
     const float c2 = p.scale_log2;
@@ -471,6 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
             lds_wait_grp<0>(ra[sl], ta[sl]);
           }
           mm_first(dv, ta[sl], pbp, SSc);
+          if constexpr (SS == 1) dma_q(src, (st + 2) & 3);  // tile t + 2, first part
           sacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sacc[0]);
           mm_second(dv, ta[sl], pbp, SSc);
           dacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dacc[0]);
@@ -507,6 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
             lds_wait<0>(ra[sl]);
           }
           sacc[1] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sacc[1]);
+          if constexpr (SS == 1) dma_o(src, (st + 2) & 3);  // tile t + 2, second part
           if constexpr (NSS == 8) p_ds(0, gg, 2 * (SS % 2), rl[(SS / 2) & 1]);
           dacc[1] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dacc[1]);
           if constexpr (NSS == 8 && SS % 4 == 3) pin(gg / 2);
@@ -576,10 +580,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       }
 
       // Tile t + 1 has landed (t + 2 may still be in flight); past the
-      // barrier no wave reads the stage of t - 1, which takes tile t + 3.
+      // barrier no wave reads the stage of t - 1, which the next step fills
+      // with tile t + 3.
       wait_vm<NCOPY>();
       wg_barrier();
-      dma(src, (st + 3) & 3);
       // the read addresses move one stage (the previous tile is now t), and
       // the first read group of the next step goes out
       const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::QST_B : L::QST_B;
@@ -599,18 +603,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       cl += st == kNst - 1 ? -(kNst - 1) * kQm * 4 : kQm * 4;
       st = (st + 1) & (kNst - 1);
       rd1(ra0, ta0, ic<0>{});
-      // t + 1 becomes current
+      // t + 1 becomes current, the walk moves on to t + 3
       v0 = v1;
       v1 = v2;
-      v2 = v3;
       pass0 = pass1;
-      pass1 = pass2;
       lo0 = lo1;
-      lo1 = lo2;
-      if (v3) {
-        pass2 = wpass;
-        lo2 = lo_of_walk();
-        v3 = advance();
+      if (v2) {
+        pass1 = wpass;
+        lo1 = lo_of_walk();
+        v2 = advance();
       }
     };
     while (v0 && pass0 == 0) step(ic<1>{});
