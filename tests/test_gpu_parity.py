@@ -215,6 +215,11 @@ SMALL_BWD = [
     Case(155, 1, 4, 800, 128, 4, True, "zigzag", "bf16", Hk=1),
     Case(156, 1, 4, 400, 64, 4, True, "striped", "f32", Hk=2),
     Case(157, 2, 6, 512, 128, 4, False, "contiguous", "bf16", Hk=3),
+    # blocks that end inside a 64-row / 64-key tile without a causal mask:
+    # the last tile is the only one the walks treat as partly visible
+    Case(158, 1, 2, 600, 128, 4, False, "contiguous", "bf16"),
+    Case(159, 1, 2, 344, 64, 4, False, "striped", "bf16", Hk=1),
+    Case(160, 1, 4, 1020, 64, 6, True, "zigzag", "bf16", Hk=2),
 ]
 
 
