@@ -70,15 +70,15 @@ constexpr int kRawRsrcWord3 = 0x00020000;  // untyped 32-bit data, bounds-checke
 
 template <int D>
 struct BwdLds {
-  static constexpr int QST_B = kQm * D * 2;         // one stage of Q (or dO), bytes
-  static constexpr int Q_B = 0;                     // Q stages
-  static constexpr int DO_B = kNst * QST_B;        // dO stages
-  static constexpr int F32_B = 2 * kNst * QST_B;   // lse2[4][64], then dsum[4][64], then 2 spare rows
+  static constexpr int QST_B = kQm * D * 2;         // one tile of Q (or dO), bytes
+  static constexpr int DO_B = QST_B;                // dO after Q in each stage
+  static constexpr int STG_B = 2 * QST_B;           // one stage: Q, then dO
+  static constexpr int F32_B = kNst * STG_B;        // lse2[4][64], then dsum[4][64], then 2 spare rows
   static constexpr int DS_B = kNst * kQm * 4;      // dsum after lse2
   static constexpr int SPARE_B = F32_B + 2 * DS_B;  // [2][64] floats, written by waves 2 and 3
   static constexpr int BYTES = SPARE_B + 2 * kQm * 4;
   static_assert(BYTES <= 160 * 1024, "LDS");
-  static_assert(32 * D * 2 + 16 * D * 2 < 65536, "DS offsets are 16 bits");
+  static_assert(DO_B + 48 * D * 2 < 65536, "DS offsets are 16 bits");
 };
 
 // s_waitcnt lgkmcnt(N) with the registers of one read group tied to it.
@@ -263,8 +263,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       constexpr int N16 = L::QST_B / 16;
 #pragma unroll
       for (int k = 0; k < N16 / kThreads; ++k) {
-        reinterpret_cast<u32x4*>(smem_raw + L::Q_B + 3 * L::QST_B)[tid + k * kThreads] = z;
-        reinterpret_cast<u32x4*>(smem_raw + L::DO_B + 3 * L::QST_B)[tid + k * kThreads] = z;
+        reinterpret_cast<u32x4*>(smem_raw + 3 * L::STG_B)[tid + k * kThreads] = z;
+        reinterpret_cast<u32x4*>(smem_raw + 3 * L::STG_B + L::DO_B)[tid + k * kThreads] = z;
       }
     }
 
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       for (int k = 0; k < NCP; ++k) {
         const int qc = wave + kWaves * k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rq, (__attribute__((address_space(3))) void*)(smem_raw + L::Q_B + stage * L::QST_B + qc * 1024), 16,
+            rq, (__attribute__((address_space(3))) void*)(smem_raw + stage * L::STG_B + qc * 1024), 16,
             vq + k * kWaves * RW * sq2, 0, 0, 0);
       }
     };
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       for (int k = 0; k < NCP; ++k) {
         const int qc = wave + kWaves * k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ro, (__attribute__((address_space(3))) void*)(smem_raw + L::DO_B + stage * L::QST_B + qc * 1024), 16,
+            ro, (__attribute__((address_space(3))) void*)(smem_raw + stage * L::STG_B + L::DO_B + qc * 1024), 16,
             vo + k * kWaves * RW * so2, 0, 0, 0);
       }
     };
@@ -342,26 +342,24 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
 
     const float c2 = p.scale_log2;
     // LDS byte addresses of this lane's reads. Current tile (stage st):
-    //   cq / co[ss]: Q / dO row n, columns 16ss + 8hf (row block rb: + 32 rows)
+    //   cq[ss]: Q row n, columns 16ss + 8hf (row block rb: + 32 rows; dO: + DO_B)
     //   cl: lse2 of rows 4hf .. +3 (+ 8gg + 32rb; D: + DS_B)
     // previous tile (stage st - 1), transposing reads:
-    //   pq / po[h2][dt]: Q / dO rows 4hf + j16/4 + 8h2 (chunk kc: + 16 rows),
+    //   pq[h2][dt]: Q rows 4hf + j16/4 + 8h2 (chunk kc: + 16 rows; dO: + DO_B),
     //   columns 32dt + 16grp + 4(j16%4)
     const uint32_t lbase = lds_addr(smem_raw);
-    uint32_t cq[NSS], co[NSS], pq[2][NDT], po[2][NDT];
+    uint32_t cq[NSS], pq[2][NDT];
 #pragma unroll
     for (int ss = 0; ss < NSS; ++ss) {
       const uint32_t c = 2 * tile_off<D>(n, 16 * ss + 8 * hf);
-      cq[ss] = lbase + L::Q_B + c;
-      co[ss] = lbase + L::DO_B + c;
+      cq[ss] = lbase + c;
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint32_t c = 2 * tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
-        pq[h2][dt] = lbase + L::Q_B + 3 * L::QST_B + c;
-        po[h2][dt] = lbase + L::DO_B + 3 * L::QST_B + c;
+        pq[h2][dt] = lbase + 3 * L::STG_B + c;
       }
     uint32_t cl = lbase + L::F32_B + 4 * (4 * hf);
 
@@ -378,15 +376,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     // products, (feature tile dt, row chunk kc); product pair X (X < 2 NDT)
     // is (X % NDT, X / NDT) and ((X + 1) % NDT, 2 + X / NDT): two different
     // accumulators. The two transposing reads of one product:
-    auto rd_chunk = [&](u32x2* t, const uint32_t(&base)[2][NDT], auto DTc, auto KCc) __attribute__((always_inline)) {
-      constexpr int dt = decltype(DTc)::value, kc = decltype(KCc)::value;
-      t[0] = tr_read_at<kc * 16 * D * 2>(base[0][dt]);
-      t[1] = tr_read_at<kc * 16 * D * 2>(base[1][dt]);
+    // (TOc: 0 for Q^T, DO_B for dO^T)
+    auto rd_chunk = [&](u32x2* t, auto TOc, auto DTc, auto KCc) __attribute__((always_inline)) {
+      constexpr int to = decltype(TOc)::value, dt = decltype(DTc)::value, kc = decltype(KCc)::value;
+      t[0] = tr_read_at<to + kc * 16 * D * 2>(pq[0][dt]);
+      t[1] = tr_read_at<to + kc * 16 * D * 2>(pq[1][dt]);
     };
-    auto rd_pair = [&](u32x2* t, const uint32_t(&base)[2][NDT], auto Xc) __attribute__((always_inline)) {
+    auto rd_pair = [&](u32x2* t, auto TOc, auto Xc) __attribute__((always_inline)) {
       constexpr int X = decltype(Xc)::value;
-      rd_chunk(t, base, ic<X % NDT>{}, ic<X / NDT>{});
-      rd_chunk(t + 2, base, ic<(X + 1) % NDT>{}, ic<2 + X / NDT>{});
+      rd_chunk(t, TOc, ic<X % NDT>{}, ic<X / NDT>{});
+      rd_chunk(t + 2, TOc, ic<(X + 1) % NDT>{}, ic<2 + X / NDT>{});
     };
     auto mm_chunk = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto DTc, auto KCc) __attribute__((always_inline)) {
       constexpr int dt = decltype(DTc)::value, kc = decltype(KCc)::value;
@@ -408,8 +407,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     auto rd1 = [&](u32x4* r, u32x2* t, auto SSc) __attribute__((always_inline)) {
       constexpr int SS = decltype(SSc)::value;
       r[0] = lds_read16<0>(cq[SS]);
-      r[1] = lds_read16<0>(co[SS]);
-      rd_pair(t, po, SSc);
+      r[1] = lds_read16<L::DO_B>(cq[SS]);
+      rd_pair(t, ic<L::DO_B>{}, SSc);
     };
     rd1(ra0, ta0, ic<0>{});
 
@@ -489,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
           constexpr int SS = decltype(SSc)::value;
           constexpr int sl = SS & 1;
           ra[sl][0] = lds_read16<32 * D * 2>(cq[SS]);
-          ra[sl][1] = lds_read16<32 * D * 2>(co[SS]);
+          ra[sl][1] = lds_read16<L::DO_B + 32 * D * 2>(cq[SS]);
           if constexpr (SS % 2 == 0) {
             rl[(SS / 2) & 1][0] = lds_read16<(SS / 2) * 32>(cl);
             rl[(SS / 2) & 1][1] = lds_read16<L::DS_B + (SS / 2) * 32>(cl);
@@ -540,7 +539,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         auto rd = [&](auto Xc) __attribute__((always_inline)) {
           constexpr int X = decltype(Xc)::value;
           constexpr int sl = X & 1;
-          rd_pair(tq[sl], pq, Xc);
+          rd_pair(tq[sl], ic<0>{}, Xc);
           constexpr int g0 = X * GPX / 2;  // first group of this pair
           if constexpr ((X * GPX) % 2 == 0) {
             rl[g0 & 1][0] = lds_read16<g0 * 32 + 32 * 4>(cl);
@@ -586,20 +585,14 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       wg_barrier();
       // the read addresses move one stage (the previous tile is now t), and
       // the first read group of the next step goes out
-      const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::QST_B : L::QST_B;
-      const int32_t dp = st == 0 ? -(kNst - 1) * L::QST_B : L::QST_B;
+      const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::STG_B : L::STG_B;
+      const int32_t dp = st == 0 ? -(kNst - 1) * L::STG_B : L::STG_B;
 #pragma unroll
-      for (int ss = 0; ss < NSS; ++ss) {
-        cq[ss] += dc;
-        co[ss] += dc;
-      }
+      for (int ss = 0; ss < NSS; ++ss) cq[ss] += dc;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          pq[h2][dt] += dp;
-          po[h2][dt] += dp;
-        }
+        for (int dt = 0; dt < NDT; ++dt) pq[h2][dt] += dp;
       cl += st == kNst - 1 ? -(kNst - 1) * kQm * 4 : kQm * 4;
       st = (st + 1) & (kNst - 1);
       rd1(ra0, ta0, ic<0>{});
@@ -623,11 +616,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ra0[0]), "+v"(ra0[1]), "+v"(ta0[0]), "+v"(ta0[1]), "+v"(ta0[2]),
                    "+v"(ta0[3]));
       unroll<2 * NDT>([&](auto Xc) __attribute__((always_inline)) {
-        rd_pair(t, po, Xc);
+        rd_pair(t, ic<L::DO_B>{}, Xc);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
         mm_first(dv, t, pbp, Xc);
         mm_second(dv, t, pbp, Xc);
-        rd_pair(t, pq, Xc);
+        rd_pair(t, ic<0>{}, Xc);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
         mm_first(dk, t, dsp, Xc);
         mm_second(dk, t, dsp, Xc);
