@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5, 6, 7],
                     help="7: the Blockwise Parallel Transformer layer tail (W_o, LN, FFN, LN) at d_model 4096")
     ap.add_argument("--layout", default=None, help="workloads 3, 5 and 6: contiguous, striped or zigzag")
+    ap.add_argument("--memory", default="original", choices=["blocked", "original"],
+                    help="blocked: Q/K/V/dO resident as [P, B, Bb, H, d], each rank's block contiguous as a "
+                         "device holds it (prepared before the timed region); original: [B, L, H, d] in token "
+                         "order, the blocks read through strides")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the library's layout copy with one block) three "
@@ -398,8 +402,11 @@ def main():
             return torch.from_numpy(x.view(np.int16)).to("cuda").view(torch.bfloat16)
         return torch.from_numpy(x).to("cuda")
 
-    blocked = layout == "zigzag"  # zigzag blocks are not strided slices: keep blocked copies resident
-    if blocked and w.q_ranks:
+    # zigzag blocks are not strided slices of the token order, and a device
+    # holds its block contiguously in any layout: keep blocked copies resident
+    # (the one-device share of workload 4 holds its query rows in local order)
+    blocked = layout == "zigzag" or (args.memory == "blocked" and not w.q_ranks)
+    if layout == "zigzag" and w.q_ranks:
         raise SystemExit("the one-device share is run in the striped layout")
     t = {}
     for n in names:
@@ -410,10 +417,16 @@ def main():
             pos = x * P + rb if layout == "striped" else rb * Bb + x
             pay = np.ascontiguousarray(pay[:, pos])
         if blocked:
-            # blocked order [P, B, Bb, H, d]: block s holds half-blocks s and 2P-1-s
-            hb = Bb // 2
-            perm = np.concatenate([np.r_[s_ * hb:(s_ + 1) * hb, (2 * P - 1 - s_) * hb:(2 * P - s_) * hb]
-                                   for s_ in range(P)])
+            # blocked order [P, B, Bb, H, d]: block s holds tokens s, s + P, ...
+            # (striped), half-blocks s and 2P-1-s (zigzag), or s Bb .. (contiguous)
+            if layout == "zigzag":
+                hb = Bb // 2
+                perm = np.concatenate([np.r_[s_ * hb:(s_ + 1) * hb, (2 * P - 1 - s_) * hb:(2 * P - s_) * hb]
+                                       for s_ in range(P)])
+            elif layout == "striped":
+                perm = np.concatenate([np.arange(s_, P * Bb, P) for s_ in range(P)])
+            else:
+                perm = np.arange(P * Bb)
             pay = np.ascontiguousarray(pay[:, perm].reshape(w.batch, P, Bb, pay.shape[2], d).transpose(1, 0, 2, 3, 4))
         t[n] = dev(pay)
         del pay
@@ -534,7 +547,8 @@ def main():
         "config": {"workload": workload_name(w, layout), "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len, "head_dim": d,
                    "kv_heads": w.kv_heads or w.heads,
                    "ring_size": P, "block_len": Bb, "layout": layout, "causal": w.causal,
-                   "ranks": [rb, re_], "passes": list(w.passes), "prefetch": w.prefetch},
+                   "ranks": [rb, re_], "passes": list(w.passes), "prefetch": w.prefetch,
+                   "memory": "blocked" if blocked else "original"},
         "frac_of_peak": round(value / peak, 4),
         "roofline": roof, "cpu_baseline": cpu, "details": details,
         "device": torch.cuda.get_device_name(0),
