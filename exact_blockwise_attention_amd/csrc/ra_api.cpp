@@ -49,7 +49,8 @@ ra_status check_problem(const ra_problem* pb, int32_t rb, int32_t re) {
   return RA_OK;
 }
 
-constexpr int64_t kMaxTokStride = int64_t(1) << 25;  // elements
+constexpr int64_t kMaxTokStride = int64_t(1) << 25;     // elements
+constexpr int64_t kMaxBwdTokStride = int64_t(1) << 24;  // elements, exclusive
 
 ra_status check_seq(const ra_seq* s, int32_t es) {
   if (!s || !s->ptr) return RA_ERR_NULL;
@@ -272,6 +273,10 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
     if ((st = check_seq(s, es)) != RA_OK) return st;
   if (!lse) return RA_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(lse) % 4) return RA_ERR_ALIGN;
+  // the bf16 dK/dV walk addresses a 64-row query tile of Q and dO through
+  // signed 32-bit byte offsets
+  if (pb->dtype == RA_BF16 && (q->s_tok >= kMaxBwdTokStride || dout->s_tok >= kMaxBwdTokStride))
+    return RA_ERR_UNSUPPORTED;
   const int32_t n = rank_end - rank_begin;
   const BwdWs w = bwd_ws_layout(pb, n);
   if (!workspace || workspace_bytes < w.total) return RA_ERR_WORKSPACE;
@@ -470,8 +475,8 @@ const char* ra_status_string(int32_t status) {
     case RA_ERR_NULL: return "a required pointer is NULL";
     case RA_ERR_SHAPE: return "sizes, ranks, strides or layout out of range";
     case RA_ERR_UNSUPPORTED:
-      return "valid but unsupported configuration (head_dim other than 64 or 128, or a bf16 forward K/V "
-             "token stride above 2^25 elements)";
+      return "valid but unsupported configuration (head_dim other than 64 or 128, a bf16 forward K/V "
+             "token stride above 2^25 elements, or a bf16 backward Q/dO token stride of 2^24 or more)";
     case RA_ERR_WORKSPACE: return "workspace missing or too small";
     case RA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case RA_ERR_HIP: return "HIP runtime call failed";

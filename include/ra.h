@@ -117,7 +117,8 @@ typedef struct {
  * tensors ([P][B][block_len][H][d]: s_blk = B*block_len*H*d, s_batch =
  * block_len*H*d, s_tok = H*d, s_head = d), which ra_layout_copy produces.
  * ptr and every stride times the element size must be multiples of 16 bytes.
- * The bf16 forward needs the K and V token strides at most 2^25 elements
+ * The bf16 forward needs the K and V token strides at most 2^25 elements,
+ * the bf16 backward the Q and dO token strides below 2^24 elements
  * (RA_ERR_UNSUPPORTED otherwise). */
 typedef struct {
   void* ptr;

@@ -181,6 +181,15 @@ def test_backward_validation():
     assert lib.ra_backward(*args(0x100000, need, lse=None)) == 1
     s[6] = None
     assert lib.ra_backward(*args(0x100000, need)) == 1
+    # the bf16 dK/dV walk addresses a 64-row Q / dO tile with 32-bit offsets;
+    # checked before the workspace, so these fail without launching anything
+    for idx in (0, 4):
+        s = [fake_seq() for _ in range(8)]
+        s[idx] = fake_seq(s_tok=1 << 24)
+        assert lib.ra_backward(*args(None, 0)) == 3
+    s = [fake_seq() for _ in range(8)]
+    s[0] = fake_seq(s_tok=(1 << 24) - 8)
+    assert lib.ra_backward(*args(None, 0)) == 4
 
 
 def test_merge_and_layout_copy_validation():
