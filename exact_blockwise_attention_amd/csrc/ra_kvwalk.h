@@ -160,14 +160,6 @@ __device__ __forceinline__ void dma_rows(__bf16* tile, const __bf16* base, int64
   }
 }
 
-// fp32 rows (lse, D) of a query tile: lane l of one wave copies element
-// r_lo + l (clamped to nrows - 1) to tile[l]; 64 elements.
-__device__ __forceinline__ void dma_f32_64(float* tile, const float* base, int32_t r_lo, int32_t nrows, int lane) {
-  int32_t x = r_lo + lane;
-  if (x > nrows - 1) x = nrows - 1;
-  __builtin_amdgcn_global_load_lds(base + x, (__attribute__((address_space(3))) void*)tile, 4, 0, 0);
-}
-
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Waits until at most N vector-memory loads of this wave are outstanding

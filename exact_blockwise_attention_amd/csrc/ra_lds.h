@@ -34,16 +34,9 @@ using ic = std::integral_constant<int, N>;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Row stride (elements) of a [rows][D] bf16 tile.
-template <int D>
-struct PadRow {
-  static constexpr int RS = D;
-};
 
 template <int D>
 __device__ __forceinline__ int chunk_swz(int r) {
@@ -57,21 +50,6 @@ __device__ __forceinline__ int tile_off(int r, int c) {
   return r * D + ((((c >> 3) ^ chunk_swz<D>(r)) << 3) | (c & 7));
 }
 
-// 8-byte unit swizzle for [rows][64] bf16 tiles (128-byte rows) written in
-// 8-byte pieces by 16 lanes on 16 consecutive rows and read by transposing
-// reads on 4 consecutive rows and 4 consecutive units.
-__device__ __forceinline__ int swz8(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-
-__device__ __forceinline__ int tile64_off(int r, int c) {
-  return r * 64 + ((((c >> 2) ^ swz8(r)) << 2) | (c & 3));
-}
-
-__device__ __forceinline__ bf16x4 tr_read(const __bf16* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
-
 // Hides a value from the optimizer so that addresses derived from it are
 // recomputed where they are used instead of being kept live across a loop
 // (the transposing reads take no immediate offset, so every one of them
@@ -79,10 +57,6 @@ __device__ __forceinline__ bf16x4 tr_read(const __bf16* p) {
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
-}
-
-__device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
