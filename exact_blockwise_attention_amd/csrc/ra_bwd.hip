@@ -145,11 +145,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
 
   const int32_t BHk = p.B * p.Hk;
   const int32_t tiles = (int32_t)((p.Bb + kKn - 1) / kKn);
-  const int64_t lw = xcd_logical(blockIdx.x, (int64_t)BHk * p.P * tiles);
-  const int32_t tile = (int32_t)(lw % tiles);
-  const int64_t g = lw / tiles;
-  const int32_t bhk = (int32_t)(g / p.P);
-  const int32_t j = (int32_t)(g % p.P);
+  const uint32_t lw = (uint32_t)xcd_logical(blockIdx.x, (int64_t)BHk * p.P * tiles);
+  // key tiles of a block heaviest first (its first keys are seen by the most
+  // query rows), ordered so that the shader engines get equal work; striped
+  // causal key tiles drift apart at every rank, so there equal turns
+  uint32_t g, wit;
+  if (p.causal && p.layout == kStriped) {
+    turn_balanced_split(lw, (uint32_t)(BHk * p.P), (uint32_t)tiles, &g, &wit);
+  } else {
+    g = lw / (uint32_t)tiles;
+    wit = se_balanced_rank(lw % (uint32_t)tiles, (uint32_t)tiles);
+  }
+  const int32_t tile = (int32_t)wit;
+  const int32_t bhk = (int32_t)(g / (uint32_t)p.P);
+  const int32_t j = (int32_t)(g % (uint32_t)p.P);
   const int32_t b = bhk / p.Hk;
   const int32_t hk = bhk % p.Hk;
   const int32_t Bb = (int32_t)p.Bb;

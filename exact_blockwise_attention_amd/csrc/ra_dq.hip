@@ -44,7 +44,9 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t tiles = (Bb + kQTm - 1) / kQTm;
   int32_t bh, ri, tile;
-  query_work_of(blockIdx.x, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
+  // the tiles of a group share K/V tiles in L2 through the walk's second
+  // pass: keep them together
+  query_work_of(blockIdx.x, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, false, &bh, &ri, &tile);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
   const int32_t hk = h / p.G;  // the K/V head this query head reads

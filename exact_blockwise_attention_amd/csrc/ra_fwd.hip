@@ -96,7 +96,11 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t tiles = (Bb + kQTm - 1) / kQTm;
   int32_t bh, ri, tile;
-  query_work_of(blockIdx.x, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, &bh, &ri, &tile);
+  // striped causal query tiles drift apart at every block: equal turns
+  // (when G is a multiple of 4, the G query heads of a tile already make
+  // every turn's workgroups equal, and the tiles stay together)
+  const bool turns = p.causal && p.layout == kStriped && p.G % 4 != 0;
+  query_work_of(blockIdx.x, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, turns, &bh, &ri, &tile);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
   const int32_t hk = h / p.G;  // the K/V head this query head reads
