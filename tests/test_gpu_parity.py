@@ -72,6 +72,10 @@ SMALL_FWD = [
     Case(164, 1, 4, 400, 64, 4, True, "striped", "f32", Hk=2),
     Case(165, 2, 6, 1024, 128, 2, False, "contiguous", "bf16", Hk=3),
     Case(166, 1, 8, 2048, 128, 2, True, "striped", "bf16", Hk=2),
+    # work orders with partial runs: 9 (head, rank) groups (runs of 4 groups
+    # end short) and 6 query tiles per block (the last run of 4 tiles is cut)
+    Case(167, 1, 3, 4140, 128, 3, True, "striped", "bf16"),
+    Case(168, 1, 3, 4140, 128, 3, True, "zigzag", "bf16"),
 ]
 
 
@@ -220,6 +224,10 @@ SMALL_BWD = [
     Case(158, 1, 2, 600, 128, 4, False, "contiguous", "bf16"),
     Case(159, 1, 2, 344, 64, 4, False, "striped", "bf16", Hk=1),
     Case(160, 1, 4, 1020, 64, 6, True, "zigzag", "bf16", Hk=2),
+    # work orders with partial runs: 9 groups, 6 query tiles and 11 key tiles
+    # per block; and two query heads per K/V head (turns of unequal heads)
+    Case(169, 1, 3, 4140, 128, 3, True, "striped", "bf16"),
+    Case(170, 1, 6, 2100, 64, 3, True, "striped", "bf16", Hk=3),
 ]
 
 
