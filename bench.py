@@ -159,18 +159,60 @@ def hbm_row(ms, nbytes):
     return {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def time_calls(torch, stream, fn, n=5):
+def time_calls(torch, stream, fn, n=5, head_start=False):
     """Average ms of n back-to-back calls, HIP events on the launch stream
-    (after one untimed call)."""
+    (after one untimed call). With head_start the stream first runs a short
+    device-side delay, so the calls are all queued before the first starts."""
     fn()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if head_start:
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(50_000_000)
     a.record(stream)
     for _ in range(n):
         fn()
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n
+
+
+def small_block_sweep(torch, ra, w, sh, stream):
+    """One rank's share on the non-causal 16384-token shape (8 heads of 128)
+    with query blocks of 64, 128 and 256 rows: the rank visits all L / rows
+    ring blocks, so every K/V byte is used by only `rows` query rows (about
+    `rows` flops per byte, below the MFMA/HBM ridge of 2500 / 8 = 312) and the
+    share is bound by reading K and V from HBM. Algorithmic bytes: K and V of
+    the whole sequence, the rank's Q and O rows, and its lse. The library
+    splits the ring steps of such a share into parallel runs merged by
+    log-sum-exp; the unsplit launch (one workgroup per head) is timed beside
+    it. Each rate is the average of back-to-back calls queued behind a
+    device-side delay, so the host's launch rate does not enter it."""
+    B, L, H, d = 1, w.seq_len, w.heads, w.head_dim
+    g = torch.Generator(device="cuda").manual_seed(1000 + w.wid)
+    q, k, v = (torch.randn((B, L, H, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    out = {}
+    for rows in (64, 128, 256):
+        P = L // rows
+        pb = ra.make_problem(B, H, d, P, rows, "contiguous", False, ra.BF16)
+        need = ra.workspace_bytes(pb, 0, 1, False, False)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+        o = torch.empty((B, rows, H, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((1, B, H, rows), dtype=torch.float32, device="cuda")
+        qs = ra.Seq(q.data_ptr(), rows * H * d, L * H * d, H * d, d)
+        os_ = ra.Seq(o.data_ptr(), rows * H * d, rows * H * d, H * d, d)
+        ks = ra.Seq(k.data_ptr(), rows * H * d, L * H * d, H * d, d)
+        vs = ra.Seq(v.data_ptr(), rows * H * d, L * H * d, H * d, d)
+        nbytes = 2 * L * H * d * 2 + 2 * rows * H * d * 2 + rows * H * 4
+        row = {"ring_size": P}
+        for label, wsp, wsb in (("split", ws.data_ptr(), need), ("unsplit", None, 0)):
+            ms = time_calls(torch, stream, lambda: ra.forward_raw(pb, 0, 1, qs, ks, vs, os_, lse.data_ptr(), wsp, wsb,
+                                                                  sh, None), n=50, head_start=True)
+            row[label] = {**hbm_row(ms, nbytes), "TFLOP/s": round(4 * d * rows * L * H / ms / 1e9, 2)}
+        row["split_workspace_bytes"] = need
+        out[f"q_rows_{rows}"] = row
+        del ws, o, lse
+    return out
 
 
 def memory_rows(torch, ra, w, q, sh, stream):
@@ -532,6 +574,8 @@ def main():
         pre_bytes = len(ranks) * B_ * H_ * Bb * (2 * d_ * t["q"].element_size() + 4)
         details["memory_rows"] = {"B1_rowsum_dO_O": hbm_row(details["bwd_pre_ms"], pre_bytes),
                                   **memory_rows(torch, ra, w, t["q"], sh, stream)}
+    if w.wid == 2:
+        details["small_block_sweep"] = small_block_sweep(torch, ra, w, sh, stream)
     if w.wid == 3:
         details["balance"] = balance_report(torch, ra, w, layout, t, pb, blocked, o, lse, sh, stream)
     if w.prefetch:

@@ -270,7 +270,8 @@ def make_problem(B, H, d, P, Bb, layout, causal, dtype_code, scale=None, kv_head
 
 
 def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causal: bool = False,
-                      scale=None, rank_range=None, copy_stream=None, out=None, lse=None, workspace=None):
+                      scale=None, rank_range=None, copy_stream=None, out=None, lse=None, workspace=None,
+                      split=True):
     """Blockwise ring attention forward on original-order [B, L, H, d] tensors.
 
     k, v: the whole sequence, [B, L, Hk, d] with Hk dividing H (query head h
@@ -279,7 +280,11 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     written) or just those ranks' rows ([B, nr*Bb, H, d], each rank's block
     contiguous in its local row order). Returns (o, lse) with lse fp32
     [nr, B, H, Bb] in local row order. A non-None ``copy_stream`` selects the
-    double-buffered receive mode (single rank).
+    double-buffered receive mode (single rank). Without it, a single rank
+    whose query tiles cannot fill the GPU runs its ring steps as parallel runs
+    merged by log-sum-exp (the library does so when it is given the workspace
+    ra_workspace_bytes asks for); ``split=False`` passes no workspace, so the
+    whole ring runs in one unsplit launch.
     """
     torch = _torch()
     B, L, Hk, d = k.shape
@@ -295,7 +300,7 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     if lse is None:
         lse = torch.empty((nr, B, H, Bb), dtype=torch.float32, device=q.device)
     use_copy = copy_stream is not None
-    need = workspace_bytes(pb, rb, re, use_copy, False)
+    need = workspace_bytes(pb, rb, re, use_copy, False) if (split or use_copy) else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     keep = []

@@ -69,11 +69,37 @@ float eff_scale(const ra_problem* pb) {
 
 struct FwdWs {
   size_t kbuf[2], vbuf[2], st_o, st_lse, total;
+  int32_t n_split;  // runs of ring steps of a split launch (1: not split)
 };
+
+// One rank's share whose query tiles (256 rows per workgroup) cannot fill the
+// chip's 256 CUs runs its P ring steps as this many parallel runs, merged by
+// log-sum-exp: enough runs for one workgroup per CU (the forward holds one
+// per CU), at most P. More runs, in two rounds, measured slower: each run
+// pays its start-up and its partial state's write and merge.
+int32_t split_runs(const ra_problem* pb, int32_t n_ranks) {
+  if (pb->dtype != RA_BF16 || n_ranks != 1 || pb->ring_size < 2) return 1;
+  const int64_t tiles = (pb->block_len + 255) / 256;
+  const int64_t base = (int64_t)n_ranks * pb->batch * pb->heads * tiles;
+  if (base >= 256) return 1;
+  const int64_t want = (256 + base - 1) / base;
+  return (int32_t)(want < pb->ring_size ? want : pb->ring_size);
+}
 
 FwdWs fwd_ws_layout(const ra_problem* pb, int32_t n_ranks, int32_t copy) {
   FwdWs w{};
-  if (!copy) return w;
+  w.n_split = 1;
+  if (!copy) {
+    // split launch: n_split partial states (fp32 O and lse per query row)
+    const int32_t ns = split_runs(pb, n_ranks);
+    if (ns < 2) return w;
+    const size_t rows = (size_t)ns * n_ranks * pb->batch * pb->heads * pb->block_len;
+    w.n_split = ns;
+    w.st_o = 0;
+    w.st_lse = align_up(rows * pb->head_dim * sizeof(float));
+    w.total = align_up(w.st_lse + rows * sizeof(float));
+    return w;
+  }
   const size_t es = elem_bytes(pb->dtype);
   const size_t blk = (size_t)pb->batch * pb->block_len * kv_heads_of(pb) * pb->head_dim * es;
   const size_t rows = (size_t)n_ranks * pb->batch * pb->heads * pb->block_len;
@@ -172,7 +198,10 @@ ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
   const bool use_copy = copy != nullptr;
   if (use_copy && n != 1) return RA_ERR_SHAPE;
   const FwdWs w = fwd_ws_layout(pb, n, use_copy ? 1 : 0);
-  if (w.total > 0) {
+  // without the copy stream the workspace is optional: it enables the split
+  // launch, and a call without it runs the whole ring in one unsplit launch
+  const bool split = !use_copy && w.n_split > 1 && workspace && workspace_bytes >= w.total;
+  if (use_copy || split) {
     if (!workspace || workspace_bytes < w.total) return RA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return RA_ERR_ALIGN;
   }
@@ -199,6 +228,19 @@ ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
     return pb->dtype == RA_BF16 ? ra::launch_fwd_bf16(pp, compute) : ra::launch_fwd_f32(pp, compute);
   };
 
+  if (split) {
+    // the runs' partial states, then their log-sum-exp merge into O and lse
+    char* ws = reinterpret_cast<char*>(workspace);
+    p.mode = 2;
+    p.n_split = w.n_split;
+    p.first = 1;
+    p.last = 0;
+    p.st_o = reinterpret_cast<float*>(ws + w.st_o);
+    p.st_lse = reinterpret_cast<float*>(ws + w.st_lse);
+    RA_HIP(launch(p));
+    RA_HIP(ra::launch_merge_splits(p, compute));
+    return RA_OK;
+  }
   if (!use_copy) {
     p.mode = 0;
     RA_HIP(launch(p));

@@ -100,7 +100,11 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   // (when G is a multiple of 4, the G query heads of a tile already make
   // every turn's workgroups equal, and the tiles stay together)
   const bool turns = p.causal && p.layout == kStriped && p.G % 4 != 0;
-  query_work_of(blockIdx.x, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, turns, &bh, &ri, &tile);
+  // split launch: workgroup id = run * (query tiles of the range) + tile id
+  const int64_t per_run = (int64_t)BH * p.n_ranks * tiles;
+  const int32_t run = (p.mode == 2) ? (int32_t)(blockIdx.x / per_run) : 0;
+  const int64_t wid = (p.mode == 2) ? (int64_t)(blockIdx.x % per_run) : (int64_t)blockIdx.x;
+  query_work_of(wid, BH, p.G, p.n_ranks, tiles, p.causal, p.layout, turns, &bh, &ri, &tile);
   const int32_t b = bh / p.H;
   const int32_t h = bh % p.H;
   const int32_t hk = h / p.G;  // the K/V head this query head reads
@@ -125,6 +129,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   f32x16 acc[D / 32];
   float m, l;
   const int64_t srow = (((int64_t)ri * p.B + b) * p.H + h) * p.Bb;  // state / lse row base
+  // state slot of this workgroup's run (split launch), in rows
+  const int64_t slot = (p.mode == 2) ? (int64_t)run * p.n_ranks * BH * p.Bb : 0;
   if (p.mode == 1 && !p.first) {
     m = (a < Bb) ? p.st_lse[srow + a] : -INFINITY;
     l = (hf == 0) ? 1.0f : 0.0f;
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     dk[kc] = (uint32_t)(2 * ((int64_t)row * p.k.s_tok + 8 * c));
     dv[kc] = (uint32_t)(2 * ((int64_t)row * p.v.s_tok + 8 * c));
   }
-  const int64_t kvblk_mul = (p.mode == 0) ? 1 : 0;  // the single-step buffer holds one block
+  const int64_t kvblk_mul = (p.mode == 1) ? 0 : 1;  // the single-step buffer holds one block
   auto kv_base = [&](const Seq& sq, int32_t blk, int32_t r_lo) __attribute__((always_inline)) {
     return reinterpret_cast<const char*>(reinterpret_cast<const __bf16*>(sq.ptr) + kvblk_mul * blk * sq.s_blk +
                                          b * sq.s_batch + hk * sq.s_head + (int64_t)r_lo * sq.s_tok);
@@ -323,9 +329,10 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   };
 
   KvIter first;
-  first.kstep = -1;
-  first.nsteps = (p.mode == 0) ? p.P : 1;
-  first.single_block = (p.mode == 0) ? -1 : p.step_block;
+  // ring steps walked: all, one received block, or this run's steps
+  first.kstep = (p.mode == 2) ? (int32_t)((int64_t)run * p.P / p.n_split) - 1 : -1;
+  first.nsteps = (p.mode == 0) ? p.P : (p.mode == 1) ? 1 : (int32_t)((int64_t)(run + 1) * p.P / p.n_split);
+  first.single_block = (p.mode == 1) ? p.step_block : -1;
   first.i = i;
   first.P = p.P;
   first.layout = p.layout;
@@ -361,9 +368,14 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       wait_vm<2 * DM::NI>();
     }
     wg_barrier();
+    // a wave whose rows all lie past the block's end (a block shorter than
+    // the workgroup's 256 rows) keeps to the copies and barriers only
+    const bool busy = aw < Bb;
     KvIter its = first;  // the tile whose scores are in s
-    scores(ic<0>{});
-    softmax(its);
+    if (busy) {
+      scores(ic<0>{});
+      softmax(its);
+    }
     if (g1) {
       wait_vm<2 * DM::NI>();  // tile 1: group 0 reads it in the next phase
       wg_barrier();
@@ -380,7 +392,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
         dma(itd, ic<(U + 3) % 4>{});  // tile t+3 into the stage tile t-1 freed
         dadv();
       }
-      matrix(ic<(U + 1) % 4>{}, ic<U>{}, has_next);
+      if (busy) matrix(ic<(U + 1) % 4>{}, ic<U>{}, has_next);
       if (g1) wait_vm<DM::NI>();  // tile t+2, read by group 0 in the next phase
       wg_barrier();
       if (g1) {
@@ -389,7 +401,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       }
       if (has_next) {
         its = nx;
-        softmax(its);
+        if (busy) softmax(its);
       }
       return has_next;
     };
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const float m_use = (m == -INFINITY) ? 0.0f : m;
   const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
   if (a >= Bb) return;
-  if (p.mode == 0 || p.last) {
+  if (p.mode == 0 || (p.mode == 1 && p.last)) {
     __bf16* orow = reinterpret_cast<__bf16*>(p.o.ptr) + ri * p.o.s_blk + b * p.o.s_batch +
                    (int64_t)a * p.o.s_tok + h * p.o.s_head;
 #pragma unroll
@@ -424,9 +436,9 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       for (int g4 = 0; g4 < 4; ++g4) {
         const float4 v4 = make_float4(acc[dt][4 * g4] * inv, acc[dt][4 * g4 + 1] * inv,
                                       acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv);
-        *reinterpret_cast<float4*>(p.st_o + (srow + a) * D + 32 * dt + 8 * g4 + 4 * hf) = v4;
+        *reinterpret_cast<float4*>(p.st_o + (slot + srow + a) * D + 32 * dt + 8 * g4 + 4 * hf) = v4;
       }
-    if (hf == 0) p.st_lse[srow + a] = (l_tot > 0.0f) ? m_use + log2f(l_tot) : -INFINITY;
+    if (hf == 0) p.st_lse[slot + srow + a] = (l_tot > 0.0f) ? m_use + log2f(l_tot) : -INFINITY;
   }
 }
 
@@ -552,7 +564,7 @@ __global__ __launch_bounds__(kF32Rows) void fwd_f32_kernel(FwdParams p) {
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
   const int64_t tiles = (p.Bb + kQTm - 1) / kQTm;
-  const int64_t grid = tiles * p.n_ranks * p.B * p.H;
+  const int64_t grid = tiles * p.n_ranks * p.B * p.H * (p.mode == 2 ? p.n_split : 1);
   if (grid <= 0) return hipSuccess;
   if (p.D == 128) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(fwd_bf16_kernel<128>),

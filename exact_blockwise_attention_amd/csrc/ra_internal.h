@@ -18,7 +18,11 @@ struct Seq {
 // Forward launch. mode 0: every rank in [rank_begin, rank_begin + n_ranks)
 // walks the whole ring inside one launch. mode 1: one ring step (block
 // step_block) for a single rank, K/V read from a received buffer; the running
-// state enters from / leaves to (st_o, st_lse) unless first / last.
+// state enters from / leaves to (st_o, st_lse) unless first / last. mode 2:
+// the ring steps of every rank in range are cut into n_split contiguous runs
+// (run s: steps s*P/n_split .. (s+1)*P/n_split - 1), one workgroup per (run,
+// query tile), K/V read in place; run s leaves its partial state in slot s of
+// (st_o, st_lse), and merge_splits combines the slots.
 struct FwdParams {
   Seq q, k, v, o;
   float* lse;      // [n_ranks][B][H][Bb], natural log
@@ -31,6 +35,7 @@ struct FwdParams {
   float scale_log2;  // scale * log2(e)
   int32_t rank_begin, n_ranks;
   int32_t mode, step_block, first, last;
+  int32_t n_split;  // mode 2: runs of ring steps per rank
 };
 
 // Backward launches (whole ring for ranks in range).
@@ -69,6 +74,7 @@ hipError_t launch_layer_norm(const float* in, int64_t rows, int32_t d, const flo
                              float eps, __bf16* out, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
+hipError_t launch_merge_splits(const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_preprocess(const BwdParams& p, int32_t bf16, hipStream_t s);
 hipError_t launch_dkdv_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_dkdv_f32(const BwdParams& p, hipStream_t s);

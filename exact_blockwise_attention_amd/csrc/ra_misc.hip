@@ -48,6 +48,52 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(int64_t rows, int32_t d,
   if (lane == 0) lo[row] = (tot > 0.0f) ? ms + logf(tot) : -INFINITY;
 }
 
+// Combines the partial states of the n_split runs of ring steps of a split
+// forward launch into O (bf16) and lse (natural log): the same log-sum-exp
+// correction as merge_lse_kernel, over n_split partials. Partial s of row r
+// is the normalised O at st_o[(s * rows + r) * D] and its lse in log2 units
+// at st_lse[s * rows + r]; a run that saw no key has lse -inf and weight 0.
+// D / 4 lanes per row, four features each. Row r = ((ri * B + b) * H + h) *
+// Bb + a.
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits_kernel(FwdParams p) {
+  constexpr int LPR = D / 4;
+  const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
+  const int64_t r = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int e = 4 * (threadIdx.x % LPR);
+  if (r >= rows) return;
+  // unrolled so that many partials' loads are in flight at once (the grid
+  // is small: a few hundred rows)
+  float mx = -INFINITY;
+#pragma unroll 16
+  for (int32_t s = 0; s < p.n_split; ++s) mx = fmaxf(mx, p.st_lse[s * rows + r]);
+  const float ms = (mx == -INFINITY) ? 0.0f : mx;
+  float tot = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+  for (int32_t s = 0; s < p.n_split; ++s) {
+    const float w = exp2f(p.st_lse[s * rows + r] - ms);
+    const float4 u = *reinterpret_cast<const float4*>(p.st_o + (s * rows + r) * D + e);
+    tot += w;
+    acc.x += w * u.x;
+    acc.y += w * u.y;
+    acc.z += w * u.z;
+    acc.w += w * u.w;
+  }
+  const float inv = (tot > 0.0f) ? 1.0f / tot : 0.0f;
+  const int32_t a = (int32_t)(r % p.Bb);
+  const int64_t t = r / p.Bb;
+  const int32_t h = (int32_t)(t % p.H);
+  const int32_t b = (int32_t)((t / p.H) % p.B);
+  const int32_t ri = (int32_t)(t / p.H / p.B);
+  __bf16* orow = reinterpret_cast<__bf16*>(p.o.ptr) + ri * p.o.s_blk + b * p.o.s_batch + (int64_t)a * p.o.s_tok +
+                 h * p.o.s_head;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 w4 = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
+  *reinterpret_cast<bf16x4*>(orow + e) = w4;
+  if (e == 0) p.lse[r] = (tot > 0.0f) ? (ms + log2f(tot)) * 0.69314718055994530942f : -INFINITY;
+}
+
 // Copies 16-byte chunks of one ring block of a strided sequence tensor into
 // a dense [B][Bb][H][D] buffer (the stand-in for a ring receive).
 __global__ __launch_bounds__(256) void gather_block_kernel(const char* src, int64_t s_blk,
@@ -160,6 +206,18 @@ hipError_t launch_merge_lse(int64_t rows, int32_t d, const float* oa, const floa
   if (rows <= 0) return hipSuccess;
   const int64_t grid = (rows + 3) / 4;
   hipLaunchKernelGGL(merge_lse_kernel, dim3((uint32_t)grid), dim3(256), 0, s, rows, d, oa, la, ob, lb, oo, lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_splits(const FwdParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
+  if (rows <= 0) return hipSuccess;
+  const int64_t per_block = 256 / (p.D / 4);
+  const int64_t grid = (rows + per_block - 1) / per_block;
+  if (p.D == 128)
+    hipLaunchKernelGGL(merge_splits_kernel<128>, dim3((uint32_t)grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(merge_splits_kernel<64>, dim3((uint32_t)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

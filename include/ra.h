@@ -130,8 +130,10 @@ typedef struct {
 
 /* Bytes of workspace ra_forward (backward = 0) or ra_backward (backward = 1)
  * needs for ranks [rank_begin, rank_end). use_copy_stream selects the
- * forward's double-buffered receive mode. Returns 0 for an invalid problem
- * (and when no workspace is needed). */
+ * forward's double-buffered receive mode. Without it, a bf16 forward of a
+ * single rank whose query block is too small to fill the GPU asks for the
+ * partial states of its split launch (see ra_forward). Returns 0 for an
+ * invalid problem (and when no workspace is needed). */
 size_t ra_workspace_bytes(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
                           int32_t use_copy_stream, int32_t backward);
 
@@ -148,7 +150,15 @@ size_t ra_workspace_bytes(const ra_problem* pb, int32_t rank_begin, int32_t rank
  *          KV block is gathered into a double buffer on `copy` while the
  *          previous step computes on `compute` (events order both hazards);
  *          the running state is merged between steps by log-sum-exp.
- *   workspace: ra_workspace_bytes(pb, rb, re, copy != NULL, 0) bytes. */
+ *   workspace: ra_workspace_bytes(pb, rb, re, copy != NULL, 0) bytes.
+ *          With copy = NULL it is optional. Given, and when the problem is
+ *          bf16 with a single rank whose 256-row query tiles number fewer
+ *          than 256 (one device's share with a short query block), the P ring
+ *          steps are cut into contiguous runs computed in parallel, each
+ *          leaving a partial (O, lse) in the workspace, and the partials are
+ *          merged by log-sum-exp (the blog's online-softmax correction, as in
+ *          ra_merge_lse). Without it, the same share runs in one launch, one
+ *          workgroup per query tile. The two agree within rounding. */
 ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
                      const ra_seq* q, const ra_seq* k, const ra_seq* v, const ra_seq* o,
                      float* lse, void* workspace, size_t workspace_bytes,

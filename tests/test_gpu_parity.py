@@ -28,10 +28,10 @@ def gpu():
     ra.library()  # the HIP library must load; there is no fallback
 
 
-def run_fwd(case, dev, rank_range=None, copy=False):
+def run_fwd(case, dev, rank_range=None, copy=False, split=True):
     stream = torch.cuda.Stream() if copy else None
     o, lse = ra.attention_forward(dev["q"], dev["k"], dev["v"], case.P, case.layout, case.causal,
-                                  rank_range=rank_range, copy_stream=stream)
+                                  rank_range=rank_range, copy_stream=stream, split=split)
     torch.cuda.synchronize()
     return o, lse
 
@@ -132,10 +132,51 @@ def test_forward_is_deterministic_and_grid_independent():
     o1, l1 = run_fwd(case, dev)
     o2, l2 = run_fwd(case, dev)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
-    o3, l3 = run_fwd(case, dev, rank_range=(2, 3))
+    o3, l3 = run_fwd(case, dev, rank_range=(2, 3), split=False)
     pos = rank_positions(case, [2])[0]
     assert torch.equal(o1[:, pos].view(torch.int16), o3[:, pos].view(torch.int16))
     assert torch.equal(l1[2], l3[0])
+
+
+SPLIT_CASES = [
+    # one rank's share with a small query block: its ring steps run as
+    # parallel runs merged by log-sum-exp. Runs of 1, 2 and 3 ring steps,
+    # ragged and one-tile blocks, every layout, grouped-query heads
+    Case(171, 1, 2, 1024, 128, 8, True, "striped", "bf16"),
+    Case(172, 1, 2, 1040, 128, 8, True, "contiguous", "bf16"),
+    Case(173, 1, 4, 1200, 128, 6, True, "zigzag", "bf16", Hk=2),
+    Case(174, 2, 3, 1500, 64, 5, False, "contiguous", "bf16"),
+    Case(175, 1, 8, 16384, 128, 64, False, "contiguous", "bf16"),   # 256-row blocks, 64 steps
+    Case(176, 1, 8, 16384, 128, 256, True, "striped", "bf16", Hk=1),  # 64-row blocks, 256 steps
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=str)
+def test_forward_single_rank_split_runs(case):
+    """A single rank's share, split into runs of ring steps and merged,
+    against the oracle and against the same share in one unsplit launch."""
+    pb = ra.make_problem(case.B, case.H, case.d, case.P, case.Bb, case.layout, case.causal, 1, None,
+                         kv_heads=case.kv_heads)
+    assert ra.workspace_bytes(pb, 0, 1, False, False) > 0, "the share should be split"
+    p = payloads(case)
+    dev = {n: to_device(x) for n, x in p.items()}
+    q64, k64, v64 = (syn_f64(p[n]) for n in "qkv")
+    for r in sorted({0, 1, case.P // 2, case.P - 1}):
+        log(f"split single rank {r}: {case}")
+        # the oracle on this rank's query rows, at their token positions
+        pr = rank_positions(case, [r])[0]
+        ref_o, ref_lse = oracle.attention_fwd(q64[:, pr], k64, v64, case.causal, q_pos=pr)
+        outs = []
+        for split in (True, False):
+            o, lse = run_fwd(case, dev, rank_range=(r, r + 1), split=split)
+            _, lv = lse_to_original(case, lse, [r])
+            assert_output_close("O", to_f64(o)[:, pr], ref_o, case.dtype, case)
+            assert_close("lse", lv, ref_lse, TOL[case.dtype], case)
+            outs.append((o[:, pr].float(), lse))
+        # the two launches round the bf16 probabilities against different
+        # running maxima, so they agree to the same bar, not bitwise
+        assert float((outs[0][0] - outs[1][0]).abs().max()) <= TOL[case.dtype]
+        assert float((outs[0][1] - outs[1][1]).abs().max()) <= TOL[case.dtype]
 
 
 def test_layout_copy_is_bit_exact():
