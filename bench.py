@@ -187,8 +187,12 @@ def small_block_sweep(torch, ra, w, sh, stream):
     splits the ring steps of such a share into parallel runs merged by
     log-sum-exp; the unsplit launch (one workgroup per head) is timed beside
     it. Each rate is the average of back-to-back calls queued behind a
-    device-side delay, so the host's launch rate does not enter it."""
+    device-side delay, so the host's launch rate does not enter it. Those
+    calls run warm: K and V (64 MiB) stay in the 256 MB last-level cache
+    (MALL) between calls. `split_cold` is the median of single calls each
+    preceded by a 512 MiB write that evicts them."""
     B, L, H, d = 1, w.seq_len, w.heads, w.head_dim
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     g = torch.Generator(device="cuda").manual_seed(1000 + w.wid)
     q, k, v = (torch.randn((B, L, H, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
     out = {}
@@ -206,13 +210,33 @@ def small_block_sweep(torch, ra, w, sh, stream):
         nbytes = 2 * L * H * d * 2 + 2 * rows * H * d * 2 + rows * H * 4
         row = {"ring_size": P}
         for label, wsp, wsb in (("split", ws.data_ptr(), need), ("unsplit", None, 0)):
-            ms = time_calls(torch, stream, lambda: ra.forward_raw(pb, 0, 1, qs, ks, vs, os_, lse.data_ptr(), wsp, wsb,
-                                                                  sh, None), n=50, head_start=True)
+            call = lambda: ra.forward_raw(pb, 0, 1, qs, ks, vs, os_, lse.data_ptr(), wsp, wsb, sh, None)  # noqa: E731
+            ms = time_calls(torch, stream, call, n=50, head_start=True)
             row[label] = {**hbm_row(ms, nbytes), "TFLOP/s": round(4 * d * rows * L * H / ms / 1e9, 2)}
+            if label == "split":
+                ms = cold_call_ms(torch, stream, call, flush)
+                row["split_cold"] = {**hbm_row(ms, nbytes), "TFLOP/s": round(4 * d * rows * L * H / ms / 1e9, 2)}
         row["split_workspace_bytes"] = need
         out[f"q_rows_{rows}"] = row
         del ws, o, lse
+    del flush
     return out
+
+
+def cold_call_ms(torch, stream, fn, flush, n=20):
+    """Median ms of single calls, each after writing `flush` (larger than the
+    last-level cache) on the same stream, HIP events around the call only."""
+    fn()
+    times = []
+    for _ in range(n):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    return sorted(times)[n // 2]
 
 
 def memory_rows(torch, ra, w, q, sh, stream):
