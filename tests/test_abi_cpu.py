@@ -89,6 +89,27 @@ def test_invalid_problem_fields(field, value, code):
     assert fwd_status(pb) == code
 
 
+def test_split_launch_workspace():
+    """One rank whose query tiles (256 rows) number fewer than 256 asks for
+    the partial states of its split launch: S = min(P, ceil(256 / tiles))
+    runs, each an fp32 O and lse per query row (256-byte aligned parts)."""
+    def align(x):
+        return (x + 255) // 256 * 256
+    pb = problem(d=128, P=256, Bb=64, H=8, causal=False, layout="contiguous")
+    rows = 32 * 8 * 64  # 32 runs of the rank's 8 x 64 rows
+    assert ra.workspace_bytes(pb, 5, 6, False, False) == align(rows * 128 * 4) + align(rows * 4)
+    pb3 = problem(d=64, P=3, Bb=300, H=2)  # 2 query tiles per head: 4 tiles, 3 runs (all P steps)
+    rows3 = 3 * 2 * 300
+    assert ra.workspace_bytes(pb3, 2, 3, False, False) == align(rows3 * 64 * 4) + align(rows3 * 4)
+    assert ra.workspace_bytes(pb, 0, 2, False, False) == 0  # more than one rank: one launch
+    assert ra.workspace_bytes(problem(d=128, P=256, Bb=64, H=8, dtype_code=ra.F32), 0, 1, False, False) == 0
+    assert ra.workspace_bytes(problem(d=128, P=1, Bb=64, H=8), 0, 1, False, False) == 0
+    assert ra.workspace_bytes(problem(d=128, P=8, Bb=4096, H=32), 7, 8, False, False) == 0  # fills the GPU
+    # a split-sized workspace must be aligned; checked before anything is launched
+    need = ra.workspace_bytes(pb3, 2, 3, False, False)
+    assert fwd_status(pb3, 2, 3, ws=0x40010, ws_bytes=need) == 5  # RA_ERR_ALIGN
+
+
 def test_grouped_query_heads():
     # K/V heads must divide the query heads; the receive buffers of the
     # single-rank forward hold K/V blocks with the K/V head count
