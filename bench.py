@@ -339,8 +339,10 @@ def cpu_baseline(w):
             del pay
         L = w.seq_len
         t0 = time.perf_counter()
-        oracle.attention_bwd(t["q"], t["k"], t["v"], t["do"], True)  # runs the forward inside
+        dq_r, dk_r, dv_r, o_r, lse_r = oracle.attention_bwd(t["q"], t["k"], t["v"], t["do"], True)  # runs the forward inside
         dt = time.perf_counter() - t0
+        ref = {"heads": heads, "kv_heads": [0] if G > 1 else heads,
+               "O": o_r, "lse": lse_r, "dQ": dq_r, "dK": dk_r, "dV": dv_r}
         flops = len(heads) * L * (L + 1) // 2 * (4 + 10) * d
         which = f"heads 0 and {w.heads - 1} of {w.heads}" if G == 1 else \
             f"query heads 0..{G - 1} of {w.heads} (the ones sharing K/V head 0)"
@@ -356,8 +358,151 @@ def cpu_baseline(w):
         pairs = Ls * (Ls + 1) // 2 if w.causal else Ls * Ls
         flops = pairs * 4 * d
         sample = f"one head, first {Ls} tokens, forward"
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}
+        ref = None  # a stand-alone sample, not the workload's own tensors
+    rec = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+           "sample": sample, "seconds": round(dt, 3), "cpu_model": cpu_model()}
+    return rec, ref
+
+
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+BAND = 4.0  # below it a bf16 output meets the plain bar; above it, plus its own rounding
+
+
+def half_bf16_spacing(x):
+    import numpy as np
+    ax = np.abs(x)
+    _, e = np.frexp(ax)
+    return np.where(ax > 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def parity_report(torch, ra, w, layout, blocked, outs, ref):
+    """The timed run's last outputs against the oracle results the CPU
+    baseline computed (same tensors, the oracle's head subset): max |GPU -
+    oracle| per output, max |oracle|, and whether every element meets the
+    bar (2e-2 for bf16 inputs: plainly below |ref| = 4, plus the output's
+    own bf16 rounding at and above it; 1e-4 for fp32)."""
+    import numpy as np
+    P, Bb = w.ring_size, w.block_len
+    tol = 2e-2 if w.dtype == "bf16" else 1e-4
+
+    def original(x):  # a [B, L, H, d] device tensor in token order
+        return ra.layout_copy(x, P, layout, inverse=True) if blocked else x
+
+    def f64(x):
+        return x.float().cpu().numpy().astype(np.float64)
+
+    got = {}
+    hq, hk = ref["heads"], ref["kv_heads"]
+    for name, key, hs in (("O", "o", hq), ("dQ", "dq", hq), ("dK", "dk", hk), ("dV", "dv", hk)):
+        got[name] = f64(original(outs[key])[:, :, hs])
+    lse = outs["lse"].cpu().numpy().astype(np.float64)  # [P, B, H, Bb], local row order
+    x = np.arange(Bb)
+    if layout == "striped":
+        pos = np.concatenate([x * P + i for i in range(P)])
+    elif layout == "zigzag":
+        h = Bb // 2
+        pos = np.concatenate([np.where(x < h, i * h + x, (2 * P - 1 - i) * h + (x - h)) for i in range(P)])
+    else:
+        pos = np.concatenate([i * Bb + x for i in range(P)])
+    flat = lse.transpose(1, 0, 3, 2).reshape(w.batch, P * Bb, w.heads)[:, :, hq]
+    tok = np.empty_like(flat)
+    tok[:, pos] = flat
+    got["lse"] = tok
+    err, val, ok = {}, {}, True
+    for name in ("O", "lse", "dQ", "dK", "dV"):
+        e = np.abs(got[name] - ref[name])
+        r = np.abs(ref[name])
+        err[name] = float(e.max())
+        val[name] = float(r.max())
+        if name == "lse" or w.dtype != "bf16":
+            ok = ok and err[name] <= tol
+        else:
+            band = r >= BAND
+            ok = ok and float(e[~band].max(initial=0.0)) <= tol
+            if band.any():
+                mag = np.maximum(np.abs(got[name][band]), r[band] + tol)
+                ok = ok and float((e[band] - half_bf16_spacing(mag)).max()) <= tol
+    return {"max_abs_err": {k: float(f"{v:.4g}") for k, v in err.items()},
+            "max_abs_val": {k: float(f"{v:.4g}") for k, v in val.items()},
+            "bar": tol, "within_bar": bool(ok), "heads": hq, "rows": "all"}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi) on a host thread while the
+    timed steps run; reports the median in MHz, or None where amdsmi or the
+    device's handle is not available."""
+
+    def __init__(self, torch):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            bus = None
+            try:
+                pr = torch.cuda.get_device_properties(0)
+                bus = (int(pr.pci_domain_id), int(pr.pci_bus_id), int(pr.pci_device_id))
+            except Exception:  # noqa: BLE001
+                pass
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, b, rest = bdf.split(":")
+                if bus is not None and (int(dom, 16), int(b, 16), int(rest.split(".")[0], 16)) == bus:
+                    self._handle = h
+            if self._handle is None and len(handles) == 1:
+                self._handle = handles[0]
+            self._amdsmi = amdsmi
+        except Exception:  # noqa: BLE001
+            self._handle = None
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if clks:
+            return sum(clks) / len(clks)
+        c = m.get("current_gfxclk") or m.get("average_gfxclk_frequency")
+        return float(c) if isinstance(c, (int, float)) and 0 < c < 10000 else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v:
+                    self.samples.append(v)
+            except Exception:  # noqa: BLE001
+                return
+            self._stop.wait(0.005)
+
+    def start(self):
+        if self._handle is not None:
+            import threading
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=2)
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"median_mhz": round(v[len(v) // 2], 1), "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1),
+                "samples": len(v), "source": "amdsmi gpu metrics (current gfx clock), sampled during the timed steps"}
 
 
 def bench_bpt(args):
@@ -551,12 +696,15 @@ def main():
     torch.cuda.synchronize()
     timing = {"f0": [], "f1": [], "b0": [], "b1": [], "b2": []}
     start, stop = ev(), ev()
+    clock = ClockSampler(torch)
     torch.cuda.synchronize()
+    clock.start()
     start.record(stream)
     for _ in range(args.steps):
         step(timing)
     stop.record(stream)
     torch.cuda.synchronize()
+    sclk = clock.stop()
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
 
@@ -604,7 +752,11 @@ def main():
         details["balance"] = balance_report(torch, ra, w, layout, t, pb, blocked, o, lse, sh, stream)
     if w.prefetch:
         details["receive_overlap"] = receive_overlap(torch, ra, w, t, pb, rb, re_, so, sk, o, lse, sh, stream, ms)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    cpu, ref = (None, None) if args.no_cpu_baseline else cpu_baseline(w)
+    parity = None
+    if ref is not None and bwd:
+        parity = parity_report(torch, ra, w, layout, blocked,
+                               {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, ref)
     gqa_tag = f", {w.heads} query heads on {w.kv_heads} K/V heads" if w.kv_heads else ""
     out = {
         "metric": f"attention TFLOP/s fwd+bwd (causal {layout}{gqa_tag}, d=128) and % of bf16 MFMA peak" if bwd else
@@ -618,7 +770,7 @@ def main():
                    "ranks": [rb, re_], "passes": list(w.passes), "prefetch": w.prefetch,
                    "memory": "blocked" if blocked else "original"},
         "frac_of_peak": round(value / peak, 4),
-        "roofline": roof, "cpu_baseline": cpu, "details": details,
+        "roofline": roof, "cpu_baseline": cpu, "parity": parity, "gpu_clock": sclk, "details": details,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -296,7 +296,8 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     code = _dtype_code(q)
     pb = make_problem(B, H, d, P, Bb, layout, causal, code, scale, kv_heads=Hk)
     if out is None:
-        out = torch.empty_like(q)
+        # rows of ranks outside the range are never written: zero them
+        out = torch.zeros_like(q) if (q.shape[1] == L and nr < P) else torch.empty_like(q)
     if lse is None:
         lse = torch.empty((nr, B, H, Bb), dtype=torch.float32, device=q.device)
     use_copy = copy_stream is not None

@@ -150,6 +150,11 @@ size_t ra_workspace_bytes(const ra_problem* pb, int32_t rank_begin, int32_t rank
  *          KV block is gathered into a double buffer on `copy` while the
  *          previous step computes on `compute` (events order both hazards);
  *          the running state is merged between steps by log-sum-exp.
+ *          The workspace then starts with the double buffer: K0, V0, K1,
+ *          V1, each one dense [B][block_len][kv_heads][head_dim] block in
+ *          the problem dtype at a 256-byte aligned offset; step k receives
+ *          into pair k & 1, so after the call pair (P-1) & 1 holds the block
+ *          of step P-1 and the other pair that of step P-2.
  *   workspace: ra_workspace_bytes(pb, rb, re, copy != NULL, 0) bytes.
  *          With copy = NULL it is optional. Given, and when the problem is
  *          bf16 with a single rank whose 256-row query tiles number fewer

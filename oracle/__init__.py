@@ -36,7 +36,7 @@ from .ring import (  # noqa: F401
     block_relation,
     pair_visible,
     unmasked_pairs_per_rank,
-    block_visit_work,
-    ring_timeline,
+    block_visits,
+    tick_schedule,
 )
 from . import bpt  # noqa: F401,E402

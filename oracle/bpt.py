@@ -52,15 +52,22 @@ def gelu(z):
     return 0.5 * z * (1.0 + erf(z / math.sqrt(2.0)))
 
 
-def ffn_block(attn_out, x_blk, p):
+def ffn_block(attn_out, x_blk, p, round_to=None):
     """The block tail after attention: W_o, residual + LN1, FFN, residual + LN2.
 
     attn_out, x_blk: [rows, d_model]; p: dict of PARAM_NAMES arrays.
     Returns (out, h): the block output and the first normalised activations.
+    ``round_to``, if given, is applied to the two activations the tail hands
+    on as operands of its next products, h = LN1(...) and u = GELU(...):
+    a device that keeps them in a narrower type rounds them there (tests use
+    it to size the error that rounding alone causes); None keeps every value
+    exact.
     """
+    keep = round_to if round_to is not None else (lambda z: z)
     y = linear(attn_out, p["w_o"], p["b_o"])
-    h = layer_norm(np.asarray(x_blk, np.float64) + y, p["ln1_g"], p["ln1_b"])
-    f = linear(gelu(linear(h, p["w_1"], p["b_1"])), p["w_2"], p["b_2"])
+    h = keep(layer_norm(np.asarray(x_blk, np.float64) + y, p["ln1_g"], p["ln1_b"]))
+    u = keep(gelu(linear(h, p["w_1"], p["b_1"])))
+    f = linear(u, p["w_2"], p["b_2"])
     return layer_norm(h + f, p["ln2_g"], p["ln2_b"]), h
 
 

@@ -146,41 +146,41 @@ def unmasked_pairs_per_rank(layout: str, P: int, block_len: int, causal: bool = 
     return out
 
 
-def block_visit_work(assignment, P: int, block_len: int) -> list:
-    """The chapter's demo metric: unmasked contiguous KV-block visits.
-
-    Row r of the sequence needs KV blocks 0 .. r // Bb under a causal mask
-    (blocks of Bb consecutive rows), i.e. r // Bb + 1 visits; the count is
-    added to the device that owns row r under ``assignment`` (a list mapping
-    each row to its device). Reproduces the demo exactly as printed, for both
-    assignments.
+def block_visits(owner, P: int, block_len: int) -> list:
+    """Per-device total of causal KV-block visits, the chapter's balance
+    measure ("Worked Demo: A 4-Device Ring in Discrete Ticks"): with the
+    sequence cut into contiguous blocks of ``block_len`` rows, row r attends
+    keys of blocks 0 .. floor(r / block_len), which is floor(r / block_len) + 1
+    block visits, and those visits count for the device that owns row r.
+    ``owner[r]`` is that device (r // block_len for the contiguous layout,
+    r mod P for the striped one). Device totals are a weighted histogram of
+    the owners.
     """
-    work = [0] * P
-    for r, dev in enumerate(assignment):
-        work[dev] += r // block_len + 1
-    return work
+    owner = np.asarray(owner, dtype=np.int64)
+    visits = np.arange(owner.size) // block_len + 1
+    return [int(x) for x in np.bincount(owner, weights=visits, minlength=P)]
 
 
-def ring_timeline(c: int, m: int, P: int, overlap: bool):
-    """Device 0's schedule in the chapter's discrete-tick model.
+def tick_schedule(P: int, compute_ticks: int, hop_ticks: int, overlapped: bool) -> dict:
+    """Device 0's ring steps in the chapter's tick model ("Ring Attention:
+    Compute While You Communicate", and the discrete-tick demo that follows
+    it): every step computes one block attention (c = compute_ticks) and
+    passes one KV block to the next device (m = hop_ticks). Run one after
+    the other a step occupies c + m ticks, the hop starting as the compute
+    ends; with the hop issued at the start of the step and run alongside the
+    compute, a step occupies max(c, m) ticks, so the whole ring takes
+    P * max(c, m) instead of P * (c + m) (all of the hop hidden when m <= c).
 
-    Each of the P steps computes one block attention (c ticks) and forwards
-    one KV block (m ticks). Without overlap the hop starts when the compute
-    ends and the next step waits for both (c + m per step); with overlap the
-    hop runs alongside the compute and a step lasts max(c, m).
-
-    Returns (steps, total) with steps = [(k, (c0, c1), (m0, m1), block)],
-    ``block`` being the KV block device 0 holds and forwards at step k,
-    (0 - k) mod P. (The printed demo labels the hop "KV[(k+1) % P]"; that
-    label does not change any tick count.)
+    Returns, for steps k = 0 .. P-1: "compute" [P, 2] and "hop" [P, 2] tick
+    intervals [start, end), "block" (the KV block device 0 holds at step k,
+    (0 - k) mod P), and "total" (the tick at which the ring is done).
     """
-    steps, t = [], 0
-    for k in range(P):
-        block = (0 - k) % P
-        if overlap:
-            steps.append((k, (t, t + c), (t, t + m), block))
-            t += max(c, m)
-        else:
-            steps.append((k, (t, t + c), (t + c, t + c + m), block))
-            t += c + m
-    return steps, t
+    period = max(compute_ticks, hop_ticks) if overlapped else compute_ticks + hop_ticks
+    start = np.arange(P, dtype=np.int64) * period
+    hop_start = start if overlapped else start + compute_ticks
+    return {
+        "compute": np.stack([start, start + compute_ticks], axis=1),
+        "hop": np.stack([hop_start, hop_start + hop_ticks], axis=1),
+        "block": (-np.arange(P)) % P,
+        "total": int(P * period),
+    }

@@ -4,7 +4,10 @@ float64 oracle (oracle/bpt.py), on exactly the bf16/fp32 values the GPU sees.
 
 Bars: fp32 outputs of a product of bf16 operands accumulated in fp32 within
 1e-4 (max abs, N(0, 1)-scale values); bf16 outputs within 2e-2 beyond their
-own rounding to bfloat16 (tests/gpu_cases.py assert_output_close). Small cases
+own rounding to bfloat16 (tests/gpu_cases.py assert_output_close). The layer
+tail keeps h = LN1(...) and u = GELU(...) in bfloat16 as the operands of its
+next products; the error that rounding alone causes (the oracle run exact and
+with those two values rounded) is allowed on top of the bar. Small cases
 use ragged row counts (not a multiple of the 256-row tile or of the block);
 the full-size layer tail is checked on a spread of rows, each of which the
 oracle computes on its own (every row of the tail is independent).
@@ -15,7 +18,7 @@ import pytest
 import exact_blockwise_attention_amd as ra
 import oracle.bpt as ob
 from exact_blockwise_attention_amd import synthetic as syn
-from gpu_cases import assert_close, assert_output_close, log, to_device, to_f64
+from gpu_cases import assert_close, assert_output_close, log, round_bf16, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +38,15 @@ def dev_params(p):
 
 def f64_params(p):
     return {k: syn.to_f64(v) for k, v in p.items()}
+
+
+def ffn_reference(attn, x, p):
+    """The oracle's tail, exact, and the error its bf16 intermediates h and
+    u cause on their own."""
+    a, xx, pp = syn.to_f64(attn), syn.to_f64(x), f64_params(p)
+    ref, _ = ob.ffn_block(a, xx, pp)
+    ref_bf16, _ = ob.ffn_block(a, xx, pp, round_to=round_bf16)
+    return ref, np.abs(ref_bf16 - ref)
 
 
 @pytest.mark.parametrize("m,n,k,bias,res,gelu,f32", [
@@ -86,8 +98,8 @@ def test_bpt_ffn_small(rows, dm, dff, block):
     p = syn.bpt_params(seed, dm, dff)
     out = ra.bpt_ffn(to_device(attn), to_device(x), dev_params(p), block)
     torch.cuda.synchronize()
-    ref, _ = ob.ffn_block(syn.to_f64(attn), syn.to_f64(x), f64_params(p))
-    assert_output_close("bpt ffn", to_f64(out), ref, "bf16")
+    ref, allow = ffn_reference(attn, x, p)
+    assert_output_close("bpt ffn", to_f64(out), ref, "bf16", allowance=allow)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -119,6 +131,6 @@ def test_bpt_ffn_full_size_sampled_rows():
     rng = np.random.default_rng(71)
     sel = np.unique(np.concatenate([[0, rows - 1, w["block_rows"] - 1, w["block_rows"]],
                                     rng.choice(rows, 60, replace=False)]))
-    ref, _ = ob.ffn_block(syn.to_f64(attn[sel]), syn.to_f64(x[sel]), f64_params(p))
+    ref, allow = ffn_reference(attn[sel], x[sel], p)
     got = to_f64(out[torch.as_tensor(sel, device="cuda")])
-    assert_output_close("bpt ffn full size", got, ref, "bf16", w["name"])
+    assert_output_close("bpt ffn full size", got, ref, "bf16", w["name"], allowance=allow)

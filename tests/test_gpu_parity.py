@@ -28,9 +28,9 @@ def gpu():
     ra.library()  # the HIP library must load; there is no fallback
 
 
-def run_fwd(case, dev, rank_range=None, copy=False, split=True):
+def run_fwd(case, dev, rank_range=None, copy=False, split=True, scale=None):
     stream = torch.cuda.Stream() if copy else None
-    o, lse = ra.attention_forward(dev["q"], dev["k"], dev["v"], case.P, case.layout, case.causal,
+    o, lse = ra.attention_forward(dev["q"], dev["k"], dev["v"], case.P, case.layout, case.causal, scale=scale,
                                   rank_range=rank_range, copy_stream=stream, split=split)
     torch.cuda.synchronize()
     return o, lse
@@ -272,10 +272,10 @@ SMALL_BWD = [
 ]
 
 
-def run_bwd(case, dev, rank_range=None):
-    o, lse = run_fwd(case, dev, rank_range=rank_range)
+def run_bwd(case, dev, rank_range=None, scale=None):
+    o, lse = run_fwd(case, dev, rank_range=rank_range, scale=scale)
     dq, dk, dv = ra.attention_backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, case.P, case.layout,
-                                       case.causal, rank_range=rank_range)
+                                       case.causal, scale=scale, rank_range=rank_range)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -312,3 +312,133 @@ def test_backward_rank_range(layout, hk):
     assert_output_close("dQ", to_f64(dq)[:, pos], dq_r[:, pos], case.dtype, case)
     assert_output_close("dK", to_f64(dk), dk_r, case.dtype, case)
     assert_output_close("dV", to_f64(dv), dv_r, case.dtype, case)
+
+
+SCALE_CASES = [
+    # a caller's own scale (not 1/sqrt(d)): every kernel folds it into its
+    # exponent and the backward applies it again to dQ and dK. Gradients grow
+    # with the scale (sharper softmax rows), and so does the bf16 operands'
+    # rounding error, in proportion; the scales here (0.79 to 1.47 times the
+    # default spread of the scores) keep max |dQ|, |dK| within the range of
+    # the default-scale cases (below 4.5), where 2e-2 is the bar
+    (Case(181, 1, 2, 800, 128, 4, True, "striped", "bf16"), 0.07),
+    (Case(182, 1, 2, 800, 128, 4, True, "zigzag", "bf16"), 0.13),
+    (Case(188, 1, 2, 800, 64, 4, True, "striped", "bf16"), 0.17),
+    (Case(183, 1, 2, 400, 64, 4, True, "striped", "f32"), 0.2),
+    (Case(184, 1, 4, 800, 128, 4, True, "zigzag", "bf16", Hk=2), 0.07),
+    (Case(185, 1, 2, 600, 64, 3, False, "contiguous", "bf16"), 0.2),
+    (Case(186, 1, 2, 400, 128, 4, True, "zigzag", "f32"), 0.07),
+]
+
+
+@pytest.mark.parametrize("case,scale", SCALE_CASES, ids=lambda x: str(x))
+def test_explicit_scale_forward_backward(case, scale):
+    log(f"explicit scale {scale}: {case}")
+    p = payloads(case, ("q", "k", "v", "do"))
+    dev = {n: to_device(x) for n, x in p.items()}
+    f = {n: syn_f64(x) for n, x in p.items()}
+    dq_r, dk_r, dv_r, o_r, lse_r = oracle.attention_bwd(f["q"], f["k"], f["v"], f["do"], case.causal, scale=scale)
+    o, lse = run_fwd(case, dev, scale=scale)
+    check_fwd(case, o, lse, o_r, lse_r, range(case.P))
+    dq, dk, dv = run_bwd(case, dev, scale=scale)
+    assert_output_close("dQ", to_f64(dq), dq_r, case.dtype, case)
+    assert_output_close("dK", to_f64(dk), dk_r, case.dtype, case)
+    assert_output_close("dV", to_f64(dv), dv_r, case.dtype, case)
+    # one rank's share through the receive stream, and split into runs
+    r = case.P - 1
+    o1, lse1 = run_fwd(case, dev, rank_range=(r, r + 1), copy=True, scale=scale)
+    check_fwd(case, o1, lse1, o_r, lse_r, [r])
+    o2, lse2 = run_fwd(case, dev, rank_range=(r, r + 1), split=True, scale=scale)
+    check_fwd(case, o2, lse2, o_r, lse_r, [r])
+
+
+def _copy_mode_buffers(ws, case):
+    """The receive buffers at the start of a copy-mode forward workspace:
+    K0, V0, K1, V1, each a dense [B][block_len][kv_heads][d] block, each
+    starting at a multiple of 256 bytes (include/ra.h, ra_forward)."""
+    es = 2 if case.dtype == "bf16" else 4
+    blk = case.B * case.Bb * case.kv_heads * case.d * es
+    step = (blk + 255) // 256 * 256
+    out = []
+    for i in range(4):
+        b = ws[i * step:i * step + blk]
+        out.append(b.view(torch.int16 if es == 2 else torch.int32).reshape(case.B, case.Bb, case.kv_heads, case.d))
+    return {"k": (out[0], out[2]), "v": (out[1], out[3])}
+
+
+@pytest.mark.parametrize("delay", ["none", "copy_stream_late", "inputs_written_late"])
+def test_receive_stream_ordering(delay):
+    """The receive stand-in's three ordering edges, each under a delay that
+    would expose a missing wait ("Ring Attention 論文分析", section on
+    limitations and failure cases: a receiver computing on the previous
+    round's buffer is silent corruption). The workspace, which holds the
+    double buffer, starts as NaN.
+      copy_stream_late: the copy stream is held back by a spin, so every step
+        must wait for its block's copy (read after write);
+      inputs_written_late: K and V start as NaN and receive their values on
+        the compute stream after a spin, so the first copy must wait for the
+        inputs to be ready on the compute stream;
+      write after read: a step's kernel outlasts the copies many times over
+        (checked below), so a copy that did not wait for the step that last
+        read its buffer would overwrite that buffer while it is read.
+    The output must match the oracle, and the last two blocks left in the
+    buffers must equal the striped blocks x[:, j::P] bit for bit."""
+    case = Case(187, 1, 8, 32768, 128, 4, True, "striped", "bf16")
+    P, Bb, r = case.P, case.Bb, case.P - 1
+    log(f"receive ordering ({delay}): {case} rank {r}")
+    p = payloads(case)
+    dev = {n: to_device(x) for n, x in p.items()}
+    pb = ra.make_problem(case.B, case.H, case.d, P, Bb, case.layout, True, ra.BF16)
+    need = ra.workspace_bytes(pb, r, r + 1, True, False)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN in bf16 and fp32
+    copy = torch.cuda.Stream()
+    spin = 40_000_000  # clock cycles: about 20 ms
+    k_in, v_in = dev["k"], dev["v"]
+    if delay == "inputs_written_late":
+        k_in = torch.full_like(dev["k"], float("nan"))
+        v_in = torch.full_like(dev["v"], float("nan"))
+    torch.cuda.synchronize()
+    if delay == "copy_stream_late":
+        with torch.cuda.stream(copy):
+            torch.cuda._sleep(spin)
+    if delay == "inputs_written_late":
+        torch.cuda._sleep(spin)
+        k_in.copy_(dev["k"])
+        v_in.copy_(dev["v"])
+    o, lse = ra.attention_forward(dev["q"], k_in, v_in, P, case.layout, True, rank_range=(r, r + 1),
+                                  copy_stream=copy, workspace=ws)
+    torch.cuda.synchronize()
+    # the oracle on sampled rows of rank r, heads 0 and H-1
+    pos_r = rank_positions(case, [r])[0]
+    rows = np.unique(np.concatenate([[0, Bb - 1], np.random.default_rng(187).choice(Bb, 254, replace=False)]))
+    heads = [0, case.H - 1]
+    f = {n: syn_f64(np.ascontiguousarray(p[n][:, :, heads])) for n in "qkv"}
+    ref_o, ref_lse = oracle.attention_fwd(f["q"][:, pos_r[rows]], f["k"], f["v"], True, q_pos=pos_r[rows])
+    got_o = to_f64(o[:, torch.as_tensor(pos_r[rows], device="cuda")][:, :, heads])
+    got_lse = lse.cpu().numpy()[0][:, heads][:, :, rows].transpose(0, 2, 1)
+    assert_output_close("O", got_o, ref_o, case.dtype, case)
+    assert_close("lse", got_lse, ref_lse, TOL[case.dtype], case)
+    # the buffers hold the blocks of the last two ring steps, bit for bit
+    bufs = _copy_mode_buffers(ws, case)
+    for step in (P - 2, P - 1):
+        j = (r - step) % P
+        for n in "kv":
+            want = p[n][:, j::P]  # striped block j: tokens j, j + P, ...
+            got = bufs[n][step & 1].cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, want), f"{n} block {j} (step {step}) differs from its source"
+    if delay == "none":
+        # write after read is exercised: one step's kernel takes many times
+        # longer than the copies of a block (K and V)
+        t = {}
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        ra.attention_forward(dev["q"], dev["k"], dev["v"], P, case.layout, True, rank_range=(r, r + 1), split=False)
+        ev[1].record()
+        ra.layout_copy(dev["k"], P, case.layout)
+        ra.layout_copy(dev["v"], P, case.layout)
+        ev[2].record()
+        torch.cuda.synchronize()
+        t["step"] = ev[0].elapsed_time(ev[1]) / P
+        t["copy"] = ev[1].elapsed_time(ev[2]) / P  # K and V of one block
+        log(f"  one step {t['step']:.3f} ms, one block's copies {t['copy']:.3f} ms")
+        assert t["step"] > 4 * t["copy"]

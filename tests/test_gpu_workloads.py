@@ -13,7 +13,7 @@ import pytest
 import exact_blockwise_attention_amd as ra
 import oracle
 from exact_blockwise_attention_amd import synthetic as syn
-from gpu_cases import TOL, assert_close, assert_output_close, log, to_device, to_f64
+from gpu_cases import TOL, assert_close, assert_output_close, log, lse_at_tokens, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -148,6 +148,7 @@ def test_workload5_forward_backward():
     tol = TOL["bf16"]
     sel = lambda t, rows: to_f64(t[:, torch.as_tensor(rows, device="cuda")][:, :, heads])  # noqa: E731
     assert_output_close("O", sel(o, qrows), o_r[:, qrows], w.dtype, w.name)
+    assert_close("lse", lse_at_tokens("striped", P, w.block_len, lse, qrows, heads), lse_r[:, qrows], tol, w.name)
     assert_output_close("dQ", sel(dq, qrows), dq_r, w.dtype, w.name)
     assert_output_close("dK", sel(dk, krows), dk_r, w.dtype, w.name)
     assert_output_close("dV", sel(dv, krows), dv_r, w.dtype, w.name)
@@ -175,6 +176,7 @@ def test_workload6_grouped_query_forward_backward():
     tol = TOL["bf16"]
     sel = lambda t, rows, hs: to_f64(t[:, torch.as_tensor(rows, device="cuda")][:, :, hs])  # noqa: E731
     assert_output_close("O", sel(o, qrows, q_sel), o_r[:, qrows], w.dtype, w.name)
+    assert_close("lse", lse_at_tokens("striped", P, w.block_len, lse, qrows, q_sel), lse_r[:, qrows], tol, w.name)
     assert_output_close("dQ", sel(dq, qrows, q_sel), dq_r, w.dtype, w.name)
     assert_output_close("dK", sel(dk, krows, kv_sel), dk_r, w.dtype, w.name)
     assert_output_close("dV", sel(dv, krows, kv_sel), dv_r, w.dtype, w.name)

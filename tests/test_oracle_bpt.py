@@ -107,3 +107,34 @@ def test_planted_unbiased_variance_is_caught(monkeypatch):
 
     monkeypatch.setattr(ob, "layer_norm", ln_unbiased)
     assert np.max(np.abs(ob.bpt_layer(x, p, H, block_size=8, causal=True) - ref)) > 1e-3
+
+
+def test_rounded_intermediates_are_h_and_the_gelu_output():
+    """ffn_block's round_to reaches exactly the two activations the tail
+    hands on to its next products, LN1's output and GELU's output (checked
+    against torch's routines), and changes nothing when it is the identity;
+    rounding them changes the output through both the FFN and the second
+    residual (torch with the same roundings agrees)."""
+    rng = np.random.default_rng(9)
+    rows, dm, dff = 5, 16, 40
+    p = params(10, dm, dff)
+    a, x = rng.standard_normal((rows, dm)), rng.standard_normal((rows, dm))
+    seen = []
+    out_id, h_id = ob.ffn_block(a, x, p, round_to=lambda z: seen.append(z.copy()) or z)
+    out, h = ob.ffn_block(a, x, p)
+    assert np.array_equal(out_id, out) and np.array_equal(h_id, h)
+    t = {k: torch.tensor(v) for k, v in p.items()}
+    F = torch.nn.functional
+    normed = F.layer_norm(torch.tensor(x) + F.linear(torch.tensor(a), t["w_o"], t["b_o"]), (dm,), t["ln1_g"],
+                          t["ln1_b"], eps=1e-5)
+    u = F.gelu(F.linear(normed, t["w_1"], t["b_1"]))
+    assert len(seen) == 2
+    assert np.max(np.abs(seen[0] - normed.numpy())) < 1e-12
+    assert np.max(np.abs(seen[1] - u.numpy())) < 1e-12
+    coarse = lambda z: np.round(z * 8) / 8  # noqa: E731
+    out_c, _ = ob.ffn_block(a, x, p, round_to=coarse)
+    nc = torch.tensor(coarse(normed.numpy()))
+    uc = torch.tensor(coarse(F.gelu(F.linear(nc, t["w_1"], t["b_1"])).numpy()))
+    want = F.layer_norm(nc + F.linear(uc, t["w_2"], t["b_2"]), (dm,), t["ln2_g"], t["ln2_b"], eps=1e-5).numpy()
+    assert np.max(np.abs(out_c - want)) < 1e-12
+    assert np.max(np.abs(out_c - out)) > 1e-3

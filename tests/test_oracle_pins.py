@@ -157,14 +157,16 @@ def test_bwd_matches_torch_autograd_f64(causal):
 
 # ---------------------------------------------------------------- backward: calculus and identities
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_bwd_matches_finite_differences(causal):
+@pytest.mark.parametrize("causal,scale", [(False, None), (True, None), (True, 0.07), (False, 1.3)])
+def test_bwd_matches_finite_differences(causal, scale):
+    """The gradient of <dO, O> by central differences, at the default scale
+    and at explicit ones (a caller's own scale enters dQ and dK once more)."""
     L, d = 6, 3
     q, k, v, do = (rnd(s, 1, L, 1, d) for s in (30, 31, 32, 33))
-    dq, dk, dv, _, _ = attention_bwd(q, k, v, do, causal)
+    dq, dk, dv, _, _ = attention_bwd(q, k, v, do, causal, scale=scale)
 
     def f(qq, kk, vv):
-        return float((attention_fwd(qq, kk, vv, causal)[0] * do).sum())
+        return float((attention_fwd(qq, kk, vv, causal, scale=scale)[0] * do).sum())
 
     h = 1e-6
     for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
@@ -416,20 +418,39 @@ def test_ring_order_matches_pages():
 
 
 def test_tick_demo_matches_printed_output():
+    """The chapter prints the demo's output: each step's compute and hop
+    intervals and the totals for c = 3, m = 1 on 4 devices, and the block
+    visits of each device under both assignments of 32 rows."""
     g = json.load(open(os.path.join(GOLDEN, "ring_tick_demo.json")))
     p = g["params"]
     for key, overlap in (("non_overlapped", False), ("overlapped", True)):
-        steps, total = oracle.ring_timeline(p["c"], p["m"], p["P"], overlap)
-        assert total == g[key]["total"]
-        assert [[k, list(c), list(m)] for k, c, m, _ in steps] == g[key]["steps"]
+        sch = oracle.tick_schedule(p["P"], p["c"], p["m"], overlap)
+        assert sch["total"] == g[key]["total"]
+        got = [[k, sch["compute"][k].tolist(), sch["hop"][k].tolist()] for k in range(p["P"])]
+        assert got == g[key]["steps"]
+        assert sch["block"].tolist() == oracle.ring_schedule(p["P"], 0)
     P, B = p["P"], p["block_len"]
     N = P * B
-    wc = oracle.block_visit_work([r // B for r in range(N)], P, B)
-    ws = oracle.block_visit_work([r % P for r in range(N)], P, B)
+    wc = oracle.block_visits([r // B for r in range(N)], P, B)
+    ws = oracle.block_visits([r % P for r in range(N)], P, B)
     assert wc == g["work_contiguous"] and ws == g["work_striped"]
     assert f"{max(wc) / min(wc):.2f}" == g["ratio_contiguous"]
     assert f"{max(ws) / min(ws):.2f}" == g["ratio_striped"]
     assert sum(wc) == sum(ws) == g["total_work"]
+
+
+def test_tick_model_closed_forms():
+    """The ring takes P (c + m) ticks serially and P max(c, m) overlapped;
+    overlapped, every hop lies inside its step, and when m <= c the hop is
+    entirely hidden (each step ends when its compute ends)."""
+    for P, c, m in ((1, 5, 2), (8, 3, 7), (5, 4, 4), (3, 2, 9)):
+        ser = oracle.tick_schedule(P, c, m, False)
+        ovl = oracle.tick_schedule(P, c, m, True)
+        assert ser["total"] == P * (c + m) and ovl["total"] == P * max(c, m)
+        assert np.all(ser["hop"][:, 0] == ser["compute"][:, 1])  # hop after compute
+        assert np.all(ovl["hop"][:, 0] == ovl["compute"][:, 0])  # hop alongside
+        if m <= c:
+            assert ovl["compute"][-1, 1] == ovl["total"]
 
 
 def test_layout_perm_is_the_stated_assignment():
