@@ -43,6 +43,7 @@ library_path = os.path.join(_HERE, "libra.so")
 EXPORTED_FUNCTIONS = (
     "ra_workspace_bytes", "ra_forward", "ra_backward", "ra_backward_stage", "ra_merge_lse", "ra_layout_copy",
     "ra_linear", "ra_layer_norm", "ra_bpt_workspace_bytes", "ra_bpt_ffn", "ra_status_string", "ra_abi_version",
+    "ra_backward_noalloc", "ra_backward_noalloc_max_bytes",
 )
 
 
@@ -103,6 +104,10 @@ def library():
     lib.ra_backward.restype = i32
     lib.ra_backward_stage.argtypes = [i32, P, i32, i32, S, S, S, S, S, vp, S, S, S, vp, sz, vp]
     lib.ra_backward_stage.restype = i32
+    lib.ra_backward_noalloc.argtypes = [P, i32, i32, S, S, S, S, S, vp, S, S, S, vp]
+    lib.ra_backward_noalloc.restype = i32
+    lib.ra_backward_noalloc_max_bytes.argtypes = []
+    lib.ra_backward_noalloc_max_bytes.restype = sz
     lib.ra_merge_lse.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.ra_merge_lse.restype = i32
     lib.ra_layout_copy.argtypes = [P, vp, vp, i32, vp]
@@ -157,6 +162,18 @@ def backward_raw(pb, rank_begin, rank_end, q, k, v, o, do, lse_ptr, dq, dk, dv, 
     st = library().ra_backward(ctypes.byref(pb), rank_begin, rank_end, _ref(q), _ref(k), _ref(v), _ref(o),
                                _ref(do), lse_ptr, _ref(dq), _ref(dk), _ref(dv), ws_ptr, ws_bytes, compute)
     _check("ra_backward", st)
+
+
+def backward_noalloc_raw(pb, rank_begin, rank_end, q, k, v, o, do, lse_ptr, dq, dk, dv, compute):
+    """ra_backward_noalloc: ra_backward with the library's static scratch
+    instead of a workspace."""
+    st = library().ra_backward_noalloc(ctypes.byref(pb), rank_begin, rank_end, _ref(q), _ref(k), _ref(v), _ref(o),
+                                       _ref(do), lse_ptr, _ref(dq), _ref(dk), _ref(dv), compute)
+    _check("ra_backward_noalloc", st)
+
+
+def backward_noalloc_max_bytes() -> int:
+    return int(library().ra_backward_noalloc_max_bytes())
 
 
 def backward_stage_raw(stage, pb, rank_begin, rank_end, q, k, v, o, do, lse_ptr, dq, dk, dv, ws_ptr, ws_bytes,
@@ -337,9 +354,10 @@ def _seq_rank_rows(t, nr, layout, P):
 
 
 def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "contiguous",
-                       causal: bool = False, scale=None, rank_range=None, workspace=None):
+                       causal: bool = False, scale=None, rank_range=None, workspace=None, noalloc=False):
     """Backward on original-order [B, L, H, d] tensors (k, v, dk, dv with
-    Hk heads); returns (dq, dk, dv)."""
+    Hk heads); returns (dq, dk, dv). ``noalloc`` calls ra_backward_noalloc,
+    which takes no workspace (the library's static scratch instead)."""
     torch = _torch()
     B, L, Hk, d = k.shape
     H = q.shape[2]
@@ -351,15 +369,18 @@ def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "conti
     dq = torch.zeros_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    need = workspace_bytes(pb, rb, re, False, True)
-    if workspace is None:
+    need = 0 if noalloc else workspace_bytes(pb, rb, re, False, True)
+    if workspace is None and not noalloc:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     (qs, _q), (os_, _o), (ds, _d) = (_seq_for(t, P, layout, rb) for t in (q, o, do))
     (ks, _k), (vs, _v) = (_seq_for(t, P, layout) for t in (k, v))
     (dqs, dqb), (dks, dkb), (dvs, dvb) = (_seq_for(dq, P, layout, rb), _seq_for(dk, P, layout),
                                           _seq_for(dv, P, layout))
-    backward_raw(pb, rb, re, qs, ks, vs, os_, ds, lse.data_ptr(), dqs, dks, dvs,
-                 workspace.data_ptr(), need, _stream_handle(None))
+    if noalloc:
+        backward_noalloc_raw(pb, rb, re, qs, ks, vs, os_, ds, lse.data_ptr(), dqs, dks, dvs, _stream_handle(None))
+    else:
+        backward_raw(pb, rb, re, qs, ks, vs, os_, ds, lse.data_ptr(), dqs, dks, dvs,
+                     workspace.data_ptr(), need, _stream_handle(None))
     if layout == "zigzag":  # blocked results back to the original order
         for t, tb in ((dq, dqb), (dk, dkb), (dv, dvb)):
             t.copy_(layout_copy(tb, P, layout, inverse=True))

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "ra.h"
 #include "ra_host.h"
@@ -26,6 +27,37 @@ ra::Seq to_seq(const ra_seq* s) { return ra::Seq{s->ptr, s->s_blk, s->s_batch, s
       return RA_ERR_HIP;                     \
     }                                        \
   } while (0)
+
+// The no-allocation backward's scratch: D = rowsum(dO * O) and lse in base-2
+// units for up to kScratchBytes / 8 query rows, one copy per GPU for the
+// life of the process. In host code `scratch` only names the array; its
+// device address on the current GPU comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The scratch array's address on the current device (looked up on the first
+// call made with that device current).
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  if (!g_scratch_ptr[dev]) return hipErrorInvalidSymbol;
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // Destroys the transient events of one call on every exit path.
 struct Events {
@@ -220,6 +252,24 @@ ra_status ra_backward_stage(int32_t stage, const ra_problem* pb, int32_t rank_be
                        workspace, workspace_bytes, compute);
 }
 
+ra_status ra_backward_noalloc(const ra_problem* pb, int32_t rank_begin, int32_t rank_end, const ra_seq* q,
+                              const ra_seq* k, const ra_seq* v, const ra_seq* o, const ra_seq* dout,
+                              const float* lse, const ra_seq* dq, const ra_seq* dk, const ra_seq* dv,
+                              hipStream_t compute) {
+  // every argument check first, with a stand-in for the workspace, then the
+  // size against the static scratch
+  const BwdPlan plan = plan_backward(pb, rank_begin, rank_end, q, k, v, o, dout, lse, dq, dk, dv,
+                                     reinterpret_cast<const void*>(kAlign), SIZE_MAX);
+  if (plan.st != RA_OK) return plan.st;
+  if (plan.ws.total > kScratchBytes) return RA_ERR_SCRATCH;
+  void* ws = nullptr;
+  RA_HIP(scratch_of_current_device(&ws));
+  return backward_impl(0, 2, pb, rank_begin, rank_end, q, k, v, o, dout, lse, dq, dk, dv, ws, kScratchBytes,
+                       compute);
+}
+
+size_t ra_backward_noalloc_max_bytes(void) { return kScratchBytes; }
+
 ra_status ra_merge_lse(int64_t rows, int32_t head_dim, const float* o_a, const float* lse_a,
                        const float* o_b, const float* lse_b, float* o_out, float* lse_out,
                        hipStream_t stream) {
@@ -332,10 +382,13 @@ const char* ra_status_string(int32_t status) {
     case RA_ERR_WORKSPACE: return "workspace missing or too small";
     case RA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
     case RA_ERR_HIP: return "HIP runtime call failed";
+    case RA_ERR_SCRATCH:
+      return "problem needs more than the static scratch of the no-allocation entry point "
+             "(ra_backward_noalloc_max_bytes)";
     default: return "unknown status";
   }
 }
 
-int32_t ra_abi_version(void) { return 2; }
+int32_t ra_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -80,7 +80,8 @@ typedef enum {
   RA_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. head_dim) */
   RA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required */
   RA_ERR_ALIGN = 5,       /* a pointer or stride breaks 16-byte alignment */
-  RA_ERR_HIP = 6          /* a HIP runtime call failed */
+  RA_ERR_HIP = 6,         /* a HIP runtime call failed */
+  RA_ERR_SCRATCH = 7      /* ra_backward_noalloc: problem larger than its static scratch */
 } ra_status;
 
 /* The problem: batch B, heads H, head dim d (= value dim), ring of P blocks
@@ -199,6 +200,28 @@ ra_status ra_backward_stage(int32_t stage, const ra_problem* pb, int32_t rank_be
                             const ra_seq* o, const ra_seq* dout, const float* lse,
                             const ra_seq* dq, const ra_seq* dk, const ra_seq* dv,
                             void* workspace, size_t workspace_bytes, hipStream_t compute);
+
+/* ra_backward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the same computation and kernels as ra_backward,
+ * with D and lse in base-2 units (8 bytes per query row of the range) kept
+ * in a static device array of ra_backward_noalloc_max_bytes() bytes (64 MiB:
+ * 8M query rows, e.g. 8 ranks x 32 heads x 32768 rows), one per GPU, held
+ * until the process ends. The array used is the current device's (the
+ * compute stream must belong to it); its address is looked up on the first
+ * call made with that device current. Nothing is allocated or freed, and
+ * nothing in the array needs to start at zero: every call writes the rows it
+ * reads. Calls that overlap on one GPU (concurrent streams, threads) share
+ * the one array and race: serialise them. A problem whose rows need more
+ * than the array returns RA_ERR_SCRATCH before anything is enqueued; other
+ * errors as ra_backward. */
+ra_status ra_backward_noalloc(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
+                              const ra_seq* q, const ra_seq* k, const ra_seq* v, const ra_seq* o,
+                              const ra_seq* dout, const float* lse, const ra_seq* dq,
+                              const ra_seq* dk, const ra_seq* dv, hipStream_t compute);
+
+/* Bytes of the static scratch ra_backward_noalloc uses on each GPU. */
+size_t ra_backward_noalloc_max_bytes(void);
 
 /* Merge two partial results over disjoint key sets (blog, section
  * "ブロック単位の分割戦略": the online-softmax correction; here in its

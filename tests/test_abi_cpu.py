@@ -40,9 +40,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert ra.abi_version() == 2
+    assert ra.abi_version() == 3
     assert ra.status_string(0) == "ok"
-    for code in range(1, 7):
+    for code in range(1, 8):
         assert ra.status_string(code) not in ("ok", "unknown status")
     assert ra.status_string(99) == "unknown status"
 
@@ -263,3 +263,28 @@ def test_bpt_validation_and_workspace():
     assert lib.ra_bpt_ffn(ctypes.byref(pb), p, p, ctypes.byref(w0), p, p, 1 << 40, None) == 1
     assert lib.ra_bpt_ffn(ctypes.byref(ra.BptProblem(32768, 4000, dff, br, 0.0)), p, p, ctypes.byref(w), p, p,
                           1 << 40, None) == 2
+
+
+def test_noalloc_backward_rejects_problems_beyond_its_scratch():
+    """ra_backward_noalloc keeps 8 bytes per query row in a static array of
+    ra_backward_noalloc_max_bytes(); a larger problem returns RA_ERR_SCRATCH,
+    and invalid arguments their usual codes, before anything is launched."""
+    lib = ra.library()
+    cap = ra.backward_noalloc_max_bytes()
+    assert cap == 64 << 20
+    s = [fake_seq() for _ in range(8)]
+
+    def call(pb, lse=0x20000, seqs=s):
+        return lib.ra_backward_noalloc(ctypes.byref(pb), 0, pb.ring_size, *[ra._ref(x) for x in seqs[:5]], lse,
+                                       *[ra._ref(x) for x in seqs[5:]], None)
+    big = problem(d=128, P=8, Bb=65536, H=32)  # 8 * 32 * 65536 rows * 8 B = 128 MiB
+    assert ra.workspace_bytes(big, 0, 8, False, True) > cap
+    assert call(big) == 7
+    assert "static scratch" in ra.status_string(7)
+    assert call(problem(), lse=None) == 1
+    bad = [fake_seq() for _ in range(8)]
+    bad[6] = fake_seq(ptr=0x10008)
+    assert call(problem(), seqs=bad) == 5
+    pb = problem()
+    pb.head_dim = 96
+    assert call(pb) == 3
