@@ -28,8 +28,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["exact_blockwise_attention_amd/csrc/" + f for f in
-                  ("ra_fwd.hip", "ra_bwd.hip", "ra_dq.hip", "ra_misc.hip", "ra_gemm.hip", "ra_api.cpp", "ra_schedule.h",
-                   "ra_internal.h", "ra_lds.h", "ra_kvwalk.h")]
+                  ("ra_fwd.hip", "ra_bwd.hip", "ra_dq.hip", "ra_dqds.hip", "ra_misc.hip", "ra_gemm.hip", "ra_api.cpp",
+                   "ra_schedule.h", "ra_internal.h", "ra_lds.h", "ra_kvwalk.h", "ra_host.h")]
 
 
 def parse():
@@ -45,6 +45,9 @@ def parse():
                          "device holds it (prepared before the timed region); original: [B, L, H, d] in token "
                          "order, the blocks read through strides")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-recompute", action="store_true",
+                    help="give the backward its minimum workspace, so that the query-side walk recomputes S and dP "
+                         "for dQ instead of reading the dS tiles the key-side walk stores")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the library's layout copy with one block) three "
                          "times, as the reference for HBM byte counters")
@@ -103,6 +106,19 @@ def key_extent(layout, causal, i, j, Bb, a):
         h = Bb // 2
         return a + 1 if j == i else (h if j < i else (Bb if a >= h else 0))
     return Bb if j < i else (a + 1 if j == i else 0)
+
+
+def stored_ds_tiles(layout, causal, P, Bb, ranks):
+    """dS tiles (64 query rows x 128 keys, bf16) the backward stores and
+    reads back, per (batch, head): for each query tile of each rank and each
+    block, the 128-key tiles its last row sees."""
+    total = 0
+    for i in ranks:
+        for j in range(P):
+            for qt in range(-(-Bb // 64)):
+                a_last = min(64 * qt + 63, Bb - 1)
+                total += -(-key_extent(layout, causal, i, j, Bb, a_last) // 128)
+    return total
 
 
 def rank_work(layout, causal, P, Bb, i, rows_per_wg=256, keys_per_tile=64):
@@ -498,11 +514,35 @@ class ClockSampler:
         if self._thread is not None:
             self._stop.set()
             self._thread.join(timeout=2)
-        if not self.samples:
-            return None
-        v = sorted(self.samples)
-        return {"median_mhz": round(v[len(v) // 2], 1), "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1),
-                "samples": len(v), "source": "amdsmi gpu metrics (current gfx clock), sampled during the timed steps"}
+        return list(self.samples)
+
+
+def measure_clock(torch, step, seconds=2.5):
+    """The graphics clock while the step repeats (untimed, right after the
+    timed steps, so under the same load): the firmware refreshes the metrics
+    about once a second, so readings from before the first refresh under load
+    are dropped. Median over XCDs' mean clock, in MHz; None if unavailable."""
+    cs = ClockSampler(torch)
+    if cs._handle is None:
+        return None
+    cs.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
+    samples = cs.stop()
+    if not samples:
+        return None
+    first = 0
+    while first < len(samples) and samples[first] == samples[0]:
+        first += 1
+    loaded = sorted(samples[first:])
+    if not loaded:
+        return None
+    return {"median_mhz": round(loaded[len(loaded) // 2], 1), "min_mhz": round(loaded[0], 1),
+            "max_mhz": round(loaded[-1], 1), "samples": len(loaded),
+            "source": "amdsmi gpu metrics: mean of the per-XCD current gfx clocks while the step repeats, "
+                      "untimed, for 2.5 s after the timed steps"}
 
 
 def bench_bpt(args):
@@ -666,7 +706,8 @@ def main():
     bwd = "bwd" in w.passes
     if bwd:
         dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
-        bws = ra.workspace_bytes(pb, rb, re_, False, True)
+        bws = ra.workspace_bytes(pb, rb, re_, False, 2 if args.bwd_recompute else True)
+        stores_ds = bws > ra.workspace_bytes(pb, rb, re_, False, 2)
         bwd_ws = torch.empty(bws, dtype=torch.uint8, device="cuda")
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
@@ -696,15 +737,13 @@ def main():
     torch.cuda.synchronize()
     timing = {"f0": [], "f1": [], "b0": [], "b1": [], "b2": []}
     start, stop = ev(), ev()
-    clock = ClockSampler(torch)
     torch.cuda.synchronize()
-    clock.start()
     start.record(stream)
     for _ in range(args.steps):
         step(timing)
     stop.record(stream)
     torch.cuda.synchronize()
-    sclk = clock.stop()
+    sclk = measure_clock(torch, step)
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
 
@@ -725,13 +764,24 @@ def main():
     if bwd:
         pre_ms, dkdv_ms, dq_ms = span("f1", "b0"), span("b0", "b1"), span("b1", "b2")
         kern["dkdv"] = (dkdv_ms, 8 * d_ * pairs, "dkdv_bf16_kernel")
-        kern["dq"] = (dq_ms, 2 * d_ * pairs, "dq_bf16_kernel")
         details.update({"bwd_pre_ms": round(pre_ms, 4), "dkdv_ms": round(dkdv_ms, 4), "dq_ms": round(dq_ms, 4),
                         "dkdv_tflops": round(8 * d_ * pairs / dkdv_ms / 1e9, 2),
                         "dq_tflops_alg": round(2 * d_ * pairs / dq_ms / 1e9, 2),
-                        "dq_tflops_mfma": round(6 * d_ * pairs / dq_ms / 1e9, 2),
                         "bwd_ms": round(pre_ms + dkdv_ms + dq_ms, 4),
                         "bwd_tflops": round(bwd_flops / (pre_ms + dkdv_ms + dq_ms) / 1e9, 2)})
+        if stores_ds:
+            # dQ = scale dS K from the stored tiles: bound by reading them
+            tiles = stored_ds_tiles(layout, w.causal, P, Bb, ranks) * w.batch * w.heads
+            dq_bytes = tiles * 64 * 128 * 2 + len(ranks) * w.batch * w.heads * Bb * d_ * 2
+            kern["dq"] = (dq_ms, 2 * d_ * pairs, "dq_from_ds_kernel")
+            details["dq_path"] = "stored dS (written by the dK/dV walk, read by dq_from_ds_kernel)"
+            details["stored_ds_tiles"] = tiles
+            details["workspace_bytes"] = bws
+            details["memory_rows_dq"] = hbm_row(dq_ms, dq_bytes)
+        else:
+            kern["dq"] = (dq_ms, 2 * d_ * pairs, "dq_bf16_kernel")
+            details["dq_path"] = "recompute of S and dP in the query-side walk (dq_bf16_kernel)"
+            details["dq_tflops_mfma"] = round(6 * d_ * pairs / dq_ms / 1e9, 2)
     dom = max(kern, key=lambda k_: kern[k_][0])
     dom_ms, dom_flops, tag = kern[dom]
     achieved = dom_flops / dom_ms / 1e9

@@ -146,9 +146,11 @@ def _ref(x):
     return None if x is None else ctypes.byref(x)
 
 
-def workspace_bytes(pb: Problem, rank_begin: int, rank_end: int, use_copy_stream: bool, backward: bool) -> int:
+def workspace_bytes(pb: Problem, rank_begin: int, rank_end: int, use_copy_stream: bool, backward) -> int:
+    """backward: 0 forward; 1 (True) the backward's full workspace (bf16: dS
+    stored once); 2 the backward's minimum (dQ recomputes S and dP)."""
     return int(library().ra_workspace_bytes(ctypes.byref(pb), rank_begin, rank_end,
-                                            int(bool(use_copy_stream)), int(bool(backward))))
+                                            int(bool(use_copy_stream)), int(backward)))
 
 
 def forward_raw(pb, rank_begin, rank_end, q, k, v, o, lse_ptr, ws_ptr, ws_bytes, compute, copy):

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libra.so")
-SOURCES = ["ra_api.cpp", "ra_fwd.hip", "ra_misc.hip", "ra_bwd.hip", "ra_dq.hip", "ra_gemm.hip"]
+SOURCES = ["ra_api.cpp", "ra_fwd.hip", "ra_misc.hip", "ra_bwd.hip", "ra_dq.hip", "ra_dqds.hip", "ra_gemm.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are disabled for all device code.

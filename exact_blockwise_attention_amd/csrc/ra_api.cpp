@@ -76,7 +76,7 @@ size_t ra_workspace_bytes(const ra_problem* pb, int32_t rank_begin, int32_t rank
                           int32_t use_copy_stream, int32_t backward) {
   if (check_problem(pb, rank_begin, rank_end) != RA_OK) return 0;
   const int32_t n = rank_end - rank_begin;
-  if (backward) return bwd_ws_layout(pb, n).total;
+  if (backward) return backward == 2 ? bwd_ws_layout(pb, n).small_total : bwd_ws_layout(pb, n).total;
   return fwd_ws_layout(pb, n, use_copy_stream ? 1 : 0).total;
 }
 
@@ -192,7 +192,7 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
                                const ra_seq* k, const ra_seq* v, const ra_seq* o,
                                const ra_seq* dout, const float* lse, const ra_seq* dq,
                                const ra_seq* dk, const ra_seq* dv, void* workspace,
-                               size_t workspace_bytes, hipStream_t compute) {
+                               size_t workspace_bytes, hipStream_t compute, bool allow_ds = true) {
   const BwdPlan plan = plan_backward(pb, rank_begin, rank_end, q, k, v, o, dout, lse, dq, dk, dv, workspace,
                                      workspace_bytes);
   if (plan.st != RA_OK) return plan.st;
@@ -212,6 +212,12 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
   p.lse = lse;
   p.dsum = reinterpret_cast<float*>(ws + w.dsum);
   p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+  const bool store_ds = plan.store_ds && allow_ds;
+  if (store_ds) {
+    p.kop = reinterpret_cast<__bf16*>(ws + w.kop);
+    p.ds = reinterpret_cast<__bf16*>(ws + w.ds);
+    p.ds_stride = w.ds_stride;
+  }
   p.B = pb->batch;
   p.H = pb->heads;
   p.Hk = kv_heads_of(pb);
@@ -226,11 +232,16 @@ static ra_status backward_impl(int32_t first_stage, int32_t last_stage, const ra
   p.rank_begin = rank_begin;
   p.n_ranks = n;
   const int32_t bf16 = pb->dtype == RA_BF16;
-  if (first_stage <= 0 && last_stage >= 0) RA_HIP(ra::launch_bwd_preprocess(p, bf16, compute));
+  if (first_stage <= 0 && last_stage >= 0) {
+    RA_HIP(ra::launch_bwd_preprocess(p, bf16, compute));
+    if (store_ds) RA_HIP(ra::launch_kop_pack(p, compute));
+  }
   if (first_stage <= 1 && last_stage >= 1)
     RA_HIP(bf16 ? ra::launch_dkdv_bf16(p, compute) : ra::launch_dkdv_f32(p, compute));
-  if (first_stage <= 2 && last_stage >= 2)
-    RA_HIP(bf16 ? ra::launch_dq_bf16(p, compute) : ra::launch_dq_f32(p, compute));
+  if (first_stage <= 2 && last_stage >= 2) {
+    if (store_ds) RA_HIP(ra::launch_dq_from_ds(p, compute));
+    else RA_HIP(bf16 ? ra::launch_dq_bf16(p, compute) : ra::launch_dq_f32(p, compute));
+  }
   return RA_OK;
 }
 
@@ -261,11 +272,11 @@ ra_status ra_backward_noalloc(const ra_problem* pb, int32_t rank_begin, int32_t 
   const BwdPlan plan = plan_backward(pb, rank_begin, rank_end, q, k, v, o, dout, lse, dq, dk, dv,
                                      reinterpret_cast<const void*>(kAlign), SIZE_MAX);
   if (plan.st != RA_OK) return plan.st;
-  if (plan.ws.total > kScratchBytes) return RA_ERR_SCRATCH;
+  if (plan.ws.small_total > kScratchBytes) return RA_ERR_SCRATCH;
   void* ws = nullptr;
   RA_HIP(scratch_of_current_device(&ws));
   return backward_impl(0, 2, pb, rank_begin, rank_end, q, k, v, o, dout, lse, dq, dk, dv, ws, kScratchBytes,
-                       compute);
+                       compute, /*allow_ds=*/false);
 }
 
 size_t ra_backward_noalloc_max_bytes(void) { return kScratchBytes; }

@@ -186,6 +186,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   int32_t wpass = 0, wk = -1, wi = 0, wgi = 0, wqt = 0, wq_lo = 0, wq_hi = 0;
   BlockRel wrel = make_rel(kNone, 0, Bb);
   int32_t wfrs = Bb;
+  // stored dS (p.ds): the walk position's tile is number wds + wqt (the
+  // tiles of this key tile follow each other, one per query tile)
+  const bool store_ds = p.ds != nullptr;
+  int32_t wds = 0;
   const int32_t klast = kv0 + kKn - 1 < Bb ? kv0 + kKn - 1 : Bb - 1;
   auto next_rank = [&]() -> bool {
     for (;;) {
@@ -204,6 +208,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         wqt = wq_lo;
         wgi = 0;
         wfrs = first_row_seeing32(wrel, key, Bb);
+        if (store_ds) {
+          const int32_t run = ((wi - p.rank_begin) * p.B + b) * p.H * p.P + hk * p.G * p.P + j;
+          wds = run * (int32_t)p.ds_stride + (int32_t)ds_key_tile_start(wrel, tile, Bb) - q_first;
+        }
         return true;
       }
       if (wpass == 1) return false;
@@ -216,9 +224,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     if (++wqt < wq_hi) return 1;
     if (++wgi < p.G) {
       wqt = wq_lo;
+      if (store_ds) wds += p.P * (int32_t)p.ds_stride;  // the next query head's run
       return 2;
     }
     return next_rank() ? 2 : 0;
+  };
+  // the walk position's stored dS tile (the tiles number below 2^31), kept
+  // in a vector register: the walk's scalar state already fills the scalar
+  // registers
+  auto ds_of_walk = [&]() -> int32_t {
+    int32_t t = wds + wqt;
+    asm volatile("" : "+v"(t));
+    return t;
   };
   auto src_of_walk = [&]() {
     const int32_t ri = wi - p.rank_begin;
@@ -326,6 +343,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     QTileSrc src = src_of_walk();
     int32_t pass0 = wpass, pass1 = 1;
     int32_t lo0 = lo_of_walk(), lo1 = 0;
+    // stored dS tiles of tiles t and t + 1, and of the tile before t (whose
+    // dS the step writes out)
+    int32_t ds0 = store_ds ? ds_of_walk() : 0, ds1 = 0, dsprev = 0;
+    bool have_prev = false;
     // moves the walk on and its copy source with it (the source stays on the
     // last tile once the walk is over: copies then repeat it)
     auto advance = [&]() -> bool {
@@ -339,6 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     if (v1) {
       pass1 = wpass;
       lo1 = lo_of_walk();
+      if (store_ds) ds1 = ds_of_walk();
     }
     dma(src, 1);
     bool v2 = v1 && advance();
@@ -423,6 +445,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
 
     int32_t st = 0;
     bool v0 = true;
+    unsigned char* const ds_lane = reinterpret_cast<unsigned char*>(p.ds) + (32 * wave + n) * 32 + hf * 16;
+    auto store_dsp = [&]() __attribute__((always_inline)) {
+      unsigned char* t = ds_lane + (uint64_t)(uint32_t)dsprev * (uint32_t)(kDsRows * kDsKeys * 2);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) __builtin_nontemporal_store(dsp[kc], reinterpret_cast<bf16x8*>(t + kc * 4096));
+    };
     auto step = [&](auto MASKc) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(MASKc)::value != 0;
       const int32_t clo = lo0;
@@ -463,6 +491,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
           dsc[2 * rb + gg / 2][4 * (gg % 2) + e] = (__bf16)dsv;
         }
       };
+      // the previous tile's dS goes out first (before this step's copies,
+      // so the count of copies outstanding at the step's end is unchanged):
+      // lane (hf, n) writes its rows of key n at ((kc * 128 + 32 wave + n) * 2
+      // + hf) * 16 bytes of the tile, kc the 16-row chunk
+      if (store_ds && have_prev) store_dsp();
+      have_prev = true;
       // Phase 1
       {
         u32x4 ra[2][2];
@@ -610,16 +644,20 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       v1 = v2;
       pass0 = pass1;
       lo0 = lo1;
+      dsprev = ds0;
+      ds0 = ds1;
       if (v2) {
         pass1 = wpass;
         lo1 = lo_of_walk();
+        if (store_ds) ds1 = ds_of_walk();
         v2 = advance();
       }
     };
     while (v0 && pass0 == 0) step(ic<1>{});
     while (v0) step(ic<0>{});
 
-    // the last tile's dV / dK products
+    // the last tile's dS, and its dV / dK products
+    if (store_ds) store_dsp();
     {
       u32x2 t[4];
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ra0[0]), "+v"(ra0[1]), "+v"(ta0[0]), "+v"(ta0[1]), "+v"(ta0[2]),

@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "ra.h"
+#include "ra_schedule.h"
 
 namespace ra {
 namespace host {
@@ -165,22 +166,61 @@ inline FwdPlan plan_forward(const ra_problem* pb, int32_t rb, int32_t re, const 
 // ---------------------------------------------------------------- backward
 
 struct BwdWs {
-  size_t dsum, lse2, total;
+  size_t dsum, lse2, small_total;  // D and lse in base-2 units: what every backward needs
+  size_t kop, ds, total;           // + K in operand order and the stored dS tiles (bf16)
+  int64_t ds_stride;               // dS tiles reserved per (rank, batch, head, block)
 };
 
-// D = rowsum(dO * O) and lse in log2 units, one fp32 per query row each
+// The most dS tiles a block pair stores (kDsRows x kDsKeys each): relations
+// depend only on whether the key block comes before, is, or comes after the
+// query block, so three representative pairs cover every pair.
+inline int64_t ds_pair_stride(const ra_problem* pb) {
+  const int32_t Bb = (int32_t)pb->block_len;
+  const int32_t ktiles = (Bb + kDsKeys - 1) / kDsKeys;
+  const int32_t pairs[3][2] = {{1, 0}, {0, 0}, {0, 1}};
+  int64_t best = 0;
+  for (const auto& ij : pairs) {
+    if (ij[0] >= pb->ring_size || ij[1] >= pb->ring_size) continue;
+    const BlockRel r = block_relation(pb->layout, pb->causal, ij[0], ij[1], Bb);
+    const int64_t n = ds_key_tile_start(r, ktiles, Bb);
+    best = n > best ? n : best;
+  }
+  return best;
+}
+
+// The backward's workspace. [0, small_total): D = rowsum(dO * O) and lse in
+// base-2 units, one fp32 per query row each: enough for the walk that
+// recomputes the scores for dQ. Then, for the bf16 path that stores dS once:
+// K in MFMA operand order (one 128-key tile of D features per (batch, K/V
+// head, block, key tile)) and the dS tiles, kDsRows x kDsKeys bf16 each,
+// ds_stride of them per (rank, batch, query head, key block).
 inline BwdWs bwd_ws_layout(const ra_problem* pb, int32_t n_ranks) {
   BwdWs w{};
   const size_t rows = (size_t)n_ranks * pb->batch * pb->heads * pb->block_len;
   w.dsum = 0;
   w.lse2 = align_up(rows * sizeof(float));
-  w.total = w.lse2 + align_up(rows * sizeof(float));
+  w.small_total = w.lse2 + align_up(rows * sizeof(float));
+  w.total = w.small_total;
+  if (pb->dtype != RA_BF16 || pb->block_len > kDsMaxBlock) return w;
+  const size_t ktiles = (size_t)((pb->block_len + kDsKeys - 1) / kDsKeys);
+  w.kop = w.small_total;
+  const size_t kop_bytes = (size_t)pb->batch * kv_heads_of(pb) * pb->ring_size * ktiles * kDsKeys * pb->head_dim * 2;
+  w.ds = w.kop + align_up(kop_bytes);
+  w.ds_stride = ds_pair_stride(pb);
+  const size_t tiles = (size_t)n_ranks * pb->batch * pb->heads * pb->ring_size * (size_t)w.ds_stride;
+  if (tiles >= ((size_t)1 << 31)) {  // the kernels number the tiles in 32 bits
+    w.ds_stride = 0;
+    return w;
+  }
+  const size_t tile_bytes = (size_t)kDsRows * kDsKeys * 2;
+  w.total = w.ds + align_up(tiles * tile_bytes);
   return w;
 }
 
 struct BwdPlan {
   ra_status st;
   BwdWs ws;
+  bool store_ds;  // bf16 with the full workspace: dS stored once, dQ from it
 };
 
 inline BwdPlan plan_backward(const ra_problem* pb, int32_t rb, int32_t re, const ra_seq* q, const ra_seq* k,
@@ -200,8 +240,9 @@ inline BwdPlan plan_backward(const ra_problem* pb, int32_t rb, int32_t re, const
   if (pb->dtype == RA_BF16 && (q->s_tok >= kMaxBwdTokStride || dout->s_tok >= kMaxBwdTokStride))
     return pl.st = RA_ERR_UNSUPPORTED, pl;
   pl.ws = bwd_ws_layout(pb, re - rb);
-  if (!workspace || workspace_bytes < pl.ws.total) return pl.st = RA_ERR_WORKSPACE, pl;
+  if (!workspace || workspace_bytes < pl.ws.small_total) return pl.st = RA_ERR_WORKSPACE, pl;
   if (misaligned(workspace, kAlign)) return pl.st = RA_ERR_ALIGN, pl;
+  pl.store_ds = pb->dtype == RA_BF16 && pl.ws.total > pl.ws.small_total && workspace_bytes >= pl.ws.total;
   pl.st = RA_OK;
   return pl;
 }

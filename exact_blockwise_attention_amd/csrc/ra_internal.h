@@ -50,6 +50,14 @@ struct BwdParams {
   int32_t layout, causal;
   float scale, scale_log2;
   int32_t rank_begin, n_ranks;
+  // The backward that stores dS once (bf16; null ds: dQ recomputes S and
+  // dP instead). ds: kDsRows x kDsKeys tiles, ds_stride per (rank - begin,
+  // batch, query head, key block), the query tiles of a pair in order and
+  // in each the key tiles its last row sees; kop: K of every (batch, K/V
+  // head, block, 128-key tile) in the operand order of dQ = dS K.
+  __bf16* ds;
+  __bf16* kop;
+  int64_t ds_stride;
 };
 
 // Dense product with fused epilogue: out[m][n] = sum_k a[m][k] w[n][k]
@@ -80,6 +88,8 @@ hipError_t launch_dkdv_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_dkdv_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_dq_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_dq_f32(const BwdParams& p, hipStream_t s);
+hipError_t launch_kop_pack(const BwdParams& p, hipStream_t s);
+hipError_t launch_dq_from_ds(const BwdParams& p, hipStream_t s);
 hipError_t launch_merge_lse(int64_t rows, int32_t d, const float* oa, const float* la,
                             const float* ob, const float* lb, float* oo, float* lo,
                             hipStream_t s);

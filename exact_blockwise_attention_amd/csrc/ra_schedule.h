@@ -180,6 +180,43 @@ RA_HD int32_t first_row_seeing32(const BlockRel& r, int32_t b, int32_t block_len
   return block_len;
 }
 
+// The backward's stored score gradients: dS of a block pair is kept as
+// tiles of kDsRows query rows x kDsKeys keys, only the tiles the key-side
+// walk computes: key tile kt meets the query tiles from the first one whose
+// last row sees its first key (row extents grow with the row) to the last.
+// A pair's tiles are stored key tile by key tile, and within a key tile by
+// query tile, so that the key-side walk writes consecutive tiles.
+// Blocks of at most kDsMaxBlock tokens store dS (longer ones would need
+// terabytes).
+constexpr int32_t kDsRows = 64;
+constexpr int32_t kDsKeys = 128;
+constexpr int32_t kDsMaxBlock = 1 << 18;
+
+// Key tiles that query tile qt meets: 0 .. ds_key_tiles - 1 (those whose
+// first key its last row sees).
+RA_HD int32_t ds_key_tiles(const BlockRel& r, int32_t qt, int32_t block_len) {
+  int32_t a_last = qt * kDsRows + kDsRows - 1;
+  a_last = a_last < block_len - 1 ? a_last : block_len - 1;
+  return (row_extent32(r, a_last) + kDsKeys - 1) / kDsKeys;
+}
+
+// First query tile that key tile kt meets (the number of query tiles when
+// no row sees its first key).
+RA_HD int32_t ds_first_qtile(const BlockRel& r, int32_t kt, int32_t block_len) {
+  const int32_t a = first_row_seeing32(r, kt * kDsKeys, block_len);
+  return a >= block_len ? (block_len + kDsRows - 1) / kDsRows : a / kDsRows;
+}
+
+// Position of key tile kt's first tile in its pair's run (the tiles of the
+// key tiles before it); with kt = the number of key tiles, the pair's count.
+// Tile (qt, kt) is at ds_key_tile_start(kt) + qt - ds_first_qtile(kt).
+RA_HD int64_t ds_key_tile_start(const BlockRel& r, int32_t kt, int32_t block_len) {
+  const int32_t qtiles = (block_len + kDsRows - 1) / kDsRows;
+  int64_t n = 0;
+  for (int32_t k = 0; k < kt; ++k) n += qtiles - ds_first_qtile(r, k, block_len);
+  return n;
+}
+
 // Visible (query, key) pairs between query rows [a_lo, a_hi] and all keys of
 // a block, exact.
 RA_HD int64_t visible_pairs(const BlockRel& r, int64_t a_lo, int64_t a_hi, int64_t block_len) {

@@ -74,7 +74,9 @@ def test_workspace_sizes():
     expect_fwd = 4 * blk + rows * 128 * 4 + rows * 4  # all multiples of 256 here
     assert ra.workspace_bytes(pb, 7, 8, True, False) == expect_fwd
     rows8 = 8 * rows
-    assert ra.workspace_bytes(pb, 0, 8, False, True) == rows8 * 8  # D = rowsum(dO * O) and lse * log2(e)
+    assert ra.workspace_bytes(pb, 0, 8, False, 2) == rows8 * 8  # D = rowsum(dO * O) and lse * log2(e)
+    # the full backward workspace adds K in operand order and the stored dS tiles
+    assert ra.workspace_bytes(pb, 0, 8, False, True) > 30 * rows8 * 8 * 128
     assert ra.workspace_bytes(problem(d=96), 0, 4, False, True) == 0  # invalid problem
 
 
@@ -117,7 +119,7 @@ def test_grouped_query_heads():
     blk_kv = 1 * 4096 * 8 * 128 * 2
     rows = 1 * 32 * 4096
     assert ra.workspace_bytes(pb, 7, 8, True, False) == 4 * blk_kv + rows * 128 * 4 + rows * 4
-    assert ra.workspace_bytes(pb, 0, 8, False, True) == 8 * rows * 8  # D and lse2: one row per query head
+    assert ra.workspace_bytes(pb, 0, 8, False, 2) == 8 * rows * 8  # D and lse2: one row per query head
     assert ra.workspace_bytes(problem(H=32, kv_heads=1), 0, 4, False, True) > 0  # multi-query
     assert ra.workspace_bytes(problem(H=32, kv_heads=12), 0, 4, False, True) == 0
     assert ra.workspace_bytes(problem(H=4, kv_heads=8), 0, 4, False, True) == 0
@@ -197,7 +199,7 @@ def test_backward_validation():
     args = lambda ws, nbytes, lse=0x20000: (ctypes.byref(pb), 0, 4, *[ra._ref(x) for x in s[:5]], lse,
                                             *[ra._ref(x) for x in s[5:]], ws, nbytes, None)
     assert lib.ra_backward(*args(None, 0)) == 4
-    need = ra.workspace_bytes(pb, 0, 4, False, True)
+    need = ra.workspace_bytes(pb, 0, 4, False, 2)
     assert lib.ra_backward(*args(0x100000, need - 4)) == 4
     assert lib.ra_backward(*args(0x100000, need, lse=None)) == 1
     s[6] = None
@@ -278,7 +280,7 @@ def test_noalloc_backward_rejects_problems_beyond_its_scratch():
         return lib.ra_backward_noalloc(ctypes.byref(pb), 0, pb.ring_size, *[ra._ref(x) for x in seqs[:5]], lse,
                                        *[ra._ref(x) for x in seqs[5:]], None)
     big = problem(d=128, P=8, Bb=65536, H=32)  # 8 * 32 * 65536 rows * 8 B = 128 MiB
-    assert ra.workspace_bytes(big, 0, 8, False, True) > cap
+    assert ra.workspace_bytes(big, 0, 8, False, 2) > cap
     assert call(big) == 7
     assert "static scratch" in ra.status_string(7)
     assert call(problem(), lse=None) == 1

@@ -67,8 +67,15 @@ int main() {
         if (bw) {
           const BwdWs w = bwd_ws_layout(&pb, n);
           const size_t rows = (size_t)n * pb.batch * pb.heads * pb.block_len;
-          if (!inside(w.dsum, rows * 4, w.lse2) || !inside(w.lse2, rows * 4, w.total)) printf("BAD bwd layout\n");
-          bytes = w.total;
+          if (!inside(w.dsum, rows * 4, w.lse2) || !inside(w.lse2, rows * 4, w.small_total)) printf("BAD bwd layout\n");
+          if (w.total > w.small_total) {
+            const size_t kt = (size_t)((pb.block_len + 127) / 128);
+            const size_t kop = (size_t)pb.batch * kv_heads_of(&pb) * pb.ring_size * kt * 128 * pb.head_dim * 2;
+            const size_t ds = (size_t)n * pb.batch * pb.heads * pb.ring_size * (size_t)w.ds_stride * 64 * 128 * 2;
+            if (!inside(w.kop, kop, w.ds) || !inside(w.ds, ds, w.total) || w.kop < w.small_total || w.ds_stride < 1)
+              printf("BAD stored-dS layout\n");
+          }
+          bytes = bw == 2 ? w.small_total : w.total;
         } else {
           const FwdWs w = fwd_ws_layout(&pb, n, cp);
           if (cp) {
@@ -275,7 +282,7 @@ def test_invalid_argument_table(driver, lib):
     c.fwd(problem(layout="zigzag", Bb=63), 0, 4, s4())
     exp.append(2)
     s8 = lambda: [fake_seq() for _ in range(8)]  # noqa: E731
-    bneed = ra.workspace_bytes(problem(), 0, 4, False, True)
+    bneed = ra.workspace_bytes(problem(), 0, 4, False, 2)
     c.bwd(problem(), 0, 4, s8())
     exp.append(4)
     c.bwd(problem(), 0, 4, s8(), ws=0x100000, ws_bytes=bneed - 4)
@@ -354,7 +361,7 @@ def test_seeded_fuzz(driver, lib):
         re_ = int(rb + rng.integers(0, 4)) if rng.integers(4) else int(P)
         kind = rng.integers(5)
         if kind == 0:
-            c.ws(pb, rb, re_, bool(rng.integers(2)), bool(rng.integers(2)))
+            c.ws(pb, rb, re_, bool(rng.integers(2)), int(rng.integers(3)))
         elif kind in (1, 2):
             seqs = [random_seq(rng) for _ in range(4)]
             ws = int([0, 0x100000, 0x100010][rng.integers(3)])

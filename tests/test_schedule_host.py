@@ -9,6 +9,7 @@ import subprocess
 import numpy as np
 import pytest
 
+import exact_blockwise_attention_amd as ra
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -136,3 +137,93 @@ def test_token_positions(schedule_output):
     for r in (l.split() for l in schedule_output if l.startswith("pos ")):
         layout, s, x, t = (int(v) for v in r[1:])
         assert t == int(oracle.token_position(LAYOUT_NAMES[layout], 3, 6, s, x))
+
+
+DS_DRIVER = r"""
+#include <cstdio>
+#include <vector>
+#include "ra_host.h"
+using namespace ra;
+// The stored dS tiles: the key-side walk visits query tile qt of key tile kt
+// exactly when qt >= first_row_seeing(first key of kt) / kDsRows; the dQ
+// walk reads the tiles kt < ds_key_tiles(qt). Both must name the same set,
+// the tiles of a pair must fit the run reserved for it, and the run
+// positions must follow the prefix sums.
+int main() {
+  const int Ps[] = {1, 2, 3, 5, 8};
+  const int Bbs[] = {1, 7, 64, 65, 130, 200, 256, 300, 1000, 4096};
+  long checked = 0;
+  for (int layout = 0; layout < 3; ++layout)
+    for (int causal = 0; causal < 2; ++causal)
+      for (int P : Ps)
+        for (int Bb : Bbs) {
+          if (layout == 2 && Bb % 2) continue;
+          ra_problem pb{};
+          pb.batch = 1; pb.heads = 1; pb.head_dim = 128; pb.ring_size = P; pb.block_len = Bb;
+          pb.layout = layout; pb.causal = causal; pb.dtype = RA_BF16;
+          const long stride = host::ds_pair_stride(&pb);
+          const int qtiles = (Bb + kDsRows - 1) / kDsRows, ktiles = (Bb + kDsKeys - 1) / kDsKeys;
+          for (int i = 0; i < P; ++i)
+            for (int j = 0; j < P; ++j) {
+              const BlockRel r = block_relation(layout, causal, i, j, Bb);
+              const long count = ds_key_tile_start(r, ktiles, Bb);
+              if (count > stride) printf("BAD stride %d %d %d %d %d %d\n", layout, causal, P, Bb, i, j);
+              for (int qt = 0; qt < qtiles; ++qt)
+                if (ds_key_tiles(r, qt, Bb) > ktiles) printf("BAD key tiles\n");
+              // every stored tile has its own position inside the pair's run
+              std::vector<int> used(count > 0 ? count : 1, 0);
+              long stored = 0;
+              for (int kt = 0; kt < ktiles; ++kt) {
+                const int a_first = first_row_seeing32(r, kt * kDsKeys, Bb);
+                const int qf = ds_first_qtile(r, kt, Bb);
+                for (int qt = 0; qt < qtiles; ++qt) {
+                  const bool walk = a_first < Bb && qt >= a_first / kDsRows;
+                  const bool read = kt < ds_key_tiles(r, qt, Bb);
+                  if (walk != read) printf("BAD set %d %d %d %d %d %d %d %d\n", layout, causal, P, Bb, i, j, kt, qt);
+                  if (walk != (qt >= qf)) printf("BAD first %d %d %d %d\n", layout, causal, Bb, kt);
+                  if (walk) {
+                    const long pos = ds_key_tile_start(r, kt, Bb) + qt - qf;
+                    if (pos < 0 || pos >= count || used[pos]++) printf("BAD position %ld\n", pos);
+                    ++stored;
+                  }
+                  ++checked;
+                }
+              }
+              if (stored != count) printf("BAD count\n");
+            }
+        }
+  printf("checked %ld\n", checked);
+  return 0;
+}
+"""
+
+
+def test_stored_ds_tiles_written_are_the_tiles_read(tmp_path):
+    """The key-side walk writes dS tile (qt, kt) exactly when the dQ walk
+    reads it, for every layout, causal or not, ragged blocks included; each
+    pair's tiles fit the run the workspace reserves for it."""
+    gxx = shutil.which("g++")
+    if not gxx or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("g++ or the HIP headers are missing")
+    src = tmp_path / "ds.cpp"
+    src.write_text(DS_DRIVER)
+    exe = tmp_path / "ds"
+    subprocess.run([gxx, "-std=c++17", "-O1", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", CSRC, "-I",
+                    os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    assert "BAD" not in out, out[:2000]
+    assert int(out.split()[-1]) > 10000
+
+
+def test_ds_stride_for_the_striped_backward():
+    """The 4096-token blocks of the striped backward store 1056 of the 64 x
+    32 tiles of a block pair: key tile kt meets query tiles 2 kt .. 63 (its
+    first key, 128 kt, is first seen by row 128 kt, or 128 kt + 1 past the
+    diagonal), sum over kt of (64 - 2 kt) = 1056."""
+    pb = ra.make_problem(1, 32, 128, 8, 4096, "striped", True, ra.BF16)
+    small = ra.workspace_bytes(pb, 0, 8, False, 2)
+    full = ra.workspace_bytes(pb, 0, 8, False, True)
+    kop = 1 * 32 * 8 * 32 * 128 * 128 * 2
+    tiles = 8 * 1 * 32 * 8 * 1056
+    assert small == 8 * 32 * 4096 * 8
+    assert full == small + kop + tiles * 64 * 128 * 2
