@@ -111,6 +111,13 @@ struct DqLds {
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
+// One step of the walk: the stored tiles of the pair's two query tiles at
+// one key tile (tile indices are below 2^31), the K operand tile, and which
+// of the two query tiles meet the key tile (bit 0: qt0, bit 1: qt1).
+struct DsStep {
+  int32_t t0, t1, kop, meets;
+};
+
 // The walk of a query-tile pair over the key blocks (ring order) and their
 // key tiles; one position = one step. A pair's stored tiles go key tile by
 // key tile, key tile kt holding query tiles first(kt) .. qtiles - 1, so the
@@ -118,12 +125,10 @@ struct DqLds {
 struct DsWalk {
   int32_t k, P, i, layout, causal, Bb, qt0, qtiles;
   bool has1;
-  int64_t region0, stride, kop_region0;
-  int32_t ktiles;
+  int32_t region0, stride, kop_region0, ktiles;
   // current position
   BlockRel rel;
-  int32_t j, kt, n0, n1, nsteps, first;
-  int64_t start, run, kop;  // start(kt) in the pair's run; the run's first tile; K tile of (j, kt = 0)
+  int32_t j, kt, n0, n1, nsteps, first, start, run, kop;
   __device__ bool next_block() {
     while (++k < P) {
       j = ring_block(i, k, P);
@@ -141,7 +146,7 @@ struct DsWalk {
     }
     return false;
   }
-  // false once the walk is over; the position then stays on the last step
+  // false once the walk is over (the position then stays on the last step)
   __device__ bool next() {
     if (kt + 1 < nsteps) {
       start += qtiles - first;
@@ -149,13 +154,19 @@ struct DsWalk {
       first = ds_first_qtile(rel, kt, Bb);
       return true;
     }
-    const DsWalk keep = *this;
+    const int32_t keep_k = k;
     if (next_block()) return true;
-    *this = keep;
+    k = keep_k;
     return false;
   }
-  // the stored tile of query tile qt0 + h at this position (when it meets this key tile)
-  __device__ int64_t tile(int h) const { return run + start + (qt0 + h - first); }
+  __device__ DsStep step() const {
+    DsStep s;
+    s.t0 = run + start + (qt0 - first);
+    s.t1 = s.t0 + 1;
+    s.kop = kop + kt;
+    s.meets = (kt < n0 ? 1 : 0) | (kt < n1 ? 2 : 0);
+    return s;
+  }
 };
 
 template <int D>
@@ -203,9 +214,9 @@ __global__ __launch_bounds__(kThreads, 1) void dq_from_ds_kernel(BwdParams p) {
   w0.Bb = Bb;
   w0.qt0 = 2 * qp;
   w0.has1 = 2 * qp + 1 < qtiles;
-  w0.region0 = (((int64_t)ri * p.B + b) * p.H + h) * p.P;
-  w0.stride = p.ds_stride;
-  w0.kop_region0 = ((int64_t)b * p.Hk + hk) * p.P;
+  w0.region0 = ((ri * p.B + b) * p.H + h) * p.P;
+  w0.stride = (int32_t)p.ds_stride;
+  w0.kop_region0 = (b * p.Hk + hk) * p.P;
   w0.ktiles = (Bb + kDsKeys - 1) / kDsKeys;
 
   f32x16 acc[RBW][2];
@@ -228,22 +239,25 @@ __global__ __launch_bounds__(kThreads, 1) void dq_from_ds_kernel(BwdParams p) {
     const int key = (32 * wave + lane / 2) ^ ((kc & 1) << 2);
     dsl[kc] = (uint32_t)(kc * 4096 + key * 32 + (lane % 2) * 16);
   }
-  auto load_ds = [&](const DsWalk& s, int stage) __attribute__((always_inline)) {
-    const bool v0 = s.kt < s.n0, v1 = s.kt < s.n1;
-    const int64_t tile0 = v0 ? s.tile(0) : s.tile(1);
-    const int64_t tile1 = v1 ? s.tile(1) : s.tile(0);
+  auto load_ds = [&](const DsStep& s, int stage) __attribute__((always_inline)) {
+    // a query tile that does not meet the key tile loads the other's tile
+    // (valid memory, unused data)
+    const uint32_t tile0 = (uint32_t)((s.meets & 1) ? s.t0 : s.t1);
+    const uint32_t tile1 = (uint32_t)((s.meets & 2) ? s.t1 : s.t0);
     unsigned char* st = smem_raw + stage * L::DS_STAGE;
+    const unsigned char* src0 = dsb + (uint64_t)tile0 * kTileBytes;
+    const unsigned char* src1 = dsb + (uint64_t)tile1 * kTileBytes;
 #pragma unroll
     for (int m = 0; m < DS_LOADS; ++m) {
       const int half = m / 4, kc = m % 4;
-      const unsigned char* src = dsb + (half ? tile1 : tile0) * kTileBytes + dsl[kc];
+      const unsigned char* src = (half ? src1 : src0) + dsl[kc];
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(st + half * kTileBytes +
                                                                                         kc * 4096 + wave * 1024),
                                        16, 0, 0);
     }
   };
-  auto load_kop = [&](const DsWalk& s, int stage) __attribute__((always_inline)) {
-    const unsigned char* src = kopb + (s.kop + s.kt) * (int64_t)L::KOP_STAGE + lane * 16;
+  auto load_kop = [&](const DsStep& s, int stage) __attribute__((always_inline)) {
+    const unsigned char* src = kopb + (uint64_t)(uint32_t)s.kop * L::KOP_STAGE + lane * 16;
     unsigned char* st = smem_raw + L::KOP0 + stage * L::KOP_STAGE;
 #pragma unroll
     for (int m = 0; m < KOP_LOADS; ++m) {
@@ -317,30 +331,36 @@ __global__ __launch_bounds__(kThreads, 1) void dq_from_ds_kernel(BwdParams p) {
   };
 
   if (w0.next_block()) {
-    // three walkers: the step computed (c), the step whose K tile is loaded
-    // (one ahead), the step whose dS tiles are loaded (two ahead); past the
-    // end the loads repeat the last step (valid addresses, unused data) so
-    // that every step issues the same number of loads
-    DsWalk wc = w0, wk = w0, wd = w0;
-    load_ds(wd, 0);
-    load_kop(wk, 0);
-    wd.next();
-    load_ds(wd, 1);
-    wd.next();
-    bool more = true;
+    // one walker, two steps ahead of the step computed: s0 is the step
+    // computed, s1 the one whose K tile is loaded, s2 the one whose dS tiles
+    // are loaded; past the end the loads repeat the last step (valid
+    // addresses, unused data) so that every step issues the same loads
+    DsStep s0 = w0.step(), s1 = s0, s2 = s0;
+    bool a1 = w0.next();
+    if (a1) s1 = w0.step();
+    bool a2 = a1 && w0.next();
+    s2 = a2 ? w0.step() : s1;
+    load_ds(s0, 0);
+    load_kop(s0, 0);
+    load_ds(s1, 1);
+    bool a0 = true;
     int32_t t = 0;
-    while (more) {
+    while (a0) {
       // this step's dS tiles and K tile have landed (the loads issued after
-      // the K tile: the dS tiles of step t + 2 ... one step's worth)
+      // the K tile: the dS tiles of step t + 1, one step's worth)
       wait_vm<DS_LOADS>();
       wg_barrier();
-      wk.next();
-      load_kop(wk, (t + 1) & 1);
-      load_ds(wd, (t + 2) % L::NDS);
-      wd.next();
-      const bool mine = qh == 0 ? wc.kt < wc.n0 : wc.kt < wc.n1;
-      if (mine) compute(t % L::NDS, t & 1);
-      more = wc.next();
+      load_kop(s1, (t + 1) & 1);
+      load_ds(s2, (t + 2) % L::NDS);
+      if (s0.meets & (1 << qh)) compute(t % L::NDS, t & 1);
+      s0 = s1;
+      s1 = s2;
+      a0 = a1;
+      a1 = a2;
+      if (a2) {
+        a2 = w0.next();
+        if (a2) s2 = w0.step();
+      }
       ++t;
     }
     wait_vm<0>();
