@@ -794,7 +794,13 @@ def main():
         B_, H_ = w.batch, w.heads
         # D = rowsum(dO * O): reads O and dO rows, writes one fp32 per row
         pre_bytes = len(ranks) * B_ * H_ * Bb * (2 * d_ * t["q"].element_size() + 4)
-        details["memory_rows"] = {"B1_rowsum_dO_O": hbm_row(details["bwd_pre_ms"], pre_bytes),
+        # stage 0 alone with the minimum workspace: D = rowsum(dO * O) only
+        # (with the full workspace it also arranges K for the dQ product)
+        small = ra.workspace_bytes(pb, rb, re_, False, 2)
+        pre_args = (pb, rb, re_, so(t["q"]), sk(t["k"]), sk(t["v"]), so(o), so(t["do"]), lse.data_ptr(), so(dq),
+                    sk(dk), sk(dv), bwd_ws.data_ptr(), small, sh)
+        pre_ms = time_calls(torch, stream, lambda: ra.backward_stage_raw(0, *pre_args))
+        details["memory_rows"] = {"B1_rowsum_dO_O": hbm_row(pre_ms, pre_bytes),
                                   **memory_rows(torch, ra, w, t["q"], sh, stream)}
     if w.wid == 2:
         details["small_block_sweep"] = small_block_sweep(torch, ra, w, sh, stream)

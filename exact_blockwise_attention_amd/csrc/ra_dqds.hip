@@ -93,8 +93,8 @@ __global__ __launch_bounds__(kThreads) void kop_pack_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dQ from the stored tiles
 // A workgroup owns query tiles qt0 = 2 qp and qt1 = 2 qp + 1 (128 rows) of
-// rank i for one (batch, query head). It visits the key blocks in ring order
-// and in each the key tiles the tiles' last rows see (qt1's, a superset of
+// rank i for one (batch, query head). It visits the key blocks in block
+// order (the sum does not depend on it) and in each the key tiles the tiles' last rows see (qt1's, a superset of
 // qt0's), one step per key tile: the step's two stored dS tiles and its K
 // operand tile go global -> LDS directly, the dS tiles two steps ahead and
 // the K tile one step ahead. d = 128: wave w takes the 64 rows of tile
@@ -118,7 +118,7 @@ struct DsStep {
   int32_t t0, t1, kop, meets;
 };
 
-// The walk of a query-tile pair over the key blocks (ring order) and their
+// The walk of a query-tile pair over the key blocks (block order) and their
 // key tiles; one position = one step. A pair's stored tiles go key tile by
 // key tile, key tile kt holding query tiles first(kt) .. qtiles - 1, so the
 // step's two tiles are at start(kt) + qt - first(kt).
@@ -131,7 +131,7 @@ struct DsWalk {
   int32_t j, kt, n0, n1, nsteps, first, start, run, kop;
   __device__ bool next_block() {
     while (++k < P) {
-      j = ring_block(i, k, P);
+      j = k;  // every rank walks the blocks in the same order: workgroups share K tiles
       rel = block_relation(layout, causal, i, j, Bb);
       n0 = ds_key_tiles(rel, qt0, Bb);
       n1 = has1 ? ds_key_tiles(rel, qt0 + 1, Bb) : 0;
@@ -187,15 +187,17 @@ __global__ __launch_bounds__(kThreads, 1) void dq_from_ds_kernel(BwdParams p) {
   const int32_t qtiles = (Bb + kDsRows - 1) / kDsRows;
   const int32_t npairs = (qtiles + 1) / 2;
   const int32_t BH = p.B * p.H;
-  // consecutive logical indices: the pairs of one (batch, head, rank),
-  // heaviest (latest rows) first; an XCD's workgroups share the head's K
-  // tiles in L2
+  // consecutive logical indices: the ranks of one (batch, head, query-tile
+  // pair), pairs heaviest (latest rows) first. Every rank walks the key
+  // blocks in the same order and a pair's walk hardly depends on the rank,
+  // so an XCD's workgroups read the same K tiles at about the same time and
+  // share them in L2
   const int64_t nwg = (int64_t)BH * p.n_ranks * npairs;
   const uint32_t L0 = (uint32_t)xcd_logical(blockIdx.x, nwg);
-  const int32_t qp = npairs - 1 - (int32_t)(L0 % (uint32_t)npairs);
-  const uint32_t g0 = L0 / (uint32_t)npairs;
-  const int32_t ri = (int32_t)(g0 % (uint32_t)p.n_ranks);
-  const int32_t bh = (int32_t)(g0 / (uint32_t)p.n_ranks);
+  const int32_t ri = (int32_t)(L0 % (uint32_t)p.n_ranks);
+  const uint32_t g0 = L0 / (uint32_t)p.n_ranks;
+  const int32_t qp = npairs - 1 - (int32_t)(g0 % (uint32_t)npairs);
+  const int32_t bh = (int32_t)(g0 / (uint32_t)npairs);
   const int32_t b = bh / p.H, h = bh % p.H, hk = h / p.G;
 
   // this wave's rows: query tile qh of the pair, 32-row blocks rb0 .. rb0 + RBW - 1;
@@ -251,9 +253,11 @@ __global__ __launch_bounds__(kThreads, 1) void dq_from_ds_kernel(BwdParams p) {
     for (int m = 0; m < DS_LOADS; ++m) {
       const int half = m / 4, kc = m % 4;
       const unsigned char* src = (half ? src1 : src0) + dsl[kc];
+      // non-temporal: the tiles are read once, and should not push the K
+      // tiles, which the workgroups share, out of L2
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(st + half * kTileBytes +
                                                                                         kc * 4096 + wave * 1024),
-                                       16, 0, 0);
+                                       16, 0, 2);
     }
   };
   auto load_kop = [&](const DsStep& s, int stage) __attribute__((always_inline)) {

@@ -12,40 +12,74 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// One wave per row: every lane reads the row's two lse values before lane 0
-// writes the merged one, so lse_out may alias an input (a wave executes in
-// lockstep). Merge rule ("Ring Attention 論文分析" (blog), section "ブロック
+// Merge rule ("Ring Attention 論文分析" (blog), section "ブロック
 // 単位の分割戦略", the online-softmax correction in log-sum-exp form):
 // lse = M + ln(e^(la-M) + e^(lb-M)), O = e^(la-lse) Oa + e^(lb-lse) Ob.
+__device__ __forceinline__ void merge_weights(float xa, float xb, float* ca, float* cb, float* lo) {
+  const float m = fmaxf(xa, xb);
+  const float ms = (m == -INFINITY) ? 0.0f : m;
+  const float wa = expf(xa - ms), wb = expf(xb - ms);
+  const float tot = wa + wb;
+  *ca = (tot > 0.0f) ? wa / tot : 0.0f;
+  *cb = (tot > 0.0f) ? wb / tot : 0.0f;
+  *lo = (tot > 0.0f) ? ms + logf(tot) : -INFINITY;
+}
+
+// Any head_dim: one wave per row. Every lane reads the row's two lse values
+// before lane 0 writes the merged one, so lse_out may alias an input (a
+// wave executes in lockstep).
 __global__ __launch_bounds__(256) void merge_lse_kernel(int64_t rows, int32_t d, const float* oa,
                                                         const float* la, const float* ob,
                                                         const float* lb, float* oo, float* lo) {
   const int lane = threadIdx.x % 64;
   const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
   if (row >= rows) return;
-  const float xa = la[row], xb = lb[row];
-  const float m = fmaxf(xa, xb);
-  const float ms = (m == -INFINITY) ? 0.0f : m;
-  const float wa = expf(xa - ms), wb = expf(xb - ms);
-  const float tot = wa + wb;
-  const float ca = (tot > 0.0f) ? wa / tot : 0.0f;
-  const float cb = (tot > 0.0f) ? wb / tot : 0.0f;
+  float ca, cb, l;
+  merge_weights(la[row], lb[row], &ca, &cb, &l);
   const int64_t base = row * d;
-  if ((d & 3) == 0) {
-    for (int e = 4 * lane; e < d; e += 256) {
-      const float4 u = *reinterpret_cast<const float4*>(oa + base + e);
-      const float4 w = *reinterpret_cast<const float4*>(ob + base + e);
-      float4 r;
-      r.x = ca * u.x + cb * w.x;
-      r.y = ca * u.y + cb * w.y;
-      r.z = ca * u.z + cb * w.z;
-      r.w = ca * u.w + cb * w.w;
-      *reinterpret_cast<float4*>(oo + base + e) = r;
-    }
-  } else {
-    for (int e = lane; e < d; e += 64) oo[base + e] = ca * oa[base + e] + cb * ob[base + e];
+  for (int e = lane; e < d; e += 64) oo[base + e] = ca * oa[base + e] + cb * ob[base + e];
+  if (lane == 0) lo[row] = l;
+}
+
+// head_dim 64 or 128 (D): D / 4 lanes per row, 16 bytes each per input, and
+// kRowsPerLane rows per lane group, all loads issued before any use so that
+// enough bytes are in flight to keep HBM busy. The group's lanes read the
+// row's lse values before its first lane writes the merged one (in place is
+// allowed: a wave executes in lockstep).
+constexpr int kMergeRows = 4;
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_lse_vec_kernel(int64_t rows, const float* oa, const float* la,
+                                                            const float* ob, const float* lb, float* oo,
+                                                            float* lo) {
+  constexpr int LPR = D / 4;
+  constexpr int GROUPS = 256 / LPR;
+  const int g = threadIdx.x / LPR, e = 4 * (threadIdx.x % LPR);
+  const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + g) * kMergeRows;
+  float4 u[kMergeRows], w[kMergeRows];
+  float xa[kMergeRows], xb[kMergeRows];
+#pragma unroll
+  for (int k = 0; k < kMergeRows; ++k) {
+    const int64_t row = row0 + k < rows ? row0 + k : rows - 1;
+    u[k] = *reinterpret_cast<const float4*>(oa + row * D + e);
+    w[k] = *reinterpret_cast<const float4*>(ob + row * D + e);
+    xa[k] = la[row];
+    xb[k] = lb[row];
   }
-  if (lane == 0) lo[row] = (tot > 0.0f) ? ms + logf(tot) : -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMergeRows; ++k) {
+    const int64_t row = row0 + k;
+    if (row >= rows) break;
+    float ca, cb, l;
+    merge_weights(xa[k], xb[k], &ca, &cb, &l);
+    float4 r;
+    r.x = ca * u[k].x + cb * w[k].x;
+    r.y = ca * u[k].y + cb * w[k].y;
+    r.z = ca * u[k].z + cb * w[k].z;
+    r.w = ca * u[k].w + cb * w[k].w;
+    *reinterpret_cast<float4*>(oo + row * D + e) = r;
+    if (e == 0) lo[row] = l;
+  }
 }
 
 // Combines the partial states of the n_split runs of ring steps of a split
@@ -161,15 +195,20 @@ __device__ __forceinline__ void load8(const void* base, int64_t off, int32_t bf1
 
 // D = rowsum(dO * O) per (rank, batch, head, row) ("Ring Attention 論文分析"
 // (blog), section "逆伝播での KV 再循環"). Each lane handles 8 features; D/8
-// lanes share a row.
+// lanes share a row, and a lane group takes kPreRows rows, all their loads
+// issued before the sums so that enough bytes are in flight.
+constexpr int kPreRows = 4;
+
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p, int32_t bf16) {
   const int tpr = p.D / 8;  // lanes per row (16 or 8), a power of two dividing 64
-  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / tpr;
+  const int64_t group = ((int64_t)blockIdx.x * 256 + threadIdx.x) / tpr;
   const int part = threadIdx.x % tpr;
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
-  float acc = 0.0f;
-  if (row < rows) {
-    int64_t r = row;
+  float o8[kPreRows][8], d8[kPreRows][8];
+#pragma unroll
+  for (int k = 0; k < kPreRows; ++k) {
+    int64_t r = group * kPreRows + k;
+    if (r >= rows) r = rows - 1;  // a valid row; not written
     const int64_t x = r % p.Bb;
     r /= p.Bb;
     const int32_t h = (int32_t)(r % p.H);
@@ -178,16 +217,20 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p, int32_
     const int32_t ri = (int32_t)(r / p.B);
     const int64_t oo = ri * p.o.s_blk + b * p.o.s_batch + x * p.o.s_tok + h * p.o.s_head + 8 * part;
     const int64_t od = ri * p.dout.s_blk + b * p.dout.s_batch + x * p.dout.s_tok + h * p.dout.s_head + 8 * part;
-    float o8[8], d8[8];
-    load8(p.o.ptr, oo, bf16, o8);
-    load8(p.dout.ptr, od, bf16, d8);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc = fmaf(o8[k], d8[k], acc);
+    load8(p.o.ptr, oo, bf16, o8[k]);
+    load8(p.dout.ptr, od, bf16, d8[k]);
   }
-  for (int off = tpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) {
-    p.dsum[row] = acc;
-    p.lse2[row] = p.lse[row] * 1.44269504088896340736f;  // log2(e): the walks use exp2
+#pragma unroll
+  for (int k = 0; k < kPreRows; ++k) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(o8[k][e], d8[k][e], acc);
+    for (int off = tpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    const int64_t row = group * kPreRows + k;
+    if (row < rows && part == 0) {
+      p.dsum[row] = acc;
+      p.lse2[row] = p.lse[row] * 1.44269504088896340736f;  // log2(e): the walks use exp2
+    }
   }
 }
 
@@ -204,6 +247,16 @@ hipError_t launch_merge_lse(int64_t rows, int32_t d, const float* oa, const floa
                             const float* ob, const float* lb, float* oo, float* lo,
                             hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (d == 128 || d == 64) {
+    // 16-byte aligned rows (the C ABI checks the O pointers for d % 4 == 0)
+    const int64_t per_block = (256 / (d / 4)) * kMergeRows;
+    const int64_t grid = (rows + per_block - 1) / per_block;
+    if (d == 128)
+      hipLaunchKernelGGL(merge_lse_vec_kernel<128>, dim3((uint32_t)grid), dim3(256), 0, s, rows, oa, la, ob, lb, oo, lo);
+    else
+      hipLaunchKernelGGL(merge_lse_vec_kernel<64>, dim3((uint32_t)grid), dim3(256), 0, s, rows, oa, la, ob, lb, oo, lo);
+    return hipGetLastError();
+  }
   const int64_t grid = (rows + 3) / 4;
   hipLaunchKernelGGL(merge_lse_kernel, dim3((uint32_t)grid), dim3(256), 0, s, rows, d, oa, la, ob, lb, oo, lo);
   return hipGetLastError();
@@ -247,7 +300,7 @@ hipError_t launch_layout_copy(const void* src, void* dst, int32_t B, int32_t H, 
 hipError_t launch_bwd_preprocess(const BwdParams& p, int32_t bf16, hipStream_t s) {
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
   if (rows <= 0) return hipSuccess;
-  const int64_t lanes = rows * (p.D / 8);
+  const int64_t lanes = (rows + kPreRows - 1) / kPreRows * (p.D / 8);
   hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((uint32_t)((lanes + 255) / 256)), dim3(256), 0, s, p, bf16);
   return hipGetLastError();
 }
