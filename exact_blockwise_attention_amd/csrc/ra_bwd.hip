@@ -52,9 +52,10 @@ __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int3
 // whole walk (the B operands of S = Q K^T and dP = dO V^T), so only Q, dO,
 // lse and D go through LDS, in a ring of four stages copied two tiles ahead.
 // With a single wave per SIMD the matrix and vector work overlap inside the
-// wave: each step computes S, dP, P and dS of its tile while it finishes the
-// tile before it, whose dV^T += dO^T P and dK^T += Q^T dS products are
-// issued between the S / dP products and the exponentials.
+// wave: a step is a two-phase software pipeline over 32-row blocks, every
+// phase interleaving the S / dP products of one row block, the P / dS of
+// the row block before it and the dV^T += dO^T P, dK^T += Q^T dS products
+// of the row block before that, slot by slot.
 //
 // The copies are bounds-checked buffer loads whose range ends at the last
 // row of the block, so rows past it arrive as zeros (Q = dO = lse = D = 0,
@@ -102,17 +103,6 @@ template <int N>
 __device__ __forceinline__ void lds_wait_grp2(u32x4 (&r)[2], u32x4 (&t)[2]) {
   static_assert(N >= 0 && N <= 15, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(r[0]), "+v"(r[1]), "+v"(t[0]), "+v"(t[1]) : "n"(N));
-}
-
-template <typename F, int... I>
-__device__ __forceinline__ void unroll_seq(F& f, std::integer_sequence<int, I...>) {
-  (f(ic<I>{}), ...);
-}
-
-// f(ic<0>{}), ..., f(ic<N-1>{}).
-template <int N, typename F>
-__device__ __forceinline__ void unroll(F&& f) {
-  unroll_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // One query tile as its copies see it: the first byte of its Q and dO rows
@@ -372,273 +362,218 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     wg_barrier();
 
     const float c2 = p.scale_log2;
-    // LDS byte addresses of this lane's reads. Current tile (stage st):
-    //   cq[ss]: Q row n, columns 16ss + 8hf (row block rb: + 32 rows; dO: + DO_B)
-    //   cl: lse2 of rows 4hf .. +3 (+ 8gg + 32rb; D: + DS_B)
-    // previous tile (stage st - 1), transposing reads:
-    //   pq[h2][dt]: Q rows 4hf + j16/4 + 8h2 (chunk kc: + 16 rows; dO: + DO_B),
-    //   columns 32dt + 16grp + 4(j16%4)
+    // LDS byte addresses of this lane's reads, for the current tile's stage
+    // st (and its neighbours):
+    //   cq[ss]: Q row n of stage st, columns 16ss + 8hf (row block 1: + 32
+    //     rows; dO: + DO_B); cqn[ss]: the same in stage st + 1
+    //   cl: lse2 of rows 4hf .. +3 of stage st (+ 8gg + 32rb; D: + DS_B)
+    //   pqc[h2][dt]: transposing reads of stage st: Q rows 4hf + j16/4 + 8h2
+    //     (chunk kc: + 16 rows; dO: + DO_B), columns 32dt + 16grp +
+    //     4(j16%4); pqp[h2][dt]: the same in stage st - 1
     const uint32_t lbase = lds_addr(smem_raw);
-    uint32_t cq[NSS], pq[2][NDT];
+    uint32_t cq[NSS], cqn[NSS], pqc[2][NDT], pqp[2][NDT];
 #pragma unroll
     for (int ss = 0; ss < NSS; ++ss) {
       const uint32_t c = 2 * tile_off<D>(n, 16 * ss + 8 * hf);
       cq[ss] = lbase + c;
+      cqn[ss] = lbase + L::STG_B + c;
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint32_t c = 2 * tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
-        pq[h2][dt] = lbase + 3 * L::STG_B + c;
+        pqc[h2][dt] = lbase + c;
+        pqp[h2][dt] = lbase + 3 * L::STG_B + c;
       }
     uint32_t cl = lbase + L::F32_B + 4 * (4 * hf);
 
-    // P and dS of the previous tile (B operands of its dV / dK products, one
-    // per 16-row chunk kc: rows 16kc + 8(x/4) + 4hf + x%4 for element x)
-    bf16x8 pbp[4], dsp[4];
+    // The step is a two-phase software pipeline over the tile's two row
+    // blocks of 32 rows. Phase A: S / dP of row block 1 of tile t, P / dS
+    // of its row block 0, and dV^T / dK^T of row block 1 of tile t - 1;
+    // phase B: S / dP of row block 0 of tile t + 1, P / dS of row block 1 of
+    // tile t, and dV^T / dK^T of its row block 0. Every phase thus holds 16
+    // products that feed the vector work, 16 that consume it, and the vector
+    // work of one row block, interleaved slot by slot.
+    //   s0 / d0, s1 / d1: S and dP of row blocks 0 and 1 (element i of row
+    //     block rb: row 32rb + 8(i/4) + 4hf + i%4, key n)
+    //   pa / da, pb2 / db2: P and dS (bf16) of the 16-row chunks 0, 1 and
+    //     2, 3 (chunk kc, element x: row 16kc + 8(x/4) + 4hf + x%4), the B
+    //     operands of the dV^T / dK^T products
+    f32x16 s0, d0, s1, d1;
+    bf16x8 pa[2], da[2], pb2[2], db2[2];
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      pbp[kc] = bf16x8{};
-      dsp[kc] = bf16x8{};
+    for (int c = 0; c < 2; ++c) {
+      pa[c] = bf16x8{};
+      da[c] = bf16x8{};
+      pb2[c] = bf16x8{};
+      db2[c] = bf16x8{};
     }
+    const f32x16 zacc = {};
 
-    // dV^T += dO^T P and dK^T += Q^T dS of the previous tile come in 4 NDT
-    // products, (feature tile dt, row chunk kc); product pair X (X < 2 NDT)
-    // is (X % NDT, X / NDT) and ((X + 1) % NDT, 2 + X / NDT): two different
-    // accumulators. The two transposing reads of one product:
-    // (TOc: 0 for Q^T, DO_B for dO^T)
-    auto rd_chunk = [&](u32x2* t, auto TOc, auto DTc, auto KCc) __attribute__((always_inline)) {
-      constexpr int to = decltype(TOc)::value, dt = decltype(DTc)::value, kc = decltype(KCc)::value;
-      t[0] = tr_read_at<to + kc * 16 * D * 2>(pq[0][dt]);
-      t[1] = tr_read_at<to + kc * 16 * D * 2>(pq[1][dt]);
-    };
-    auto rd_pair = [&](u32x2* t, auto TOc, auto Xc) __attribute__((always_inline)) {
-      constexpr int X = decltype(Xc)::value;
-      rd_chunk(t, TOc, ic<X % NDT>{}, ic<X / NDT>{});
-      rd_chunk(t + 2, TOc, ic<(X + 1) % NDT>{}, ic<2 + X / NDT>{});
-    };
-    auto mm_chunk = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto DTc, auto KCc) __attribute__((always_inline)) {
-      constexpr int dt = decltype(DTc)::value, kc = decltype(KCc)::value;
-      acc[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3)), bop[kc], acc[dt]);
-    };
-    auto mm_first = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto Xc) __attribute__((always_inline)) {
-      constexpr int X = decltype(Xc)::value;
-      mm_chunk(acc, t, bop, ic<X % NDT>{}, ic<X / NDT>{});
-    };
-    auto mm_second = [&](f32x16* acc, const u32x2* t, const bf16x8* bop, auto Xc) __attribute__((always_inline)) {
-      constexpr int X = decltype(Xc)::value;
-      mm_chunk(acc, t + 2, bop, ic<(X + 1) % NDT>{}, ic<2 + X / NDT>{});
+    // s_waitcnt lgkmcnt(N) tied to one slot's reads
+    auto slot_wait = [&](auto Nc, u32x4(&ra)[2], u32x2(&ta)[4], u32x4(&rl)[2]) __attribute__((always_inline)) {
+      constexpr int N = decltype(Nc)::value;
+      static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+      asm volatile("s_waitcnt lgkmcnt(%8)"
+                   : "+v"(ra[0]), "+v"(ra[1]), "+v"(ta[0]), "+v"(ta[1]), "+v"(ta[2]), "+v"(ta[3]), "+v"(rl[0]),
+                     "+v"(rl[1])
+                   : "n"(N));
     };
 
-    // the first read group of phase 1 (Q / dO row block 0 at feature step
-    // 0, and the dO^T pair 0 of the previous tile), issued ahead of the step
-    u32x4 ra0[2];
-    u32x2 ta0[4];
-    auto rd1 = [&](u32x4* r, u32x2* t, auto SSc) __attribute__((always_inline)) {
-      constexpr int SS = decltype(SSc)::value;
-      r[0] = lds_read16<0>(cq[SS]);
-      r[1] = lds_read16<L::DO_B>(cq[SS]);
-      rd_pair(t, ic<L::DO_B>{}, SSc);
+    // One phase, NSS slots. Slot SS: the S / dP products of feature step SS
+    // of the row block read through ca (+ROFF bytes) into (sx, dx); the
+    // dV^T and dK^T products of pair SS (feature tile SS/2, chunk KC0 + SS%2)
+    // read through ta_ with B operands (pi, di); and EPS elements of P / dS
+    // of row block RBP of the current tile from (sp, dp), lse2 / D rows at
+    // LOFF, into (po, dq_). The reads of slot SS + 1 go out before slot SS
+    // waits for its own.
+    constexpr int EPS = 16 / NSS;  // P / dS elements per slot
+    static_assert(EPS * NSS == 16 && 4 * NDT == 2 * NSS, "slot shape");
+    auto phase = [&](auto MASKc, auto RBPc, auto KC0c, auto ROFFc, auto LOFFc, const uint32_t(&ca)[NSS],
+                     const uint32_t(&ta_)[2][NDT], f32x16& sx, f32x16& dx, const f32x16& sp, const f32x16& dp,
+                     bf16x8(&po)[2], bf16x8(&dq_)[2], const bf16x8(&pi)[2], const bf16x8(&di)[2], int32_t clo,
+                     auto&& at_slot) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(MASKc)::value != 0;
+      constexpr int RBP = decltype(RBPc)::value, KC0 = decltype(KC0c)::value;
+      constexpr int ROFF = decltype(ROFFc)::value, LOFF = decltype(LOFFc)::value;
+      u32x4 ra[2][2];
+      u32x2 tr[2][4];
+      u32x4 rl[2][2];
+      // reads of slot SS (the lse2 / D group of its first element when it
+      // starts a group of 4)
+      auto reads = [&](auto SSc) __attribute__((always_inline)) {
+        constexpr int SS = decltype(SSc)::value;
+        constexpr int sl = SS & 1, dt = SS / 2, kc = KC0 + SS % 2;
+        ra[sl][0] = lds_read16<ROFF>(ca[SS]);
+        ra[sl][1] = lds_read16<L::DO_B + ROFF>(ca[SS]);
+        tr[sl][0] = tr_read_at<L::DO_B + kc * 16 * D * 2>(ta_[0][dt]);
+        tr[sl][1] = tr_read_at<L::DO_B + kc * 16 * D * 2>(ta_[1][dt]);
+        tr[sl][2] = tr_read_at<kc * 16 * D * 2>(ta_[0][dt]);
+        tr[sl][3] = tr_read_at<kc * 16 * D * 2>(ta_[1][dt]);
+        if constexpr ((SS * EPS) % 4 == 0) {
+          constexpr int gg = SS * EPS / 4;
+          rl[gg & 1][0] = lds_read16<LOFF + gg * 32>(cl);
+          rl[gg & 1][1] = lds_read16<L::DS_B + LOFF + gg * 32>(cl);
+        }
+      };
+      constexpr auto nreads = [](int SS) { return 6 + ((SS * EPS) % 4 == 0 ? 2 : 0); };
+      reads(ic<0>{});
+      unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
+        constexpr int SS = decltype(SSc)::value;
+        constexpr int sl = SS & 1, dt = SS / 2, c = SS % 2;
+        constexpr int g0 = SS * EPS / 4;  // the lse2 / D group of this slot
+        if constexpr (SS + 1 < NSS) {
+          reads(ic<SS + 1>{});
+          slot_wait(ic<nreads(SS + 1)>{}, ra[sl], tr[sl], rl[g0 & 1]);
+        } else {
+          slot_wait(ic<0>{}, ra[sl], tr[sl], rl[g0 & 1]);
+        }
+        const float4 l4 = __builtin_bit_cast(float4, rl[g0 & 1][0]);
+        const float4 d4 = __builtin_bit_cast(float4, rl[g0 & 1][1]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};  // lse in log2 units
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+        sx = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sx);
+        dv[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[sl][0], tr[sl][1], 0, 1, 2, 3)), pi[c],
+                        dv[dt]);
+        at_slot(SSc);
+#pragma unroll
+        for (int x = 0; x < EPS; ++x) {
+          const int i = SS * EPS + x, gg = i / 4, e = i % 4;
+          float pv = fexp2(fmaf(sp[i], c2, -lv[e]));
+          if constexpr (MASK) {
+            if (32 * RBP + 8 * gg + e < clo) pv = 0.0f;
+          }
+          const float dsv = pv * (dp[i] - dd[e]);
+          po[gg / 2][4 * (gg % 2) + e] = (__bf16)pv;
+          dq_[gg / 2][4 * (gg % 2) + e] = (__bf16)dsv;
+        }
+        dx = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dx);
+        dk[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[sl][2], tr[sl][3], 0, 1, 2, 3)), di[c],
+                        dk[dt]);
+        // keeps the conversions of a finished chunk where they are
+        if constexpr (((SS + 1) * EPS) % 8 == 0) {
+          constexpr int ch = ((SS + 1) * EPS) / 8 - 1;
+          asm volatile("" : "+v"(po[ch]), "+v"(dq_[ch]));
+        }
+      });
     };
-    rd1(ra0, ta0, ic<0>{});
 
     int32_t st = 0;
     bool v0 = true;
     unsigned char* const ds_lane = reinterpret_cast<unsigned char*>(p.ds) + (32 * wave + n) * 32 + hf * 16;
-    auto store_dsp = [&]() __attribute__((always_inline)) {
-      unsigned char* t = ds_lane + (uint64_t)(uint32_t)dsprev * (uint32_t)(kDsRows * kDsKeys * 2);
+    // dS chunks C0, C0 + 1 of stored tile `tix`: lane (hf, n) writes its
+    // rows of key n at ((kc * 128 + 32 wave + n) * 2 + hf) * 16 bytes of the
+    // tile, kc the 16-row chunk
+    auto store_ds2 = [&](const bf16x8(&v)[2], int32_t tix, auto C0c) __attribute__((always_inline)) {
+      constexpr int C0 = decltype(C0c)::value;
+      unsigned char* t = ds_lane + (uint64_t)(uint32_t)tix * (uint32_t)(kDsRows * kDsKeys * 2);
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) __builtin_nontemporal_store(dsp[kc], reinterpret_cast<bf16x8*>(t + kc * 4096));
+      for (int c = 0; c < 2; ++c)
+        __builtin_nontemporal_store(v[c], reinterpret_cast<bf16x8*>(t + (C0 + c) * 4096));
     };
+
+    // S / dP of row block 0 of tile 0 (stage 0)
+    {
+      u32x4 ra[2][2];
+      ra[0][0] = lds_read16<0>(cq[0]);
+      ra[0][1] = lds_read16<L::DO_B>(cq[0]);
+      unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
+        constexpr int SS = decltype(SSc)::value;
+        constexpr int sl = SS & 1;
+        if constexpr (SS + 1 < NSS) {
+          ra[sl ^ 1][0] = lds_read16<0>(cq[SS + 1]);
+          ra[sl ^ 1][1] = lds_read16<L::DO_B>(cq[SS + 1]);
+          lds_wait<2>(ra[sl]);
+        } else {
+          lds_wait<0>(ra[sl]);
+        }
+        s0 = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : s0);
+        d0 = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : d0);
+      });
+    }
+
     auto step = [&](auto MASKc) __attribute__((always_inline)) {
-      constexpr bool MASK = decltype(MASKc)::value != 0;
       const int32_t clo = lo0;
-
-      // The step in three phases, each a stretch of straight-line code that
-      // mixes matrix products with the reads and vector work they do not
-      // depend on:
-      //   1. S and dP of row block 0 (A operands: Q / dO rows n), and dV^T of
-      //      the previous tile;
-      //   2. S and dP of row block 1 (rows 32 + n), and P / dS of row block 0;
-      //   3. dK^T of the previous tile, and P / dS of row block 1.
-      // Reads are issued one group ahead of their use. P and dS of element i
-      // of row block rb belong to row 32rb + 8(i/4) + 4hf + i%4.
-      f32x16 sacc[2], dacc[2];
-      bf16x8 pbc[4], dsc[4];
-      const f32x16 zacc = {};
-      // keeps the conversions of chunk kc where they are, between the
-      // products (they would otherwise sink to the next step, which uses them)
-      auto pin = [&](int kc) __attribute__((always_inline)) {
-        asm volatile("" : "+v"(pbc[kc]), "+v"(dsc[kc]));
-      };
-      // P and dS of elements 4gg + e0, +1 of row block rb, lse2 / D of the
-      // group's rows in lr
-      auto p_ds = [&](int rb, int gg, int e0, const u32x4(&lr)[2]) __attribute__((always_inline)) {
-        const float4 l4 = __builtin_bit_cast(float4, lr[0]);
-        const float4 d4 = __builtin_bit_cast(float4, lr[1]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};  // lse in log2 units
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = e0; e < e0 + 2; ++e) {
-          const int i = 4 * gg + e;
-          float pv = fexp2(fmaf(sacc[rb][i], c2, -lv[e]));
-          if constexpr (MASK) {
-            if (32 * rb + 8 * gg + e < clo) pv = 0.0f;
-          }
-          const float dsv = pv * (dacc[rb][i] - dd[e]);
-          pbc[2 * rb + gg / 2][4 * (gg % 2) + e] = (__bf16)pv;
-          dsc[2 * rb + gg / 2][4 * (gg % 2) + e] = (__bf16)dsv;
-        }
-      };
-      // the previous tile's dS goes out first (before this step's copies,
-      // so the count of copies outstanding at the step's end is unchanged):
-      // lane (hf, n) writes its rows of key n at ((kc * 128 + 32 wave + n) * 2
-      // + hf) * 16 bytes of the tile, kc the 16-row chunk
-      if (store_ds && have_prev) store_dsp();
+      // Phase A. The previous tile's dS chunks 2, 3 go out first (before
+      // this step's copies, so the copies are the last memory operations
+      // when the phase ends); tile t + 2's copies go to the stage of t - 2,
+      // which no wave reads any more.
+      if (store_ds && have_prev) store_ds2(db2, dsprev, ic<2>{});
       have_prev = true;
-      // Phase 1
-      {
-        u32x4 ra[2][2];
-        u32x2 ta[2][4];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) ra[0][k] = ra0[k];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) ta[0][k] = ta0[k];
-        unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
-          constexpr int SS = decltype(SSc)::value;
-          constexpr int sl = SS & 1;
-          if constexpr (SS + 1 < NSS) {
-            rd1(ra[sl ^ 1], ta[sl ^ 1], ic<SS + 1>{});
-            lds_wait_grp<6>(ra[sl], ta[sl]);
-          } else {
-            lds_wait_grp<0>(ra[sl], ta[sl]);
-          }
-          mm_first(dv, ta[sl], pbp, SSc);
-          if constexpr (SS == 1) dma_q(src, (st + 2) & 3);  // tile t + 2, first part
-          sacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sacc[0]);
-          mm_second(dv, ta[sl], pbp, SSc);
-          dacc[0] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dacc[0]);
-        });
-      }
+      phase(MASKc, ic<0>{}, ic<2>{}, ic<32 * D * 2>{}, ic<0>{}, cq, pqp, s1, d1, s0, d0, pa, da, pb2, db2, clo,
+            [&](auto SSc) __attribute__((always_inline)) {
+              constexpr int SS = decltype(SSc)::value;
+              if constexpr (SS == 1) dma_q(src, (st + 2) & 3);
+              if constexpr (SS == NSS / 2 + 1) dma_o(src, (st + 2) & 3);
+            });
       __builtin_amdgcn_sched_barrier(0);
-      // Phase 2 (the lse2 / D rows of group gg of row block 0 come with the
-      // reads of feature step 2gg)
-      {
-        u32x4 ra[2][2];
-        u32x4 rl[2][2];
-        auto rd = [&](auto SSc) __attribute__((always_inline)) {
-          constexpr int SS = decltype(SSc)::value;
-          constexpr int sl = SS & 1;
-          ra[sl][0] = lds_read16<32 * D * 2>(cq[SS]);
-          ra[sl][1] = lds_read16<L::DO_B + 32 * D * 2>(cq[SS]);
-          if constexpr (SS % 2 == 0) {
-            rl[(SS / 2) & 1][0] = lds_read16<(SS / 2) * 32>(cl);
-            rl[(SS / 2) & 1][1] = lds_read16<L::DS_B + (SS / 2) * 32>(cl);
-          }
-        };
-        rd(ic<0>{});
-        unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
-          constexpr int SS = decltype(SSc)::value;
-          constexpr int sl = SS & 1;
-          constexpr int gg = (SS / 2) % 4;
-          if constexpr (SS + 1 < NSS) {
-            rd(ic<SS + 1>{});
-            // outstanding after this step's group: the next group's reads
-            constexpr int nxt = ((SS + 1) % 2 == 0) ? 4 : 2;
-            if constexpr (SS % 2 == 0) lds_wait_grp2<nxt>(ra[sl], rl[(SS / 2) & 1]);
-            else lds_wait<nxt>(ra[sl]);
-          } else {
-            lds_wait<0>(ra[sl]);
-          }
-          sacc[1] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sacc[1]);
-          if constexpr (SS == 1) dma_o(src, (st + 2) & 3);  // tile t + 2, second part
-          if constexpr (NSS == 8) p_ds(0, gg, 2 * (SS % 2), rl[(SS / 2) & 1]);
-          dacc[1] = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dacc[1]);
-          if constexpr (NSS == 8 && SS % 4 == 3) pin(gg / 2);
-        });
-        if constexpr (NSS != 8) {
-          // d = 64: four feature steps; P / dS of row block 0 after them
-#pragma unroll
-          for (int gg = 0; gg < 4; ++gg) {
-            u32x4 lr[2];
-            lr[0] = lds_read16<0>(cl + gg * 32);
-            lr[1] = lds_read16<L::DS_B>(cl + gg * 32);
-            lds_wait<0>(lr);
-            p_ds(0, gg, 0, lr);
-            p_ds(0, gg, 2, lr);
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // Phase 3: dK^T product pairs X < 2 NDT of the previous tile; P / dS
-      // of row block 1 (group gg = X/2, elements 2(X%2), +1 for 8 pairs;
-      // d = 64: a whole group per pair)
-      {
-        u32x2 tq[2][4];
-        u32x4 rl[2][2];
-        constexpr int NX = 2 * NDT;
-        constexpr int GPX = 8 / NX;  // element pairs per product pair
-        auto rd = [&](auto Xc) __attribute__((always_inline)) {
-          constexpr int X = decltype(Xc)::value;
-          constexpr int sl = X & 1;
-          rd_pair(tq[sl], ic<0>{}, Xc);
-          constexpr int g0 = X * GPX / 2;  // first group of this pair
-          if constexpr ((X * GPX) % 2 == 0) {
-            rl[g0 & 1][0] = lds_read16<g0 * 32 + 32 * 4>(cl);
-            rl[g0 & 1][1] = lds_read16<L::DS_B + g0 * 32 + 32 * 4>(cl);
-          }
-        };
-        rd(ic<0>{});
-        unroll<NX>([&](auto Xc) __attribute__((always_inline)) {
-          constexpr int X = decltype(Xc)::value;
-          constexpr int sl = X & 1;
-          constexpr int g0 = X * GPX / 2;
-          constexpr bool lnext = (X + 1 < NX) && (((X + 1) * GPX) % 2 == 0);
-          if constexpr (X + 1 < NX) {
-            rd(ic<X + 1>{});
-            lds_wait_grp<lnext ? 6 : 4>(rl[g0 & 1], tq[sl]);
-          } else {
-            lds_wait_grp<0>(rl[g0 & 1], tq[sl]);
-          }
-          mm_first(dk, tq[sl], dsp, Xc);
-#pragma unroll
-          for (int k = 0; k < GPX; ++k) {
-            const int pr = X * GPX + k;  // element pair of row block 1
-            p_ds(1, pr / 2, 2 * (pr % 2), rl[(pr / 2) & 1]);
-          }
-          mm_second(dk, tq[sl], dsp, Xc);
-          if constexpr (((X + 1) * GPX) % 2 == 0) {
-            constexpr int gl = ((X + 1) * GPX) / 2 - 1;  // group just finished
-            if constexpr (gl % 2 == 1) pin(2 + gl / 2);
-          }
-        });
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        pbp[kc] = pbc[kc];
-        dsp[kc] = dsc[kc];
-      }
-
       // Tile t + 1 has landed (t + 2 may still be in flight); past the
-      // barrier no wave reads the stage of t - 1, which the next step fills
-      // with tile t + 3.
+      // barrier every wave is done with the stage of t - 1.
       wait_vm<NCOPY>();
       wg_barrier();
-      // the read addresses move one stage (the previous tile is now t), and
-      // the first read group of the next step goes out
-      const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::STG_B : L::STG_B;
-      const int32_t dp = st == 0 ? -(kNst - 1) * L::STG_B : L::STG_B;
+      // Phase B: this tile's dS chunks 0, 1 go out first
+      if (store_ds) store_ds2(da, ds0, ic<0>{});
+      phase(MASKc, ic<1>{}, ic<0>{}, ic<0>{}, ic<32 * 4>{}, cqn, pqc, s0, d0, s1, d1, pb2, db2, pa, da, clo,
+            [&](auto) __attribute__((always_inline)) {});
+      __builtin_amdgcn_sched_barrier(0);
+      // the read addresses move one stage
+      const int32_t dn = st == kNst - 2 ? -(kNst - 1) * L::STG_B : L::STG_B;  // st + 1 -> st + 2
+      const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::STG_B : L::STG_B;  // st -> st + 1
 #pragma unroll
-      for (int ss = 0; ss < NSS; ++ss) cq[ss] += dc;
+      for (int ss = 0; ss < NSS; ++ss) {
+        cq[ss] = cqn[ss];
+        cqn[ss] += dn;
+      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) pq[h2][dt] += dp;
+        for (int dt = 0; dt < NDT; ++dt) {
+          pqp[h2][dt] = pqc[h2][dt];
+          pqc[h2][dt] += dc;
+        }
       cl += st == kNst - 1 ? -(kNst - 1) * kQm * 4 : kQm * 4;
       st = (st + 1) & (kNst - 1);
-      rd1(ra0, ta0, ic<0>{});
       // t + 1 becomes current, the walk moves on to t + 3
       v0 = v1;
       v1 = v2;
@@ -656,21 +591,21 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     while (v0 && pass0 == 0) step(ic<1>{});
     while (v0) step(ic<0>{});
 
-    // the last tile's dS, and its dV / dK products
-    if (store_ds) store_dsp();
+    // the last tile's dS chunks 2, 3, and its dV^T / dK^T products of them
+    // (stage of the last tile: now st - 1)
+    if (store_ds) store_ds2(db2, dsprev, ic<2>{});
     {
       u32x2 t[4];
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ra0[0]), "+v"(ra0[1]), "+v"(ta0[0]), "+v"(ta0[1]), "+v"(ta0[2]),
-                   "+v"(ta0[3]));
-      unroll<2 * NDT>([&](auto Xc) __attribute__((always_inline)) {
-        rd_pair(t, ic<L::DO_B>{}, Xc);
+      unroll<2 * NDT>([&](auto Qc) __attribute__((always_inline)) {
+        constexpr int Q = decltype(Qc)::value;
+        constexpr int dt = Q / 2, c = Q % 2, kc = 2 + c;
+        t[0] = tr_read_at<L::DO_B + kc * 16 * D * 2>(pqp[0][dt]);
+        t[1] = tr_read_at<L::DO_B + kc * 16 * D * 2>(pqp[1][dt]);
+        t[2] = tr_read_at<kc * 16 * D * 2>(pqp[0][dt]);
+        t[3] = tr_read_at<kc * 16 * D * 2>(pqp[1][dt]);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
-        mm_first(dv, t, pbp, Xc);
-        mm_second(dv, t, pbp, Xc);
-        rd_pair(t, ic<0>{}, Xc);
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
-        mm_first(dk, t, dsp, Xc);
-        mm_second(dk, t, dsp, Xc);
+        dv[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3)), pb2[c], dv[dt]);
+        dk[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3)), db2[c], dk[dt]);
       });
     }
     wait_vm<0>();  // the repeated copies of the last steps

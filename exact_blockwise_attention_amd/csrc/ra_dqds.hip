@@ -33,16 +33,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileBytes = kDsRows * kDsKeys * 2;  // one stored dS tile: 16 KB
 
-template <typename F, int... I>
-__device__ __forceinline__ void unroll_seq(F& f, std::integer_sequence<int, I...>) {
-  (f(ic<I>{}), ...);
-}
-
-template <int N, typename F>
-__device__ __forceinline__ void unroll(F&& f) {
-  unroll_seq(f, std::make_integer_sequence<int, N>{});
-}
-
 // ---------------------------------------------------------------- K in operand order
 // One 128-key tile of block j as the B operands of dQ = dS K, unit (dt, kk)
 // (32 features x 16 keys) holding lane l's 16 bytes at (unit * 64 + l) * 16:

@@ -29,8 +29,9 @@
 // phases and group 1 runs one phase behind group 0, so on every SIMD one
 // wave feeds the matrix core while the other does the softmax. KV tiles go
 // straight from global memory to a ring of four LDS stages (K tiles in the
-// lower half of LDS, V tiles in the upper half); a tile is requested four
-// phases before its first use.
+// lower half of LDS, V tiles in the upper half); each group copies its half
+// of a tile between the products of its matrix phase, three (group 1) or
+// four (group 0) phases before the tile's first use.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -67,6 +68,7 @@ struct FwdDma {
   static constexpr int CPW = kKvTn / RW / kQWaves;
   static constexpr int NI = 2 * CPW;  // instructions per tile per wave (K and V)
   static_assert(CPW >= 1 && (kKvTn / RW) % kQWaves == 0, "tile copies must split over the waves");
+  static_assert(NI == D / 32, "a matrix phase issues one copy per feature group");
 };
 
 // max over the two half-waves (lanes n and n ^ 32)
@@ -212,6 +214,38 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       }
     }
   };
+  // The same copies one at a time, so that a matrix phase can spread them
+  // between its products: copy I < CPW is K row group I, the others V row
+  // group I - CPW. CopySrc holds the tile's first source rows.
+  struct CopySrc {
+    const char *kb, *vb;
+    int32_t lim;  // last row of the tile inside the block
+  };
+  auto copy_src = [&](const KvIter& t) __attribute__((always_inline)) {
+    const int32_t r_lo = t.t * kKvTn;
+    CopySrc c;
+    c.kb = kv_base(p.k, t.j, r_lo);
+    c.vb = kv_base(p.v, t.j, r_lo);
+    c.lim = Bb - 1 - r_lo;
+    return c;
+  };
+  auto copy_one = [&](const CopySrc& c, auto STc, int I) __attribute__((always_inline)) {
+    constexpr int ST = decltype(STc)::value;
+    const bool isv = I >= DM::CPW;
+    const int kc = I % DM::CPW;
+    const int q = wave + kQWaves * kc;
+    uint32_t off = isv ? dv[kc] : dk[kc];
+    if (c.lim < kKvTn - 1) {
+      // a tile cut by the block's end: rows past it read the last row
+      int row = q * DM::RW + lane / DM::CPR;
+      const int ch = (lane % DM::CPR) ^ chunk_swz<D>(row);
+      if (row > c.lim) row = c.lim;
+      off = (uint32_t)(2 * ((int64_t)row * (isv ? p.v.s_tok : p.k.s_tok) + 8 * ch));
+    }
+    unsigned char* dst = smem_raw + (isv ? L::VBASE_B : 0) + ST * L::TILE_B + q * 1024;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>((isv ? c.vb : c.kb) + off),
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
 
   const float c2 = p.scale_log2;
   f32x16 s[2];    // S^T of the tile in flight (32 keys each)
@@ -245,7 +279,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   // Matrix phase: scores of the tile in stage SK (if any) and O^T += V^T P^T
   // with the V tile in stage SV. The V^T fragments of one 32-feature group
   // (4 k-steps x 2 halves) are requested one group ahead of their MFMAs.
-  auto matrix = [&](auto SKc, auto SVc, bool with_scores) __attribute__((always_inline)) {
+  auto matrix = [&](auto SKc, auto SVc, bool with_scores, const CopySrc& cs, auto SCc) __attribute__((always_inline)) {
     constexpr int SV = decltype(SVc)::value;
     u32x2 vf[2][4][2];
     auto request = [&](u32x2(&r)[4][2], int dt) __attribute__((always_inline)) {
@@ -276,6 +310,8 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
         const bf16x8 a8 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vf[dt & 1][kk][0], vf[dt & 1][kk][1], 0, 1, 2, 3));
         acc[dt] = mfma32(a8, pb[kk], acc[dt]);
       }
+      // one tile copy per feature group (D / 32 groups, as many copies)
+      copy_one(cs, SCc, dt);
     }
   };
   // Vector phase of tile t (scores in s): mask, running max, probabilities,
@@ -360,13 +396,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     dadv();
     dma(itd, ic<2>{});
     dadv();
-    if (g1) {
-      dma(itd, ic<3>{});
-      dadv();
-      wait_vm<3 * DM::NI>();
-    } else {
-      wait_vm<2 * DM::NI>();
-    }
+    wait_vm<2 * DM::NI>();  // tile 0
     wg_barrier();
     // a wave whose rows all lie past the block's end (a block shorter than
     // the workgroup's 256 rows) keeps to the copies and barriers only
@@ -377,28 +407,33 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       softmax(its);
     }
     if (g1) {
-      wait_vm<2 * DM::NI>();  // tile 1: group 0 reads it in the next phase
+      wait_vm<DM::NI>();  // tile 1: group 0 reads it in the next phase
       wg_barrier();
     }
     // Phase pair t: [matrix: scores of tile t+1, P V of tile t] then
-    // [vector: softmax of tile t+1]. Stage of tile t is t % 4.
+    // [vector: softmax of tile t+1]. Stage of tile t is t % 4. Each group
+    // copies its half of tile t+3 during its own matrix phase, into the
+    // stage of tile t-1: group 1 read that stage last, before the barrier
+    // that opens group 0's matrix phase. Every wave waits for its copies of
+    // tile t+2 before the barrier that opens group 0's next matrix phase
+    // (group 0 at the top of the next step, group 1 at the end of its own
+    // matrix phase), so the one copy of a tile in flight is t+3's.
     auto step = [&](auto Uc) __attribute__((always_inline)) -> bool {
       constexpr int U = decltype(Uc)::value;
       KvIter nx = its;
       const bool has_next = nx.next();
       if (!g1) wait_vm<DM::NI>();  // tile t+1 (its K is read now)
       wg_barrier();
-      if (!g1) {
-        dma(itd, ic<(U + 3) % 4>{});  // tile t+3 into the stage tile t-1 freed
-        dadv();
+      const CopySrc cs = copy_src(itd);  // tile t+3 into the stage tile t-1 freed
+      if (busy) {
+        matrix(ic<(U + 1) % 4>{}, ic<U>{}, has_next, cs, ic<(U + 3) % 4>{});
+      } else {
+#pragma unroll
+        for (int c = 0; c < DM::NI; ++c) copy_one(cs, ic<(U + 3) % 4>{}, c);
       }
-      if (busy) matrix(ic<(U + 1) % 4>{}, ic<U>{}, has_next);
+      dadv();
       if (g1) wait_vm<DM::NI>();  // tile t+2, read by group 0 in the next phase
       wg_barrier();
-      if (g1) {
-        dma(itd, ic<U>{});  // tile t+4 into the stage tile t freed
-        dadv();
-      }
       if (has_next) {
         its = nx;
         if (busy) softmax(its);

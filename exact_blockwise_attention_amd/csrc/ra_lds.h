@@ -25,12 +25,25 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace ra {
 
 // A compile-time index (an LDS stage, an offset) passed to a generic lambda.
 template <int N>
 using ic = std::integral_constant<int, N>;
+
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(ic<I>{}), ...);
+}
+
+// f(ic<0>{}), ..., f(ic<N-1>{}): straight-line code whose steps see their
+// index as a constant.
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
