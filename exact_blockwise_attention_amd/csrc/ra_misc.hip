@@ -175,62 +175,69 @@ __global__ __launch_bounds__(256) void layout_copy_kernel(const char* src, char*
   }
 }
 
-// Eight consecutive elements of a row as floats (16 bytes of bf16, or two
-// 16-byte loads of fp32).
-__device__ __forceinline__ void load8(const void* base, int64_t off, int32_t bf16, float* out) {
-  if (bf16) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + off);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      out[2 * k] = __uint_as_float(w[k] << 16);
-      out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-    }
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off + 4);
-    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-  }
-}
-
 // D = rowsum(dO * O) per (rank, batch, head, row) ("Ring Attention 論文分析"
-// (blog), section "逆伝播での KV 再循環"). Each lane handles 8 features; D/8
-// lanes share a row, and a lane group takes kPreRows rows, all their loads
-// issued before the sums so that enough bytes are in flight.
-constexpr int kPreRows = 4;
+// (blog), section "逆伝播での KV 再循環"). Each lane handles 8 features; TPR =
+// D/8 lanes share a row, and a lane group takes ROWS consecutive rows (8 for
+// bf16, kept as raw words until the sums; 4 for fp32), all their loads
+// issued before the sums so that enough bytes are in flight. A workgroup
+// covers the rows of one (rank, batch, head) run that its lane groups take
+// together, decoding the run once; lanes 0 .. ROWS-1 of a group then write
+// D and lse * log2(e) of the group's rows side by side.
+template <bool BF16>
+constexpr int pre_rows() { return BF16 ? 8 : 4; }
 
-__global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p, int32_t bf16) {
-  const int tpr = p.D / 8;  // lanes per row (16 or 8), a power of two dividing 64
-  const int64_t group = ((int64_t)blockIdx.x * 256 + threadIdx.x) / tpr;
-  const int part = threadIdx.x % tpr;
-  const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
-  float o8[kPreRows][8], d8[kPreRows][8];
+template <int TPR, bool BF16>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(BwdParams p, int32_t xblocks) {
+  constexpr int ROWS = pre_rows<BF16>();
+  constexpr int PER_BLK = 256 / TPR * ROWS;
+  constexpr int W = BF16 ? 1 : 2;  // 16-byte words per 8 features
+  static_assert(ROWS <= TPR, "one writing lane per row");
+  const int32_t run = (int32_t)(blockIdx.x / (uint32_t)xblocks);  // (ri * B + b) * H + h
+  const int32_t xb = (int32_t)(blockIdx.x % (uint32_t)xblocks);
+  const int32_t h = run % p.H;
+  const int32_t b = (run / p.H) % p.B;
+  const int32_t ri = run / (p.H * p.B);
+  const int part = threadIdx.x % TPR;
+  const int64_t x0 = (int64_t)xb * PER_BLK + (threadIdx.x / TPR) * ROWS;
+  constexpr int ES = BF16 ? 2 : 4;  // element bytes
+  const char* ob = reinterpret_cast<const char*>(p.o.ptr) +
+                   ES * (ri * p.o.s_blk + b * p.o.s_batch + h * p.o.s_head + 8 * part);
+  const char* db = reinterpret_cast<const char*>(p.dout.ptr) +
+                   ES * (ri * p.dout.s_blk + b * p.dout.s_batch + h * p.dout.s_head + 8 * part);
+  u32x4 ow[ROWS][W], dw[ROWS][W];
 #pragma unroll
-  for (int k = 0; k < kPreRows; ++k) {
-    int64_t r = group * kPreRows + k;
-    if (r >= rows) r = rows - 1;  // a valid row; not written
-    const int64_t x = r % p.Bb;
-    r /= p.Bb;
-    const int32_t h = (int32_t)(r % p.H);
-    r /= p.H;
-    const int32_t b = (int32_t)(r % p.B);
-    const int32_t ri = (int32_t)(r / p.B);
-    const int64_t oo = ri * p.o.s_blk + b * p.o.s_batch + x * p.o.s_tok + h * p.o.s_head + 8 * part;
-    const int64_t od = ri * p.dout.s_blk + b * p.dout.s_batch + x * p.dout.s_tok + h * p.dout.s_head + 8 * part;
-    load8(p.o.ptr, oo, bf16, o8[k]);
-    load8(p.dout.ptr, od, bf16, d8[k]);
+  for (int k = 0; k < ROWS; ++k) {
+    const int64_t x = x0 + k < p.Bb ? x0 + k : p.Bb - 1;  // a valid row; not written
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      ow[k][w] = *reinterpret_cast<const u32x4*>(ob + ES * x * p.o.s_tok + 16 * w);
+      dw[k][w] = *reinterpret_cast<const u32x4*>(db + ES * x * p.dout.s_tok + 16 * w);
+    }
   }
+  float mine = 0.0f;  // D of row x0 + part (lanes part < ROWS)
 #pragma unroll
-  for (int k = 0; k < kPreRows; ++k) {
+  for (int k = 0; k < ROWS; ++k) {
     float acc = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(o8[k][e], d8[k][e], acc);
-    for (int off = tpr / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    const int64_t row = group * kPreRows + k;
-    if (row < rows && part == 0) {
-      p.dsum[row] = acc;
-      p.lse2[row] = p.lse[row] * 1.44269504088896340736f;  // log2(e): the walks use exp2
-    }
+    for (int w = 0; w < W; ++w)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (BF16) {
+          acc = fmaf(__uint_as_float(ow[k][w][q] << 16), __uint_as_float(dw[k][w][q] << 16), acc);
+          acc = fmaf(__uint_as_float(ow[k][w][q] & 0xFFFF0000u), __uint_as_float(dw[k][w][q] & 0xFFFF0000u), acc);
+        } else {
+          acc = fmaf(__uint_as_float(ow[k][w][q]), __uint_as_float(dw[k][w][q]), acc);
+        }
+      }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (part == k) mine = acc;
+  }
+  const int64_t x = x0 + part;
+  if (part < ROWS && x < p.Bb) {
+    const int64_t row = (int64_t)run * p.Bb + x;
+    p.dsum[row] = mine;
+    p.lse2[row] = p.lse[row] * 1.44269504088896340736f;  // log2(e): the walks use exp2
   }
 }
 
@@ -300,8 +307,17 @@ hipError_t launch_layout_copy(const void* src, void* dst, int32_t B, int32_t H, 
 hipError_t launch_bwd_preprocess(const BwdParams& p, int32_t bf16, hipStream_t s) {
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
   if (rows <= 0) return hipSuccess;
-  const int64_t lanes = (rows + kPreRows - 1) / kPreRows * (p.D / 8);
-  hipLaunchKernelGGL(bwd_preprocess_kernel, dim3((uint32_t)((lanes + 255) / 256)), dim3(256), 0, s, p, bf16);
+  const int32_t tpr = p.D / 8;  // 16 or 8 (head_dim 128 or 64)
+  const int64_t per_blk = 256 / tpr * (bf16 ? pre_rows<true>() : pre_rows<false>());
+  const int64_t xblocks = (p.Bb + per_blk - 1) / per_blk;
+  const int64_t grid = (int64_t)p.n_ranks * p.B * p.H * xblocks;
+  if (grid > 0xFFFFFFFFLL) return hipErrorInvalidValue;
+  const dim3 g((uint32_t)grid), t(256);
+  const int32_t xbl = (int32_t)xblocks;
+  if (tpr == 16 && bf16) hipLaunchKernelGGL((bwd_preprocess_kernel<16, true>), g, t, 0, s, p, xbl);
+  else if (tpr == 16) hipLaunchKernelGGL((bwd_preprocess_kernel<16, false>), g, t, 0, s, p, xbl);
+  else if (bf16) hipLaunchKernelGGL((bwd_preprocess_kernel<8, true>), g, t, 0, s, p, xbl);
+  else hipLaunchKernelGGL((bwd_preprocess_kernel<8, false>), g, t, 0, s, p, xbl);
   return hipGetLastError();
 }
 
