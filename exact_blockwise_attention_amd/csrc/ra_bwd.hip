@@ -37,13 +37,13 @@ constexpr int kQm = 64;   // query rows per visited tile
 // Heaviest KV tiles first: early keys are seen by more query rows.
 __device__ __forceinline__ void kv_tile_of(const BwdParams& p, int64_t ord, int32_t tiles, int32_t* j,
                                            int32_t* tile) {
-  if (p.causal && p.layout == kContiguous) {
-    *j = (int32_t)(ord / tiles);
-    *tile = (int32_t)(ord % tiles);
-  } else {
-    *tile = (int32_t)(ord / p.P);
-    *j = (int32_t)(ord % p.P);
-  }
+  // (selects on the values, not on where they go: the kernels keep j and
+  // tile in registers)
+  const bool by_block = p.causal && p.layout == kContiguous;
+  const int64_t div = by_block ? tiles : p.P;
+  const int32_t q = (int32_t)(ord / div), r = (int32_t)(ord % div);
+  *j = by_block ? q : r;
+  *tile = by_block ? r : q;
 }
 
 // ---------------------------------------------------------------- bf16 path
@@ -632,15 +632,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Plain VALU kernel for float32: one lane per key (64 keys per workgroup),
-// dK/dV of that key in registers, query tiles of 32 rows staged in LDS (dQ:
-// dq_f32_kernel).
+// Plain VALU kernel for float32: kF32Split lanes per key (64 keys per
+// workgroup), each holding dK/dV of a quarter of the features in registers;
+// the S and dP dot products add the quarters with two lane exchanges. Query
+// tiles of 32 rows are staged in LDS (dQ: dq_f32_kernel).
 constexpr int kF32Keys = 64;
 constexpr int kF32Rows = 32;
+constexpr int kF32Split = 4;  // lanes per key
+constexpr int kF32Threads = kF32Keys * kF32Split;
 
 template <int D>
 struct BwdF32Lds {
-  static constexpr int S = D + 1;  // padded rows: per-lane own-row reads are conflict-free
+  static constexpr int S = D + 1;  // padded rows
   static constexpr int KS = 0;
   static constexpr int VS = KS + kF32Keys * S;
   static constexpr int QS = VS + kF32Keys * S;
@@ -652,8 +655,9 @@ struct BwdF32Lds {
 };
 
 template <int D>
-__global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
+__global__ __launch_bounds__(kF32Threads) void dkdv_f32_kernel(BwdParams p) {
   using L = BwdF32Lds<D>;
+  constexpr int DQ = D / kF32Split;  // features per lane
   extern __shared__ __align__(16) unsigned char smem_raw[];
   float* sm = reinterpret_cast<float*>(smem_raw);
   float* ks = sm + L::KS;
@@ -663,6 +667,8 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
   float* lse_s = sm + L::LSE;
   float* dsum_s = sm + L::DSUM;
   const int tid = threadIdx.x;
+  const int kl = tid / kF32Split;          // this lane's key in the tile
+  const int f0 = (tid % kF32Split) * DQ;   // its first feature
   const int32_t BHk = p.B * p.Hk;
   const int32_t tiles = (int32_t)((p.Bb + kF32Keys - 1) / kF32Keys);
   const int64_t id = blockIdx.x;
@@ -672,18 +678,18 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
   int32_t j, tile;
   kv_tile_of(p, id / BHk, tiles, &j, &tile);
   const int64_t kv0 = (int64_t)tile * kF32Keys;
-  const int64_t key = kv0 + tid;
+  const int64_t key = kv0 + kl;
   const float* kbase = reinterpret_cast<const float*>(p.k.ptr) + j * p.k.s_blk + b * p.k.s_batch + hk * p.k.s_head;
   const float* vbase = reinterpret_cast<const float*>(p.v.ptr) + j * p.v.s_blk + b * p.v.s_batch + hk * p.v.s_head;
-  for (int idx = tid; idx < kF32Keys * D; idx += kF32Keys) {
+  for (int idx = tid; idx < kF32Keys * D; idx += kF32Threads) {
     const int r = idx / D, e = idx % D;
     const int64_t x = kv0 + r;
     ks[r * L::S + e] = (x < p.Bb) ? kbase[x * p.k.s_tok + e] : 0.0f;
     vs[r * L::S + e] = (x < p.Bb) ? vbase[x * p.v.s_tok + e] : 0.0f;
   }
-  float dk[D], dv[D];
+  float dk[DQ], dv[DQ];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
+  for (int e = 0; e < DQ; ++e) {
     dk[e] = 0.0f;
     dv[e] = 0.0f;
   }
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
       for (int32_t qt = (int32_t)(a_first / kF32Rows); qt < qtiles; ++qt) {
         const int64_t q0 = (int64_t)qt * kF32Rows;
         __syncthreads();
-        for (int idx = tid; idx < kF32Rows * D; idx += kF32Keys) {
+        for (int idx = tid; idx < kF32Rows * D; idx += kF32Threads) {
           const int r = idx / D, e = idx % D;
           const int64_t x = q0 + r;
           qs[r * L::S + e] = (x < p.Bb) ? qbase[x * p.q.s_tok + e] : 0.0f;
@@ -723,16 +729,21 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
           const bool vis = key < p.Bb && a < p.Bb && a >= a_min;
           float s = 0.0f, dpv = 0.0f;
 #pragma unroll
-          for (int e = 0; e < D; ++e) {
-            s = fmaf(qs[r * L::S + e], ks[tid * L::S + e], s);
-            dpv = fmaf(os[r * L::S + e], vs[tid * L::S + e], dpv);
+          for (int e = 0; e < DQ; ++e) {
+            s = fmaf(qs[r * L::S + f0 + e], ks[kl * L::S + f0 + e], s);
+            dpv = fmaf(os[r * L::S + f0 + e], vs[kl * L::S + f0 + e], dpv);
           }
+          // the four quarters of this key's lanes (lanes 4k .. 4k+3)
+          s += __shfl_xor(s, 1);
+          s += __shfl_xor(s, 2);
+          dpv += __shfl_xor(dpv, 1);
+          dpv += __shfl_xor(dpv, 2);
           const float pv = vis ? fexp2(fmaf(s, c2, -lse_s[r])) : 0.0f;
           const float dsv = pv * (dpv - dsum_s[r]);
 #pragma unroll
-          for (int e = 0; e < D; ++e) {
-            dv[e] = fmaf(pv, os[r * L::S + e], dv[e]);
-            dk[e] = fmaf(dsv, qs[r * L::S + e], dk[e]);
+          for (int e = 0; e < DQ; ++e) {
+            dv[e] = fmaf(pv, os[r * L::S + f0 + e], dv[e]);
+            dk[e] = fmaf(dsv, qs[r * L::S + f0 + e], dk[e]);
           }
         }
       }
@@ -742,9 +753,9 @@ __global__ __launch_bounds__(kF32Keys) void dkdv_f32_kernel(BwdParams p) {
   float* dkrow = reinterpret_cast<float*>(p.dk.ptr) + j * p.dk.s_blk + b * p.dk.s_batch + key * p.dk.s_tok + hk * p.dk.s_head;
   float* dvrow = reinterpret_cast<float*>(p.dv.ptr) + j * p.dv.s_blk + b * p.dv.s_batch + key * p.dv.s_tok + hk * p.dv.s_head;
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    dkrow[e] = dk[e] * p.scale;
-    dvrow[e] = dv[e];
+  for (int e = 0; e < DQ; ++e) {
+    dkrow[f0 + e] = dk[e] * p.scale;
+    dvrow[f0 + e] = dv[e];
   }
 }
 
@@ -766,8 +777,8 @@ hipError_t launch_dkdv_bf16(const BwdParams& p, hipStream_t s) {
 
 hipError_t launch_dkdv_f32(const BwdParams& p, hipStream_t s) {
   const int64_t grid = ((p.Bb + kF32Keys - 1) / kF32Keys) * (int64_t)p.P * p.B * p.Hk;
-  if (p.D == 128) return launch_dyn(dkdv_f32_kernel<128>, grid, kF32Keys, BwdF32Lds<128>::BYTES, s, p);
-  return launch_dyn(dkdv_f32_kernel<64>, grid, kF32Keys, BwdF32Lds<64>::BYTES, s, p);
+  if (p.D == 128) return launch_dyn(dkdv_f32_kernel<128>, grid, kF32Threads, BwdF32Lds<128>::BYTES, s, p);
+  return launch_dyn(dkdv_f32_kernel<64>, grid, kF32Threads, BwdF32Lds<64>::BYTES, s, p);
 }
 
 }  // namespace ra

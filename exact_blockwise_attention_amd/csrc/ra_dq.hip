@@ -262,16 +262,22 @@ __global__ __launch_bounds__(kQThreads, 1) void dq_bf16_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Plain VALU kernel for float32: one lane per query row, KV tiles staged in
-// LDS and read as broadcasts; same ring walk and masks as the forward.
+// Plain VALU kernel for float32: kF32Split lanes per query row, each holding
+// a quarter of the row's features (Q, dO and the dQ accumulator); the S and
+// dP dot products add the quarters with two lane exchanges. KV tiles are
+// staged in LDS; same ring walk and masks as the forward.
 constexpr int kF32Rows = 64;
+constexpr int kF32Split = 4;  // lanes per row
+constexpr int kF32Threads = kF32Rows * kF32Split;
 
 template <int D>
-__global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
+__global__ __launch_bounds__(kF32Threads) void dq_f32_kernel(BwdParams p) {
   constexpr int TN = 2048 / D;  // keys per staged tile: 16 KiB of LDS for K and V
+  constexpr int DQ = D / kF32Split;
   __shared__ float ks[TN][D];
   __shared__ float vs[TN][D];
   const int tid = threadIdx.x;
+  const int f0 = (tid % kF32Split) * DQ;  // this lane's first feature
   const int32_t BH = p.B * p.H;
   const int32_t Bb = (int32_t)p.Bb;
   const int32_t tiles = (Bb + kF32Rows - 1) / kF32Rows;
@@ -283,16 +289,16 @@ __global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
   query_tile_of(p.causal, p.layout, p.n_ranks, id / BH, tiles, &ri, &tile);
   const int32_t i = p.rank_begin + ri;
   const int32_t a0 = tile * kF32Rows;
-  const int32_t a = a0 + tid;
+  const int32_t a = a0 + tid / kF32Split;
   const int32_t a_hi = (a0 + kF32Rows - 1 < Bb - 1) ? a0 + kF32Rows - 1 : Bb - 1;
   const bool live = a < Bb;
   const float* qrow = reinterpret_cast<const float*>(p.q.ptr) + ri * p.q.s_blk + b * p.q.s_batch +
-                      (int64_t)a * p.q.s_tok + h * p.q.s_head;
+                      (int64_t)a * p.q.s_tok + h * p.q.s_head + f0;
   const float* orow = reinterpret_cast<const float*>(p.dout.ptr) + ri * p.dout.s_blk + b * p.dout.s_batch +
-                      (int64_t)a * p.dout.s_tok + h * p.dout.s_head;
-  float qv[D], ov[D], dq[D];
+                      (int64_t)a * p.dout.s_tok + h * p.dout.s_head + f0;
+  float qv[DQ], ov[DQ], dq[DQ];
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
+  for (int e = 0; e < DQ; ++e) {
     qv[e] = live ? qrow[e] : 0.0f;
     ov[e] = live ? orow[e] : 0.0f;
     dq[e] = 0.0f;
@@ -313,35 +319,39 @@ __global__ __launch_bounds__(kF32Rows) void dq_f32_kernel(BwdParams p) {
                          (h / p.G) * p.v.s_head;
     for (int32_t b0 = 0; b0 < extent; b0 += TN) {
       __syncthreads();
-      for (int idx = tid; idx < TN * D; idx += kF32Rows) {
+      for (int idx = tid; idx < TN * D; idx += kF32Threads) {
         const int r = idx / D, e = idx % D;
         const int32_t x = b0 + r;
         ks[r][e] = (x < Bb) ? kbase[(int64_t)x * p.k.s_tok + e] : 0.0f;
         vs[r][e] = (x < Bb) ? vbase[(int64_t)x * p.v.s_tok + e] : 0.0f;
       }
       __syncthreads();
-      if (!live) continue;
+      if (!live) continue;  // the four lanes of a row leave together
       for (int u = 0; u < TN; ++u) {
         const int32_t kb = b0 + u;
         float s = 0.0f, dpv = 0.0f;
 #pragma unroll
-        for (int e = 0; e < D; ++e) {
-          s = fmaf(qv[e], ks[u][e], s);
-          dpv = fmaf(ov[e], vs[u][e], dpv);
+        for (int e = 0; e < DQ; ++e) {
+          s = fmaf(qv[e], ks[u][f0 + e], s);
+          dpv = fmaf(ov[e], vs[u][f0 + e], dpv);
         }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        dpv += __shfl_xor(dpv, 1);
+        dpv += __shfl_xor(dpv, 2);
         const bool vis = kb < ext_a;
         const float pv = vis ? fexp2(fmaf(s, c2, -lse2)) : 0.0f;
         const float dsv = pv * (dpv - dsum);
 #pragma unroll
-        for (int e = 0; e < D; ++e) dq[e] = fmaf(dsv, ks[u][e], dq[e]);
+        for (int e = 0; e < DQ; ++e) dq[e] = fmaf(dsv, ks[u][f0 + e], dq[e]);
       }
     }
   }
   if (!live) return;
   float* drow = reinterpret_cast<float*>(p.dq.ptr) + ri * p.dq.s_blk + b * p.dq.s_batch + (int64_t)a * p.dq.s_tok +
-                h * p.dq.s_head;
+                h * p.dq.s_head + f0;
 #pragma unroll
-  for (int e = 0; e < D; ++e) drow[e] = dq[e] * p.scale;
+  for (int e = 0; e < DQ; ++e) drow[e] = dq[e] * p.scale;
 }
 
 }  // namespace
@@ -365,9 +375,9 @@ hipError_t launch_dq_f32(const BwdParams& p, hipStream_t s) {
   const int64_t grid = ((p.Bb + kF32Rows - 1) / kF32Rows) * (int64_t)p.n_ranks * p.B * p.H;
   if (grid <= 0) return hipSuccess;
   if (p.D == 128) {
-    hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((uint32_t)grid), dim3(kF32Rows), 0, s, p);
+    hipLaunchKernelGGL(dq_f32_kernel<128>, dim3((uint32_t)grid), dim3(kF32Threads), 0, s, p);
   } else {
-    hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((uint32_t)grid), dim3(kF32Rows), 0, s, p);
+    hipLaunchKernelGGL(dq_f32_kernel<64>, dim3((uint32_t)grid), dim3(kF32Threads), 0, s, p);
   }
   return hipGetLastError();
 }
