@@ -172,13 +172,19 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
 
   // per-lane source offsets (bytes, from the tile's first row) of the rows
   // this wave copies, and their swizzled chunk
+  // (crow: the row, c16: the chunk's byte offset, for the copies of a tile
+  // cut by the block's end)
   uint32_t dk[DM::CPW], dv[DM::CPW];
+  int32_t crow[DM::CPW];
+  uint32_t c16[DM::CPW];
 #pragma unroll
   for (int kc = 0; kc < DM::CPW; ++kc) {
     const int row = (wave + kQWaves * kc) * DM::RW + lane / DM::CPR;
     const int c = (lane % DM::CPR) ^ chunk_swz<D>(row);
     dk[kc] = (uint32_t)(2 * ((int64_t)row * p.k.s_tok + 8 * c));
     dv[kc] = (uint32_t)(2 * ((int64_t)row * p.v.s_tok + 8 * c));
+    crow[kc] = row;
+    c16[kc] = 16 * c;
   }
   const int64_t kvblk_mul = (p.mode == 1) ? 0 : 1;  // the single-step buffer holds one block
   auto kv_base = [&](const Seq& sq, int32_t blk, int32_t r_lo) __attribute__((always_inline)) {
@@ -229,19 +235,16 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     c.lim = Bb - 1 - r_lo;
     return c;
   };
+  // (no branch: the matrix phase has LDS reads in flight around the copies)
   auto copy_one = [&](const CopySrc& c, auto STc, int I) __attribute__((always_inline)) {
     constexpr int ST = decltype(STc)::value;
     const bool isv = I >= DM::CPW;
     const int kc = I % DM::CPW;
     const int q = wave + kQWaves * kc;
-    uint32_t off = isv ? dv[kc] : dk[kc];
-    if (c.lim < kKvTn - 1) {
-      // a tile cut by the block's end: rows past it read the last row
-      int row = q * DM::RW + lane / DM::CPR;
-      const int ch = (lane % DM::CPR) ^ chunk_swz<D>(row);
-      if (row > c.lim) row = c.lim;
-      off = (uint32_t)(2 * ((int64_t)row * (isv ? p.v.s_tok : p.k.s_tok) + 8 * ch));
-    }
+    // a tile cut by the block's end: rows past it read the last row
+    const int32_t lim = c.lim < kKvTn - 1 ? c.lim : kKvTn - 1;
+    const uint32_t last = (uint32_t)(2 * (int64_t)lim * (isv ? p.v.s_tok : p.k.s_tok)) + c16[kc];
+    const uint32_t off = crow[kc] > lim ? last : (isv ? dv[kc] : dk[kc]);
     unsigned char* dst = smem_raw + (isv ? L::VBASE_B : 0) + ST * L::TILE_B + q * 1024;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const __bf16*>((isv ? c.vb : c.kb) + off),
                                      (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   // Matrix phase: scores of the tile in stage SK (if any) and O^T += V^T P^T
   // with the V tile in stage SV. The V^T fragments of one 32-feature group
   // (4 k-steps x 2 halves) are requested one group ahead of their MFMAs.
-  auto matrix = [&](auto SKc, auto SVc, bool with_scores, const CopySrc& cs, auto SCc) __attribute__((always_inline)) {
+  auto matrix = [&](auto SKc, auto SVc, const CopySrc& cs, auto SCc) __attribute__((always_inline)) {
     constexpr int SV = decltype(SVc)::value;
     u32x2 vf[2][4][2];
     auto request = [&](u32x2(&r)[4][2], int dt) __attribute__((always_inline)) {
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       r[3][1] = tr_read_at<SV * L::TILE_B + 3 * 16 * D * 2>(o1);
     };
     request(vf[0], 0);
-    if (with_scores) scores(SKc);
+    scores(SKc);  // on the last tile: of the spare copy in stage SK (finite, unused)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       if (dt + 1 < D / 32) {
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       wg_barrier();
       const CopySrc cs = copy_src(itd);  // tile t+3 into the stage tile t-1 freed
       if (busy) {
-        matrix(ic<(U + 1) % 4>{}, ic<U>{}, has_next, cs, ic<(U + 3) % 4>{});
+        matrix(ic<(U + 1) % 4>{}, ic<U>{}, cs, ic<(U + 3) % 4>{});
       } else {
 #pragma unroll
         for (int c = 0; c < DM::NI; ++c) copy_one(cs, ic<(U + 3) % 4>{}, c);
