@@ -87,34 +87,78 @@ __global__ __launch_bounds__(256) void merge_lse_vec_kernel(int64_t rows, const 
 // correction as merge_lse_kernel, over n_split partials. Partial s of row r
 // is the normalised O at st_o[(s * rows + r) * D] and its lse in log2 units
 // at st_lse[s * rows + r]; a run that saw no key has lse -inf and weight 0.
-// D / 4 lanes per row, four features each. Row r = ((ri * B + b) * H + h) *
-// Bb + a.
+// Row r = ((ri * B + b) * H + h) * Bb + a.
+//
+// The rows are few (a short query block), so the kernel is bound by load
+// latency: one wave per row, split into G groups of D/8 lanes (8 features
+// each). Group g takes partials g, g + G, ..., kMergeBatch at a time with
+// all their loads in flight, keeps its own (max, sum, accumulator), and the
+// groups combine by lane exchanges.
+constexpr int kMergeBatch = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_splits_kernel(FwdParams p) {
-  constexpr int LPR = D / 4;
+  constexpr int LPR = D / 8;    // lanes per copy of a row
+  constexpr int G = 64 / LPR;   // partial groups per row
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
-  const int64_t r = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int e = 4 * (threadIdx.x % LPR);
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // uniform over the wave
   if (r >= rows) return;
-  // unrolled so that many partials' loads are in flight at once (the grid
-  // is small: a few hundred rows)
-  float mx = -INFINITY;
-#pragma unroll 16
-  for (int32_t s = 0; s < p.n_split; ++s) mx = fmaxf(mx, p.st_lse[s * rows + r]);
-  const float ms = (mx == -INFINITY) ? 0.0f : mx;
-  float tot = 0.0f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-  for (int32_t s = 0; s < p.n_split; ++s) {
-    const float w = exp2f(p.st_lse[s * rows + r] - ms);
-    const float4 u = *reinterpret_cast<const float4*>(p.st_o + (s * rows + r) * D + e);
-    tot += w;
-    acc.x += w * u.x;
-    acc.y += w * u.y;
-    acc.z += w * u.z;
-    acc.w += w * u.w;
+  const int lane = threadIdx.x % 64;
+  const int g = lane / LPR;
+  const int e = 8 * (lane % LPR);
+  float m = -INFINITY, l = 0.0f;  // group max and sum (log2 units, relative to m)
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
+  for (int32_t s0 = g; s0 < p.n_split; s0 += kMergeBatch * G) {
+    float lv[kMergeBatch];
+    float4 u[kMergeBatch][2];
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int32_t sk = s0 + k * G;
+      const bool ok = sk < p.n_split;
+      const int64_t at = (int64_t)(ok ? sk : 0) * rows + r;
+      lv[k] = ok ? p.st_lse[at] : -INFINITY;
+      u[k][0] = *reinterpret_cast<const float4*>(p.st_o + at * D + e);
+      u[k][1] = *reinterpret_cast<const float4*>(p.st_o + at * D + e + 4);
+    }
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) mb = fmaxf(mb, lv[k]);
+    const float ms = (mb == -INFINITY) ? 0.0f : mb;
+    const float c = (m == -INFINITY) ? 0.0f : exp2f(m - ms);  // rescales what the group has
+    l *= c;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] *= c;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float w = exp2f(lv[k] - ms);  // 0 for a run that saw no key (and past n_split)
+      l += w;
+      const float uv[8] = {u[k][0].x, u[k][0].y, u[k][0].z, u[k][0].w, u[k][1].x, u[k][1].y, u[k][1].z, u[k][1].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += w * uv[q];
+    }
+    m = mb;
   }
-  const float inv = (tot > 0.0f) ? 1.0f / tot : 0.0f;
+  // combine the G groups (lanes LPR apart)
+#pragma unroll
+  for (int off = LPR; off < 64; off *= 2) {
+    const float mo = __shfl_xor(m, off);
+    const float lo = __shfl_xor(l, off);
+    const float mn = fmaxf(m, mo);
+    const float ms = (mn == -INFINITY) ? 0.0f : mn;
+    const float a = (m == -INFINITY) ? 0.0f : exp2f(m - ms);
+    const float b = (mo == -INFINITY) ? 0.0f : exp2f(mo - ms);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float ao = __shfl_xor(acc[q], off);
+      acc[q] = acc[q] * a + ao * b;
+    }
+    l = l * a + lo * b;
+    m = mn;
+  }
+  if (g != 0) return;
+  const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
   const int32_t a = (int32_t)(r % p.Bb);
   const int64_t t = r / p.Bb;
   const int32_t h = (int32_t)(t % p.H);
@@ -122,10 +166,15 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(FwdParams p) {
   const int32_t ri = (int32_t)(t / p.H / p.B);
   __bf16* orow = reinterpret_cast<__bf16*>(p.o.ptr) + ri * p.o.s_blk + b * p.o.s_batch + (int64_t)a * p.o.s_tok +
                  h * p.o.s_head;
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 w4 = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv), (__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
-  *reinterpret_cast<bf16x4*>(orow + e) = w4;
-  if (e == 0) p.lse[r] = (tot > 0.0f) ? (ms + log2f(tot)) * 0.69314718055994530942f : -INFINITY;
+  typedef __bf16 b16x8 __attribute__((ext_vector_type(8)));
+  b16x8 w8;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) w8[q] = (__bf16)(acc[q] * inv);
+  *reinterpret_cast<b16x8*>(orow + e) = w8;
+  if (e == 0) {
+    const float ms = (m == -INFINITY) ? 0.0f : m;
+    p.lse[r] = (l > 0.0f) ? (ms + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+  }
 }
 
 // Copies 16-byte chunks of one ring block of a strided sequence tensor into
@@ -272,8 +321,7 @@ hipError_t launch_merge_lse(int64_t rows, int32_t d, const float* oa, const floa
 hipError_t launch_merge_splits(const FwdParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
   if (rows <= 0) return hipSuccess;
-  const int64_t per_block = 256 / (p.D / 4);
-  const int64_t grid = (rows + per_block - 1) / per_block;
+  const int64_t grid = (rows + 3) / 4;  // a wave per row
   if (p.D == 128)
     hipLaunchKernelGGL(merge_splits_kernel<128>, dim3((uint32_t)grid), dim3(256), 0, s, p);
   else
