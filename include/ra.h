@@ -129,12 +129,17 @@ typedef struct {
   int64_t s_head;
 } ra_seq;
 
-/* Bytes of workspace ra_forward (backward = 0) or ra_backward (backward = 1)
- * needs for ranks [rank_begin, rank_end). use_copy_stream selects the
+/* Bytes of workspace ra_forward (backward = 0) or ra_backward (backward = 1
+ * or 2) needs for ranks [rank_begin, rank_end). use_copy_stream selects the
  * forward's double-buffered receive mode. Without it, a bf16 forward of a
  * single rank whose query block is too small to fill the GPU asks for the
- * partial states of its split launch (see ra_forward). Returns 0 for an
- * invalid problem (and when no workspace is needed). */
+ * partial states of its split launch (see ra_forward). For the backward,
+ * backward = 2 gives the smallest workspace (8 bytes per query row: D and
+ * lse), with which dQ recomputes the scores; backward = 1 the size with
+ * which a bf16 backward also stores dS once (K in operand order and 2 bytes
+ * per visible pair, in 64 x 128 tiles) and forms dQ from it, the faster path.
+ * The two are equal when dS is not stored (fp32, block_len above 2^18).
+ * Returns 0 for an invalid problem (and when no workspace is needed). */
 size_t ra_workspace_bytes(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
                           int32_t use_copy_stream, int32_t backward);
 
@@ -175,13 +180,18 @@ ra_status ra_forward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
  * rowsum(dO * O) is computed first from the given O (into the workspace).
  * Each KV block visits the query blocks of ranks [rank_begin, rank_end) in
  * ring order ((j + k) mod P at step k) carrying its dK/dV accumulators on
- * chip; then each query block of the range walks the KV blocks in ring order
- * ((i - k) mod P) carrying its dQ accumulator. No atomics: the result is
- * deterministic.
+ * chip. With the workspace of ra_workspace_bytes(..., 1) (bf16) that walk
+ * writes dS once and dQ = scale * dS K is formed from it, each query tile's
+ * sum on chip over the KV blocks in ring order; with the smaller workspace
+ * of ra_workspace_bytes(..., 2) each query block walks the KV blocks again
+ * ((i - k) mod P), recomputing S and dP. No atomics on either path: the
+ * result is deterministic, and dK, dV are the same bits on both.
  *   q, o, dout, dq, lse: indexed by i - rank_begin; k, v, dk, dv: absolute.
  *   dk, dv receive the contributions of the ranks in range (all P ranks:
  *   the full gradient). Blocks of dk/dv are written for every j.
- *   workspace: ra_workspace_bytes(pb, rb, re, 0, 1) bytes. */
+ *   workspace: at least ra_workspace_bytes(pb, rb, re, 0, 2) bytes (else
+ *   RA_ERR_WORKSPACE); ra_workspace_bytes(pb, rb, re, 0, 1) or more selects
+ *   the stored-dS path. */
 ra_status ra_backward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end,
                       const ra_seq* q, const ra_seq* k, const ra_seq* v, const ra_seq* o,
                       const ra_seq* dout, const float* lse, const ra_seq* dq,
@@ -190,11 +200,14 @@ ra_status ra_backward(const ra_problem* pb, int32_t rank_begin, int32_t rank_end
 
 /* One stage of ra_backward, with the same arguments (ra_backward runs stages
  * 0, 1, 2 in order on `compute`): 0 = D = rowsum(dO * O), and lse in base-2
- * units, into the workspace;
- * 1 = the key-side ring walk (recompute S and P, dP, dS; dV and dK);
- * 2 = the query-side ring walk (recompute S, P, dP, dS; dQ). Stages 1 and 2
- * read the workspace, so stage 0 must complete first; lets a caller time or interleave
- * the stages. Unknown stage: RA_ERR_SHAPE. */
+ * units, into the workspace (on the stored-dS path also K in operand order);
+ * 1 = the key-side ring walk (recompute S and P, dP, dS; dV and dK; on the
+ * stored-dS path dS is written);
+ * 2 = dQ: from the stored dS, or by the query-side ring walk that recomputes
+ * S, P, dP and dS. Each stage reads what the ones before it wrote, so they
+ * must run in order; lets a caller time or interleave the stages. The
+ * workspace size selects the path as in ra_backward and must be the same
+ * for all three stages. Unknown stage: RA_ERR_SHAPE. */
 ra_status ra_backward_stage(int32_t stage, const ra_problem* pb, int32_t rank_begin,
                             int32_t rank_end, const ra_seq* q, const ra_seq* k, const ra_seq* v,
                             const ra_seq* o, const ra_seq* dout, const float* lse,
@@ -203,8 +216,10 @@ ra_status ra_backward_stage(int32_t stage, const ra_problem* pb, int32_t rank_be
 
 /* ra_backward without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
- * that forbid allocation): the same computation and kernels as ra_backward,
- * with D and lse in base-2 units (8 bytes per query row of the range) kept
+ * that forbid allocation): the same computation and kernels as ra_backward
+ * on its smallest workspace (dQ by the recomputing walk; dK, dV the same
+ * bits as ra_backward's), with D and lse in base-2 units (8 bytes per query
+ * row of the range) kept
  * in a static device array of ra_backward_noalloc_max_bytes() bytes (64 MiB:
  * 8M query rows, e.g. 8 ranks x 32 heads x 32768 rows), one per GPU, held
  * until the process ends. The array used is the current device's (the
