@@ -427,6 +427,9 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       const bool has_next = nx.next();
       if (!g1) wait_vm<DM::NI>();  // tile t+1 (its K is read now)
       wg_barrier();
+      // the matrix phase takes the SIMD's issue slots first: the hardware
+      // otherwise favours the older waves (group 0) in both phases
+      __builtin_amdgcn_s_setprio(1);
       const CopySrc cs = copy_src(itd);  // tile t+3 into the stage tile t-1 freed
       if (busy) {
         matrix(ic<(U + 1) % 4>{}, ic<U>{}, cs, ic<(U + 3) % 4>{});
@@ -436,6 +439,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       }
       dadv();
       if (g1) wait_vm<DM::NI>();  // tile t+2, read by group 0 in the next phase
+      __builtin_amdgcn_s_setprio(0);
       wg_barrier();
       if (has_next) {
         its = nx;
