@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     const int32_t b0 = t.t * kKvTn;
     // the wave's first row sees the fewest keys (row extents grow with the
     // row; they never exceed Bb, which covers the ragged last tile)
-    if (row_extent32(t.rel, aw) < b0 + kKvTn) {
+    if (t.ext_w < b0 + kKvTn) {
       // key b0 + off is visible iff off < ext(a) - b0
       const int32_t lim = row_extent32(t.rel, a) - 1 - b0;
 #pragma unroll
@@ -378,17 +378,32 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   first.causal = p.causal;
   first.a_hi = a_hi;
   first.Bb = Bb;
+  first.a_w = aw;
   if (first.next_block()) {
     // DMA walk: sticks at the last tile once the walk is done, so that the
     // copies issued for tiles past the end re-read valid rows into a free
     // stage and every wave issues the same number of loads per phase.
     KvIter itd = first;
     bool dvalid = true;
+    // the copies' source rows follow the walk: one tile further down the
+    // same block, or a new block's first tile
+    CopySrc cur = copy_src(itd);
+    const int64_t kadv = 2 * (int64_t)kKvTn * p.k.s_tok, vadv = 2 * (int64_t)kKvTn * p.v.s_tok;
     auto dadv = [&]() __attribute__((always_inline)) {
       if (dvalid) {
         KvIter nx = itd;
-        if (nx.next()) itd = nx;
-        else dvalid = false;
+        if (nx.next()) {
+          if (nx.t == 0) {
+            cur = copy_src(nx);
+          } else {
+            cur.kb += kadv;
+            cur.vb += vadv;
+            cur.lim -= kKvTn;
+          }
+          itd = nx;
+        } else {
+          dvalid = false;
+        }
       }
     };
     // prologue: tiles 0..2 (group 1 also tile 3, which group 0 requests in
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(kQThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       // the matrix phase takes the SIMD's issue slots first: the hardware
       // otherwise favours the older waves (group 0) in both phases
       __builtin_amdgcn_s_setprio(1);
-      const CopySrc cs = copy_src(itd);  // tile t+3 into the stage tile t-1 freed
+      const CopySrc cs = cur;  // tile t+3 into the stage tile t-1 freed
       if (busy) {
         matrix(ic<(U + 1) % 4>{}, ic<U>{}, cs, ic<(U + 3) % 4>{});
       } else {

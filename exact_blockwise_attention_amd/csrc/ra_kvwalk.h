@@ -129,6 +129,7 @@ struct KvIter {
   int32_t kstep, nsteps, j, t, ntile;
   BlockRel rel;
   int32_t i, P, layout, causal, a_hi, Bb, single_block;
+  int32_t a_w, ext_w;  // a row of the caller's choice and its extent in the block
   // moves to the next block with a visible tile; false when the ring is done
   __device__ bool next_block() {
     while (++kstep < nsteps) {
@@ -137,6 +138,7 @@ struct KvIter {
       const int32_t extent = row_extent32(rel, a_hi);
       if (extent <= 0) continue;
       ntile = (extent + kKvTn - 1) / kKvTn;
+      ext_w = row_extent32(rel, a_w);
       t = 0;
       return true;
     }
