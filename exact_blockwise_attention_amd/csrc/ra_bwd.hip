@@ -72,14 +72,14 @@ constexpr int kRawRsrcWord3 = 0x00020000;  // untyped 32-bit data, bounds-checke
 template <int D>
 struct BwdLds {
   static constexpr int QST_B = kQm * D * 2;         // one tile of Q (or dO), bytes
-  static constexpr int DO_B = QST_B;                // dO after Q in each stage
-  static constexpr int STG_B = 2 * QST_B;           // one stage: Q, then dO
-  static constexpr int F32_B = kNst * STG_B;        // lse2[4][64], then dsum[4][64], then 2 spare rows
+  static constexpr int DO0 = kNst * QST_B;          // the dO tiles of the stages, after their Q tiles
+  static constexpr int F32_B = 2 * kNst * QST_B;    // lse2[4][64], then dsum[4][64], then 2 spare rows
   static constexpr int DS_B = kNst * kQm * 4;      // dsum after lse2
   static constexpr int SPARE_B = F32_B + 2 * DS_B;  // [2][64] floats, written by waves 2 and 3
   static constexpr int BYTES = SPARE_B + 2 * kQm * 4;
   static_assert(BYTES <= 160 * 1024, "LDS");
-  static_assert(DO_B + 48 * D * 2 < 65536, "DS offsets are 16 bits");
+  // a read names its stage in the instruction's offset (from a Q or a dO base)
+  static_assert((kNst - 1) * QST_B + 48 * D * 2 < 65536, "DS offsets are 16 bits");
 };
 
 // s_waitcnt lgkmcnt(N) with the registers of one read group tied to it.
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       constexpr int N16 = L::QST_B / 16;
 #pragma unroll
       for (int k = 0; k < N16 / kThreads; ++k) {
-        reinterpret_cast<u32x4*>(smem_raw + 3 * L::STG_B)[tid + k * kThreads] = z;
-        reinterpret_cast<u32x4*>(smem_raw + 3 * L::STG_B + L::DO_B)[tid + k * kThreads] = z;
+        reinterpret_cast<u32x4*>(smem_raw + 3 * L::QST_B)[tid + k * kThreads] = z;
+        reinterpret_cast<u32x4*>(smem_raw + L::DO0 + 3 * L::QST_B)[tid + k * kThreads] = z;
       }
     }
 
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       for (int k = 0; k < NCP; ++k) {
         const int qc = wave + kWaves * k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rq, (__attribute__((address_space(3))) void*)(smem_raw + stage * L::STG_B + qc * 1024), 16,
+            rq, (__attribute__((address_space(3))) void*)(smem_raw + stage * L::QST_B + qc * 1024), 16,
             vq + k * kWaves * RW * sq2, 0, 0, 0);
       }
     };
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       for (int k = 0; k < NCP; ++k) {
         const int qc = wave + kWaves * k;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ro, (__attribute__((address_space(3))) void*)(smem_raw + stage * L::STG_B + L::DO_B + qc * 1024), 16,
+            ro, (__attribute__((address_space(3))) void*)(smem_raw + L::DO0 + stage * L::QST_B + qc * 1024), 16,
             vo + k * kWaves * RW * so2, 0, 0, 0);
       }
     };
@@ -362,31 +362,31 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     wg_barrier();
 
     const float c2 = p.scale_log2;
-    // LDS byte addresses of this lane's reads, for the current tile's stage
-    // st (and its neighbours):
-    //   cq[ss]: Q row n of stage st, columns 16ss + 8hf (row block 1: + 32
-    //     rows; dO: + DO_B); cqn[ss]: the same in stage st + 1
-    //   cl: lse2 of rows 4hf .. +3 of stage st (+ 8gg + 32rb; D: + DS_B)
-    //   pqc[h2][dt]: transposing reads of stage st: Q rows 4hf + j16/4 + 8h2
-    //     (chunk kc: + 16 rows; dO: + DO_B), columns 32dt + 16grp +
-    //     4(j16%4); pqp[h2][dt]: the same in stage st - 1
+    // LDS byte addresses of this lane's reads in stage 0; a read adds its
+    // stage's offset (stage x QST_B, or x 256 for lse2 / D) in the
+    // instruction:
+    //   cq[ss] / co[ss]: Q / dO row n, columns 16ss + 8hf (row block 1: + 32
+    //     rows)
+    //   cl: lse2 of rows 4hf .. +3 (+ 8gg + 32rb; D: + DS_B)
+    //   pq[h2][dt] / po[h2][dt]: transposing reads of Q / dO rows 4hf +
+    //     j16/4 + 8h2 (chunk kc: + 16 rows), columns 32dt + 16grp + 4(j16%4)
     const uint32_t lbase = lds_addr(smem_raw);
-    uint32_t cq[NSS], cqn[NSS], pqc[2][NDT], pqp[2][NDT];
+    uint32_t cq[NSS], co[NSS], pq[2][NDT], po[2][NDT];
 #pragma unroll
     for (int ss = 0; ss < NSS; ++ss) {
       const uint32_t c = 2 * tile_off<D>(n, 16 * ss + 8 * hf);
       cq[ss] = lbase + c;
-      cqn[ss] = lbase + L::STG_B + c;
+      co[ss] = lbase + L::DO0 + c;
     }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const uint32_t c = 2 * tile_off<D>(4 * hf + j16 / 4 + 8 * h2, 32 * dt + 16 * grp + 4 * (j16 % 4));
-        pqc[h2][dt] = lbase + c;
-        pqp[h2][dt] = lbase + 3 * L::STG_B + c;
+        pq[h2][dt] = lbase + c;
+        po[h2][dt] = lbase + L::DO0 + c;
       }
-    uint32_t cl = lbase + L::F32_B + 4 * (4 * hf);
+    const uint32_t cl = lbase + L::F32_B + 4 * (4 * hf);
 
     // The step is a two-phase software pipeline over the tile's two row
     // blocks of 32 rows. Phase A: S / dP of row block 1 of tile t, P / dS
@@ -422,21 +422,24 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     };
 
     // One phase, NSS slots. Slot SS: the S / dP products of feature step SS
-    // of the row block read through ca (+ROFF bytes) into (sx, dx); the
-    // dV^T and dK^T products of pair SS (feature tile SS/2, chunk KC0 + SS%2)
-    // read through ta_ with B operands (pi, di); and EPS elements of P / dS
-    // of row block RBP of the current tile from (sp, dp), lse2 / D rows at
-    // LOFF, into (po, dq_). The reads of slot SS + 1 go out before slot SS
+    // of the row block at ROFF bytes of stage SC into (sx, dx); the dV^T and
+    // dK^T products of pair SS (feature tile SS/2, chunk KC0 + SS%2) of
+    // stage ST with B operands (pi, di); and EPS elements of P / dS of row
+    // block RBP of the current tile from (sp, dp), lse2 / D rows at LOFF of
+    // stage SL, into (pw, dw). The reads of slot SS + 1 go out before slot SS
     // waits for its own.
     constexpr int EPS = 16 / NSS;  // P / dS elements per slot
     static_assert(EPS * NSS == 16 && 4 * NDT == 2 * NSS, "slot shape");
-    auto phase = [&](auto MASKc, auto RBPc, auto KC0c, auto ROFFc, auto LOFFc, const uint32_t(&ca)[NSS],
-                     const uint32_t(&ta_)[2][NDT], f32x16& sx, f32x16& dx, const f32x16& sp, const f32x16& dp,
-                     bf16x8(&po)[2], bf16x8(&dq_)[2], const bf16x8(&pi)[2], const bf16x8(&di)[2], int32_t clo,
+    auto phase = [&](auto MASKc, auto RBPc, auto KC0c, auto ROFFc, auto LOFFc, auto SCc, auto STc, auto SLc,
+                     f32x16& sx, f32x16& dx, const f32x16& sp, const f32x16& dp, bf16x8(&pw)[2], bf16x8(&dw)[2],
+                     const bf16x8(&pi)[2], const bf16x8(&di)[2], int32_t clo,
                      auto&& at_slot) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(MASKc)::value != 0;
       constexpr int RBP = decltype(RBPc)::value, KC0 = decltype(KC0c)::value;
       constexpr int ROFF = decltype(ROFFc)::value, LOFF = decltype(LOFFc)::value;
+      constexpr int SQ = decltype(SCc)::value * L::QST_B + ROFF;  // S / dP reads
+      constexpr int ST = decltype(STc)::value * L::QST_B;         // dV^T / dK^T reads
+      constexpr int SL = decltype(SLc)::value * kQm * 4 + LOFF;   // lse2 / D reads
       u32x4 ra[2][2];
       u32x2 tr[2][4];
       u32x4 rl[2][2];
@@ -445,16 +448,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       auto reads = [&](auto SSc) __attribute__((always_inline)) {
         constexpr int SS = decltype(SSc)::value;
         constexpr int sl = SS & 1, dt = SS / 2, kc = KC0 + SS % 2;
-        ra[sl][0] = lds_read16<ROFF>(ca[SS]);
-        ra[sl][1] = lds_read16<L::DO_B + ROFF>(ca[SS]);
-        tr[sl][0] = tr_read_at<L::DO_B + kc * 16 * D * 2>(ta_[0][dt]);
-        tr[sl][1] = tr_read_at<L::DO_B + kc * 16 * D * 2>(ta_[1][dt]);
-        tr[sl][2] = tr_read_at<kc * 16 * D * 2>(ta_[0][dt]);
-        tr[sl][3] = tr_read_at<kc * 16 * D * 2>(ta_[1][dt]);
+        ra[sl][0] = lds_read16<SQ>(cq[SS]);
+        ra[sl][1] = lds_read16<SQ>(co[SS]);
+        tr[sl][0] = tr_read_at<ST + kc * 16 * D * 2>(po[0][dt]);
+        tr[sl][1] = tr_read_at<ST + kc * 16 * D * 2>(po[1][dt]);
+        tr[sl][2] = tr_read_at<ST + kc * 16 * D * 2>(pq[0][dt]);
+        tr[sl][3] = tr_read_at<ST + kc * 16 * D * 2>(pq[1][dt]);
         if constexpr ((SS * EPS) % 4 == 0) {
           constexpr int gg = SS * EPS / 4;
-          rl[gg & 1][0] = lds_read16<LOFF + gg * 32>(cl);
-          rl[gg & 1][1] = lds_read16<L::DS_B + LOFF + gg * 32>(cl);
+          rl[gg & 1][0] = lds_read16<SL + gg * 32>(cl);
+          rl[gg & 1][1] = lds_read16<L::DS_B + SL + gg * 32>(cl);
         }
       };
       constexpr auto nreads = [](int SS) { return 6 + ((SS * EPS) % 4 == 0 ? 2 : 0); };
@@ -485,8 +488,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
             if (32 * RBP + 8 * gg + e < clo) pv = 0.0f;
           }
           const float dsv = pv * (dp[i] - dd[e]);
-          po[gg / 2][4 * (gg % 2) + e] = (__bf16)pv;
-          dq_[gg / 2][4 * (gg % 2) + e] = (__bf16)dsv;
+          pw[gg / 2][4 * (gg % 2) + e] = (__bf16)pv;
+          dw[gg / 2][4 * (gg % 2) + e] = (__bf16)dsv;
         }
         dx = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dx);
         dk[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[sl][2], tr[sl][3], 0, 1, 2, 3)), di[c],
@@ -494,12 +497,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         // keeps the conversions of a finished chunk where they are
         if constexpr (((SS + 1) * EPS) % 8 == 0) {
           constexpr int ch = ((SS + 1) * EPS) / 8 - 1;
-          asm volatile("" : "+v"(po[ch]), "+v"(dq_[ch]));
+          asm volatile("" : "+v"(pw[ch]), "+v"(dw[ch]));
         }
       });
     };
 
-    int32_t st = 0;
+    int32_t st = 0;  // stage of the current tile
     bool v0 = true;
     unsigned char* const ds_lane = reinterpret_cast<unsigned char*>(p.ds) + (32 * wave + n) * 32 + hf * 16;
     // dS chunks C0, C0 + 1 of stored tile `tix`: lane (hf, n) writes its
@@ -517,13 +520,13 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     {
       u32x4 ra[2][2];
       ra[0][0] = lds_read16<0>(cq[0]);
-      ra[0][1] = lds_read16<L::DO_B>(cq[0]);
+      ra[0][1] = lds_read16<0>(co[0]);
       unroll<NSS>([&](auto SSc) __attribute__((always_inline)) {
         constexpr int SS = decltype(SSc)::value;
         constexpr int sl = SS & 1;
         if constexpr (SS + 1 < NSS) {
           ra[sl ^ 1][0] = lds_read16<0>(cq[SS + 1]);
-          ra[sl ^ 1][1] = lds_read16<L::DO_B>(cq[SS + 1]);
+          ra[sl ^ 1][1] = lds_read16<0>(co[SS + 1]);
           lds_wait<2>(ra[sl]);
         } else {
           lds_wait<0>(ra[sl]);
@@ -533,7 +536,10 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       });
     }
 
-    auto step = [&](auto MASKc) __attribute__((always_inline)) {
+    // one step with the current tile in stage U (the step loop runs four
+    // steps per round, so that every stage is known when compiling)
+    auto step = [&](auto MASKc, auto Uc) __attribute__((always_inline)) {
+      constexpr int U = decltype(Uc)::value;
       const int32_t clo = lo0;
       // Phase A. The previous tile's dS chunks 2, 3 go out first (before
       // this step's copies, so the copies are the last memory operations
@@ -541,11 +547,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       // which no wave reads any more.
       if (store_ds && have_prev) store_ds2(db2, dsprev, ic<2>{});
       have_prev = true;
-      phase(MASKc, ic<0>{}, ic<2>{}, ic<32 * D * 2>{}, ic<0>{}, cq, pqp, s1, d1, s0, d0, pa, da, pb2, db2, clo,
-            [&](auto SSc) __attribute__((always_inline)) {
+      phase(MASKc, ic<0>{}, ic<2>{}, ic<32 * D * 2>{}, ic<0>{}, ic<U>{}, ic<(U + 3) % kNst>{}, ic<U>{}, s1, d1,
+            s0, d0, pa, da, pb2, db2, clo, [&](auto SSc) __attribute__((always_inline)) {
               constexpr int SS = decltype(SSc)::value;
-              if constexpr (SS == 1) dma_q(src, (st + 2) & 3);
-              if constexpr (SS == NSS / 2 + 1) dma_o(src, (st + 2) & 3);
+              if constexpr (SS == 1) dma_q(src, (U + 2) % kNst);
+              if constexpr (SS == NSS / 2 + 1) dma_o(src, (U + 2) % kNst);
             });
       __builtin_amdgcn_sched_barrier(0);
       // Tile t + 1 has landed (t + 2 may still be in flight); past the
@@ -554,26 +560,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       wg_barrier();
       // Phase B: this tile's dS chunks 0, 1 go out first
       if (store_ds) store_ds2(da, ds0, ic<0>{});
-      phase(MASKc, ic<1>{}, ic<0>{}, ic<0>{}, ic<32 * 4>{}, cqn, pqc, s0, d0, s1, d1, pb2, db2, pa, da, clo,
-            [&](auto) __attribute__((always_inline)) {});
+      phase(MASKc, ic<1>{}, ic<0>{}, ic<0>{}, ic<32 * 4>{}, ic<(U + 1) % kNst>{}, ic<U>{}, ic<U>{}, s0, d0, s1,
+            d1, pb2, db2, pa, da, clo, [&](auto) __attribute__((always_inline)) {});
       __builtin_amdgcn_sched_barrier(0);
-      // the read addresses move one stage
-      const int32_t dn = st == kNst - 2 ? -(kNst - 1) * L::STG_B : L::STG_B;  // st + 1 -> st + 2
-      const int32_t dc = st == kNst - 1 ? -(kNst - 1) * L::STG_B : L::STG_B;  // st -> st + 1
-#pragma unroll
-      for (int ss = 0; ss < NSS; ++ss) {
-        cq[ss] = cqn[ss];
-        cqn[ss] += dn;
-      }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          pqp[h2][dt] = pqc[h2][dt];
-          pqc[h2][dt] += dc;
-        }
-      cl += st == kNst - 1 ? -(kNst - 1) * kQm * 4 : kQm * 4;
-      st = (st + 1) & (kNst - 1);
       // t + 1 becomes current, the walk moves on to t + 3
       v0 = v1;
       v1 = v2;
@@ -588,21 +577,44 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         v2 = advance();
       }
     };
-    while (v0 && pass0 == 0) step(ic<1>{});
-    while (v0) step(ic<0>{});
+    // steps while cont() holds, entering the four-step round at stage st
+    auto run = [&](auto MASKc, auto&& cont) __attribute__((always_inline)) {
+      while (cont()) {
+        if (st == 0) {
+          step(MASKc, ic<0>{});
+          st = 1;
+          if (!cont()) break;
+        }
+        if (st == 1) {
+          step(MASKc, ic<1>{});
+          st = 2;
+          if (!cont()) break;
+        }
+        if (st == 2) {
+          step(MASKc, ic<2>{});
+          st = 3;
+          if (!cont()) break;
+        }
+        step(MASKc, ic<3>{});
+        st = 0;
+      }
+    };
+    run(ic<1>{}, [&]() { return v0 && pass0 == 0; });
+    run(ic<0>{}, [&]() { return v0; });
 
     // the last tile's dS chunks 2, 3, and its dV^T / dK^T products of them
     // (stage of the last tile: now st - 1)
     if (store_ds) store_ds2(db2, dsprev, ic<2>{});
     {
+      const uint32_t so = (uint32_t)(((st + kNst - 1) % kNst) * L::QST_B);
       u32x2 t[4];
       unroll<2 * NDT>([&](auto Qc) __attribute__((always_inline)) {
         constexpr int Q = decltype(Qc)::value;
         constexpr int dt = Q / 2, c = Q % 2, kc = 2 + c;
-        t[0] = tr_read_at<L::DO_B + kc * 16 * D * 2>(pqp[0][dt]);
-        t[1] = tr_read_at<L::DO_B + kc * 16 * D * 2>(pqp[1][dt]);
-        t[2] = tr_read_at<kc * 16 * D * 2>(pqp[0][dt]);
-        t[3] = tr_read_at<kc * 16 * D * 2>(pqp[1][dt]);
+        t[0] = tr_read_at<kc * 16 * D * 2>(po[0][dt] + so);
+        t[1] = tr_read_at<kc * 16 * D * 2>(po[1][dt] + so);
+        t[2] = tr_read_at<kc * 16 * D * 2>(pq[0][dt] + so);
+        t[3] = tr_read_at<kc * 16 * D * 2>(pq[1][dt] + so);
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
         dv[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3)), pb2[c], dv[dt]);
         dk[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(t[2], t[3], 0, 1, 2, 3)), db2[c], dk[dt]);
