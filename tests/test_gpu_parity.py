@@ -148,6 +148,13 @@ SPLIT_CASES = [
     Case(174, 2, 3, 1500, 64, 5, False, "contiguous", "bf16"),
     Case(175, 1, 8, 16384, 128, 64, False, "contiguous", "bf16"),   # 256-row blocks, 64 steps
     Case(176, 1, 8, 16384, 128, 256, True, "striped", "bf16", Hk=1),  # 64-row blocks, 256 steps
+    # query blocks of at most 64 rows: ragged blocks, d = 64, one-token
+    # blocks, grouped-query heads, two batches, every layout
+    Case(271, 1, 4, 800, 64, 16, True, "striped", "bf16"),              # 50-row blocks
+    Case(272, 2, 3, 960, 128, 24, False, "contiguous", "bf16"),         # 40-row blocks
+    Case(273, 1, 4, 1024, 128, 16, True, "zigzag", "bf16", Hk=2),       # 64-row blocks
+    Case(274, 1, 2, 64, 128, 64, True, "contiguous", "bf16"),           # 1-row blocks
+    Case(275, 1, 8, 2048, 64, 32, True, "contiguous", "bf16", Hk=4),    # 64-row blocks, d = 64
 ]
 
 
