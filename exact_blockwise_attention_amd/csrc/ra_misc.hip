@@ -96,12 +96,12 @@ __global__ __launch_bounds__(256) void merge_lse_vec_kernel(int64_t rows, const 
 // groups combine by lane exchanges.
 constexpr int kMergeBatch = 8;
 
-template <int D>
-__global__ __launch_bounds__(256) void merge_splits_kernel(FwdParams p) {
+template <int D, int WPB>
+__global__ __launch_bounds__(64 * WPB) void merge_splits_kernel(FwdParams p) {
   constexpr int LPR = D / 8;    // lanes per copy of a row
   constexpr int G = 64 / LPR;   // partial groups per row
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
-  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;  // uniform over the wave
+  const int64_t r = (int64_t)blockIdx.x * WPB + threadIdx.x / 64;  // uniform over the wave
   if (r >= rows) return;
   const int lane = threadIdx.x % 64;
   const int g = lane / LPR;
@@ -159,11 +159,13 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(FwdParams p) {
   }
   if (g != 0) return;
   const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
-  const int32_t a = (int32_t)(r % p.Bb);
-  const int64_t t = r / p.Bb;
-  const int32_t h = (int32_t)(t % p.H);
-  const int32_t b = (int32_t)((t / p.H) % p.B);
-  const int32_t ri = (int32_t)(t / p.H / p.B);
+  // (rows are below 2^31: the launcher checks)
+  const uint32_t r32 = (uint32_t)r, Bb32 = (uint32_t)p.Bb;
+  const int32_t a = (int32_t)(r32 % Bb32);
+  const uint32_t t = r32 / Bb32;
+  const int32_t h = (int32_t)(t % (uint32_t)p.H);
+  const int32_t b = (int32_t)((t / (uint32_t)p.H) % (uint32_t)p.B);
+  const int32_t ri = (int32_t)(t / (uint32_t)p.H / (uint32_t)p.B);
   __bf16* orow = reinterpret_cast<__bf16*>(p.o.ptr) + ri * p.o.s_blk + b * p.o.s_batch + (int64_t)a * p.o.s_tok +
                  h * p.o.s_head;
   typedef __bf16 b16x8 __attribute__((ext_vector_type(8)));
@@ -321,11 +323,21 @@ hipError_t launch_merge_lse(int64_t rows, int32_t d, const float* oa, const floa
 hipError_t launch_merge_splits(const FwdParams& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.n_ranks * p.B * p.H * p.Bb;
   if (rows <= 0) return hipSuccess;
-  const int64_t grid = (rows + 3) / 4;  // a wave per row
+  if (rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  // a wave per row; few rows (a short query block) get a workgroup each, so
+  // that they spread over every CU
+  if (rows <= 4096) {
+    if (p.D == 128)
+      hipLaunchKernelGGL((merge_splits_kernel<128, 1>), dim3((uint32_t)rows), dim3(64), 0, s, p);
+    else
+      hipLaunchKernelGGL((merge_splits_kernel<64, 1>), dim3((uint32_t)rows), dim3(64), 0, s, p);
+    return hipGetLastError();
+  }
+  const int64_t grid = (rows + 3) / 4;
   if (p.D == 128)
-    hipLaunchKernelGGL(merge_splits_kernel<128>, dim3((uint32_t)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_splits_kernel<128, 4>), dim3((uint32_t)grid), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(merge_splits_kernel<64>, dim3((uint32_t)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((merge_splits_kernel<64, 4>), dim3((uint32_t)grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
