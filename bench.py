@@ -625,8 +625,8 @@ def bench_bpt(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU ring is not part of "
-              "this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the ring across GPUs is not "
+              "implemented; it times one GPU's share of the ring at its real shape", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
