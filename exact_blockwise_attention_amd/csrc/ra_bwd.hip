@@ -113,7 +113,7 @@ struct QTileSrc {
   int32_t rows;
 };
 
-template <int D>
+template <int D, bool STORE_DS>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   using L = BwdLds<D>;
   constexpr int NSS = D / 16;          // 16-feature steps of the S / dP products
@@ -122,6 +122,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int NCP = kQm / RW / kWaves;  // row copies per wave per tensor
   constexpr int NCOPY = 2 * NCP + 1;   // copies per wave per tile
+  constexpr int kCopiesA = NCP + 1;    // of which phase A issues lse2 / D and Q
+  static_assert(kCopiesA < NSS && NCOPY - kCopiesA < NSS, "one copy per slot");
   static_assert(2 * NDT == NSS, "one pair of dV products per feature step");
   extern __shared__ __align__(16) unsigned char smem_raw[];
 
@@ -178,7 +180,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   int32_t wfrs = Bb;
   // stored dS (p.ds): the walk position's tile is number wds + wqt (the
   // tiles of this key tile follow each other, one per query tile)
-  const bool store_ds = p.ds != nullptr;
+  // p.ds != nullptr; known when compiling, so is the count of stores in flight
+  constexpr bool store_ds = STORE_DS;
   int32_t wds = 0;
   const int32_t klast = kv0 + kKn - 1 < Bb ? kv0 + kKn - 1 : Bb - 1;
   auto next_rank = [&]() -> bool {
@@ -292,38 +295,40 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     const int32_t cchunk = (lane % CPR) ^ chunk_swz<D>(crow);
     const int32_t sq2 = (int32_t)(2 * p.q.s_tok), so2 = (int32_t)(2 * p.dout.s_tok);
     const int32_t vq = crow * sq2 + 16 * cchunk, vo = crow * so2 + 16 * cchunk;
-    // the copies of one tile in two parts, lse2 / D and Q first, then dO
-    // (a step spreads them over its phases)
-    auto dma_q = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(wave == 1 ? s.d : s.l), (short)0, 4 * s.rows, kRawRsrcWord3);
-      const int32_t foff = wave < 2 ? L::F32_B + (wave * kNst + stage) * kQm * 4 : L::SPARE_B + (wave - 2) * kQm * 4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(smem_raw + foff), 4,
-                                              4 * lane, 0, 0, 0);
-      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)s.q, (short)0, sq2 * s.rows,
-                                                                          kRawRsrcWord3);
-#pragma unroll
-      for (int k = 0; k < NCP; ++k) {
-        const int qc = wave + kWaves * k;
+    // The copies of one tile, one instruction each: I = 0 is the lse2 / D
+    // row (wave 0: lse2, wave 1: D, waves 2 and 3 a spare row), 1 .. NCP
+    // the Q rows, NCP + 1 .. 2 NCP the dO rows. A direct copy holds its wave
+    // until the memory system takes the request, which takes longest when
+    // the waves of a workgroup request together, so a step issues one copy
+    // per slot of its phases.
+    auto copy_one = [&](const QTileSrc& s, int32_t stage, auto Ic) __attribute__((always_inline)) {
+      constexpr int I = decltype(Ic)::value;
+      static_assert(I >= 0 && I < NCOPY, "copy index");
+      if constexpr (I == 0) {
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(wave == 1 ? s.d : s.l), (short)0, 4 * s.rows, kRawRsrcWord3);
+        const int32_t foff = wave < 2 ? L::F32_B + (wave * kNst + stage) * kQm * 4 : L::SPARE_B + (wave - 2) * kQm * 4;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (__attribute__((address_space(3))) void*)(smem_raw + foff), 4,
+                                                4 * lane, 0, 0, 0);
+      } else if constexpr (I <= NCP) {
+        constexpr int k = I - 1;
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)s.q, (short)0, sq2 * s.rows,
+                                                                            kRawRsrcWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rq, (__attribute__((address_space(3))) void*)(smem_raw + stage * L::QST_B + qc * 1024), 16,
+            rq, (__attribute__((address_space(3))) void*)(smem_raw + stage * L::QST_B + (wave + kWaves * k) * 1024), 16,
             vq + k * kWaves * RW * sq2, 0, 0, 0);
-      }
-    };
-    auto dma_o = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)s.o, (short)0, so2 * s.rows,
-                                                                          kRawRsrcWord3);
-#pragma unroll
-      for (int k = 0; k < NCP; ++k) {
-        const int qc = wave + kWaves * k;
+      } else {
+        constexpr int k = I - 1 - NCP;
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)s.o, (short)0, so2 * s.rows,
+                                                                            kRawRsrcWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ro, (__attribute__((address_space(3))) void*)(smem_raw + L::DO0 + stage * L::QST_B + qc * 1024), 16,
-            vo + k * kWaves * RW * so2, 0, 0, 0);
+            ro,
+            (__attribute__((address_space(3))) void*)(smem_raw + L::DO0 + stage * L::QST_B + (wave + kWaves * k) * 1024),
+            16, vo + k * kWaves * RW * so2, 0, 0, 0);
       }
     };
     auto dma = [&](const QTileSrc& s, int32_t stage) __attribute__((always_inline)) {
-      dma_q(s, stage);
-      dma_o(s, stage);
+      unroll<NCOPY>([&](auto Ic) __attribute__((always_inline)) { copy_one(s, stage, Ic); });
     };
 
     // Tiles t (current), t + 1 and t + 2 (the walk's position): whether they
@@ -335,8 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     int32_t lo0 = lo_of_walk(), lo1 = 0;
     // stored dS tiles of tiles t and t + 1, and of the tile before t (whose
     // dS the step writes out)
-    int32_t ds0 = store_ds ? ds_of_walk() : 0, ds1 = 0, dsprev = 0;
-    bool have_prev = false;
+    // (the first step writes the zero chunks of a "previous" tile over tile
+    // 0's, which the next step writes again: every step stores the same)
+    int32_t ds0 = store_ds ? ds_of_walk() : 0, ds1 = 0, dsprev = ds0;
     // moves the walk on and its copy source with it (the source stays on the
     // last tile once the walk is over: copies then repeat it)
     auto advance = [&]() -> bool {
@@ -541,27 +547,28 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     auto step = [&](auto MASKc, auto Uc) __attribute__((always_inline)) {
       constexpr int U = decltype(Uc)::value;
       const int32_t clo = lo0;
-      // Phase A. The previous tile's dS chunks 2, 3 go out first (before
-      // this step's copies, so the copies are the last memory operations
-      // when the phase ends); tile t + 2's copies go to the stage of t - 2,
-      // which no wave reads any more.
-      if (store_ds && have_prev) store_ds2(db2, dsprev, ic<2>{});
-      have_prev = true;
+      // Phase A. The previous tile's dS chunks 2, 3 go out first, then
+      // tile t + 2's lse2 / D and Q copies, one per slot from slot 1, into
+      // the stage of t - 2, which no wave reads any more.
+      if (store_ds) store_ds2(db2, dsprev, ic<2>{});
       phase(MASKc, ic<0>{}, ic<2>{}, ic<32 * D * 2>{}, ic<0>{}, ic<U>{}, ic<(U + 3) % kNst>{}, ic<U>{}, s1, d1,
             s0, d0, pa, da, pb2, db2, clo, [&](auto SSc) __attribute__((always_inline)) {
               constexpr int SS = decltype(SSc)::value;
-              if constexpr (SS == 1) dma_q(src, (U + 2) % kNst);
-              if constexpr (SS == NSS / 2 + 1) dma_o(src, (U + 2) % kNst);
+              if constexpr (SS >= 1 && SS <= kCopiesA) copy_one(src, (U + 2) % kNst, ic<SS - 1>{});
             });
       __builtin_amdgcn_sched_barrier(0);
-      // Tile t + 1 has landed (t + 2 may still be in flight); past the
-      // barrier every wave is done with the stage of t - 1.
-      wait_vm<NCOPY>();
+      // Tile t + 1 has landed: only this phase's stores and copies, issued
+      // after its last copy, may still be in flight. Past the barrier every
+      // wave is done with the stage of t - 1.
+      wait_vm<kCopiesA + (store_ds ? 2 : 0)>();
       wg_barrier();
-      // Phase B: this tile's dS chunks 0, 1 go out first
+      // Phase B: this tile's dS chunks 0, 1, then tile t + 2's dO copies
       if (store_ds) store_ds2(da, ds0, ic<0>{});
       phase(MASKc, ic<1>{}, ic<0>{}, ic<0>{}, ic<32 * 4>{}, ic<(U + 1) % kNst>{}, ic<U>{}, ic<U>{}, s0, d0, s1,
-            d1, pb2, db2, pa, da, clo, [&](auto) __attribute__((always_inline)) {});
+            d1, pb2, db2, pa, da, clo, [&](auto SSc) __attribute__((always_inline)) {
+              constexpr int SS = decltype(SSc)::value;
+              if constexpr (SS >= 1 && SS <= NCOPY - kCopiesA) copy_one(src, (U + 2) % kNst, ic<SS - 1 + kCopiesA>{});
+            });
       __builtin_amdgcn_sched_barrier(0);
       // t + 1 becomes current, the walk moves on to t + 3
       v0 = v1;
@@ -783,8 +790,12 @@ hipError_t launch_dyn(K kernel, int64_t grid, int threads, int bytes, hipStream_
 
 hipError_t launch_dkdv_bf16(const BwdParams& p, hipStream_t s) {
   const int64_t grid = ((p.Bb + kKn - 1) / kKn) * (int64_t)p.P * p.B * p.Hk;
-  if (p.D == 128) return launch_dyn(dkdv_bf16_kernel<128>, grid, kThreads, BwdLds<128>::BYTES, s, p);
-  return launch_dyn(dkdv_bf16_kernel<64>, grid, kThreads, BwdLds<64>::BYTES, s, p);
+  const bool st = p.ds != nullptr;
+  if (p.D == 128)
+    return st ? launch_dyn(dkdv_bf16_kernel<128, true>, grid, kThreads, BwdLds<128>::BYTES, s, p)
+              : launch_dyn(dkdv_bf16_kernel<128, false>, grid, kThreads, BwdLds<128>::BYTES, s, p);
+  return st ? launch_dyn(dkdv_bf16_kernel<64, true>, grid, kThreads, BwdLds<64>::BYTES, s, p)
+            : launch_dyn(dkdv_bf16_kernel<64, false>, grid, kThreads, BwdLds<64>::BYTES, s, p);
 }
 
 hipError_t launch_dkdv_f32(const BwdParams& p, hipStream_t s) {
