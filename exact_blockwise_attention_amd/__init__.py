@@ -288,6 +288,11 @@ def make_problem(B, H, d, P, Bb, layout, causal, dtype_code, scale=None, kv_head
                    float(scale) if scale else 0.0, dtype_code, int(kv_heads))
 
 
+def _nbytes(t) -> int:
+    """Bytes of a workspace tensor, as the library is told them."""
+    return int(t.numel()) * int(t.element_size())
+
+
 def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causal: bool = False,
                       scale=None, rank_range=None, copy_stream=None, out=None, lse=None, workspace=None,
                       split=True):
@@ -323,6 +328,8 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     need = workspace_bytes(pb, rb, re, use_copy, False) if (split or use_copy) else 0
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    # the library is told the size of the buffer it is given, which decides the mode
+    ws_ptr, ws_size = (workspace.data_ptr(), _nbytes(workspace)) if need else (None, 0)
     keep = []
     if q.shape[1] == L:
         qs, t_ = _seq_for(q, P, layout, rb)
@@ -337,7 +344,7 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     ks, kb = _seq_for(k, P, layout)
     vs, vb = _seq_for(v, P, layout)
     forward_raw(pb, rb, re, qs, ks, vs, os_,
-                lse.data_ptr(), workspace.data_ptr() if need else None, need, _stream_handle(None),
+                lse.data_ptr(), ws_ptr, ws_size, _stream_handle(None),
                 _stream_handle(copy_stream) if use_copy else None)
     if ob is not None:  # zigzag: blocked result back to the original order
         out.copy_(layout_copy(ob, P, layout, inverse=True))
@@ -371,9 +378,8 @@ def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "conti
     dq = torch.zeros_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    need = 0 if noalloc else workspace_bytes(pb, rb, re, False, True)
     if workspace is None and not noalloc:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(workspace_bytes(pb, rb, re, False, True), dtype=torch.uint8, device=q.device)
     (qs, _q), (os_, _o), (ds, _d) = (_seq_for(t, P, layout, rb) for t in (q, o, do))
     (ks, _k), (vs, _v) = (_seq_for(t, P, layout) for t in (k, v))
     (dqs, dqb), (dks, dkb), (dvs, dvb) = (_seq_for(dq, P, layout, rb), _seq_for(dk, P, layout),
@@ -381,8 +387,10 @@ def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "conti
     if noalloc:
         backward_noalloc_raw(pb, rb, re, qs, ks, vs, os_, ds, lse.data_ptr(), dqs, dks, dvs, _stream_handle(None))
     else:
+        # a caller's smaller workspace (at least workspace_bytes(..., 2)) selects
+        # the path that recomputes dQ instead of storing dS
         backward_raw(pb, rb, re, qs, ks, vs, os_, ds, lse.data_ptr(), dqs, dks, dvs,
-                     workspace.data_ptr(), need, _stream_handle(None))
+                     workspace.data_ptr(), _nbytes(workspace), _stream_handle(None))
     if layout == "zigzag":  # blocked results back to the original order
         for t, tb in ((dq, dqb), (dk, dkb), (dv, dvb)):
             t.copy_(layout_copy(tb, P, layout, inverse=True))
@@ -466,7 +474,7 @@ def bpt_ffn(attn, x, weights, block_rows, eps=1e-5, out=None, workspace=None):
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty_like(x)
-    bpt_ffn_raw(pb, attn.data_ptr(), x.data_ptr(), wts, out.data_ptr(), workspace.data_ptr(), need,
+    bpt_ffn_raw(pb, attn.data_ptr(), x.data_ptr(), wts, out.data_ptr(), workspace.data_ptr(), _nbytes(workspace),
                 _stream_handle(None))
     return out
 

@@ -290,3 +290,43 @@ def test_noalloc_backward_rejects_problems_beyond_its_scratch():
     pb = problem()
     pb.head_dim = 96
     assert call(pb) == 3
+
+
+def test_binding_tells_the_library_the_size_of_the_callers_workspace(monkeypatch):
+    """The workspace size decides the mode (the backward stores dS only in a
+    buffer of the full size, the forward splits only in one of the split
+    size), so the binding must pass the size of the buffer it was given,
+    never the size it would have allocated. The raw calls are captured here;
+    nothing is launched."""
+    torch = pytest.importorskip("torch")
+    seen = {}
+    monkeypatch.setattr(ra, "_stream_handle", lambda s: None)
+    monkeypatch.setattr(ra, "backward_raw", lambda *a: seen.__setitem__("bwd", a[-2]))
+    monkeypatch.setattr(ra, "forward_raw", lambda *a: seen.__setitem__("fwd", (a[-4], a[-3])))
+    B, H, d, P, Bb = 1, 2, 64, 4, 128
+    L = P * Bb
+    q, k, v, o, do = (torch.zeros(B, L, H, d, dtype=torch.bfloat16) for _ in range(5))
+    lse = torch.zeros(P, B, H, Bb)
+    pb = ra.make_problem(B, H, d, P, Bb, "striped", True, ra.BF16, None, kv_heads=H)
+    full = ra.workspace_bytes(pb, 0, P, False, True)
+    small = ra.workspace_bytes(pb, 0, P, False, 2)
+    assert 0 < small < full
+    ra.attention_backward(q, k, v, o, do, lse, P, "striped", True)
+    assert seen["bwd"] == full
+    ra.attention_backward(q, k, v, o, do, lse, P, "striped", True,
+                          workspace=torch.empty(small, dtype=torch.uint8))
+    assert seen["bwd"] == small
+    ra.attention_backward(q, k, v, o, do, lse, P, "striped", True,
+                          workspace=torch.empty(small // 4 + 8, dtype=torch.float32))
+    assert seen["bwd"] == (small // 4 + 8) * 4
+    # forward, one rank of a ring too short to fill the GPU: the split size
+    pf = ra.make_problem(B, H, d, 3, 300, "striped", True, ra.BF16, None, kv_heads=H)
+    need = ra.workspace_bytes(pf, 2, 3, False, False)
+    q3, k3, v3 = (torch.zeros(B, 900, H, d, dtype=torch.bfloat16) for _ in range(3))
+    ra.attention_forward(q3, k3, v3, 3, "striped", True, rank_range=(2, 3))
+    assert seen["fwd"][1] == need
+    ra.attention_forward(q3, k3, v3, 3, "striped", True, rank_range=(2, 3),
+                         workspace=torch.empty(need // 2, dtype=torch.uint8))
+    assert seen["fwd"][1] == need // 2  # too small to split: the library runs one unsplit launch
+    ra.attention_forward(q3, k3, v3, 3, "striped", True, rank_range=(2, 3), split=False)
+    assert seen["fwd"] == (None, 0)

@@ -301,6 +301,43 @@ def test_backward_small(case):
     assert_output_close("dV", to_f64(dv), dv_r, case.dtype, case)
 
 
+MINIMAL_WS = [
+    Case(281, 1, 2, 650, 64, 5, True, "striped", "bf16"),
+    Case(282, 1, 4, 1024, 128, 4, True, "zigzag", "bf16", Hk=2),
+    Case(283, 2, 2, 768, 128, 3, False, "contiguous", "bf16"),
+    Case(284, 1, 2, 800, 128, 4, True, "striped", "bf16", Hk=1),
+]
+
+
+@pytest.mark.parametrize("case", MINIMAL_WS, ids=str)
+def test_backward_minimal_workspace(case):
+    """A caller's workspace of workspace_bytes(..., 2) bytes holds D and the
+    lse only, so the library takes the path that stores no dS and recomputes
+    S and dP for dQ. Same bar against the oracle as the default path."""
+    log(f"backward, minimal workspace {case}")
+    p = payloads(case, ("q", "k", "v", "do"))
+    dev = {n: to_device(x) for n, x in p.items()}
+    f = {n: syn_f64(x) for n, x in p.items()}
+    dq_r, dk_r, dv_r, _, _ = oracle.attention_bwd(f["q"], f["k"], f["v"], f["do"], case.causal)
+    o, lse = run_fwd(case, dev)
+    Hk = dev["k"].shape[2]
+    pb = ra.make_problem(case.B, case.H, case.d, case.P, case.L // case.P, case.layout, case.causal,
+                         ra.BF16, None, kv_heads=Hk)
+    small = ra.workspace_bytes(pb, 0, case.P, False, 2)
+    assert 0 < small < ra.workspace_bytes(pb, 0, case.P, False, True)
+    ws = torch.empty(small, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = ra.attention_backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, case.P, case.layout,
+                                       case.causal, workspace=ws)
+    torch.cuda.synchronize()
+    assert_output_close("dQ", to_f64(dq), dq_r, case.dtype, case)
+    assert_output_close("dK", to_f64(dk), dk_r, case.dtype, case)
+    assert_output_close("dV", to_f64(dv), dv_r, case.dtype, case)
+    # one byte short of the minimum is refused before anything is launched
+    with pytest.raises(ra.RaError):
+        ra.attention_backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, case.P, case.layout, case.causal,
+                              workspace=torch.empty(small - 1, dtype=torch.uint8, device="cuda"))
+
+
 @pytest.mark.parametrize("layout,hk", [("striped", 0), ("zigzag", 0), ("striped", 1)])
 def test_backward_rank_range(layout, hk):
     """Ranks [1, 3): dQ of their rows, and dK/dV holding only their queries'
