@@ -293,6 +293,41 @@ def _nbytes(t) -> int:
     return int(t.numel()) * int(t.element_size())
 
 
+# The library sees pointers and strides only: it cannot tell a buffer that is
+# too small or of another element type. These checks run before any pointer
+# is handed over and raise ValueError.
+def _expect(t, name, shape=None, dtype=None, device=None, contiguous=False, dims=None):
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name}: {t.dim()} dimensions, expected {dims}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _check_attention_inputs(q, k, v, P, rank_range):
+    """q [B, L or nr*Bb, H, d], k and v [B, L, Hk, d] of one dtype and device,
+    Hk dividing H, L a multiple of P, 0 <= rank_begin < rank_end <= P."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, n, dims=4, dtype=q.dtype, device=q.device)
+    _expect(v, "v", shape=k.shape)
+    B, L, Hk, d = k.shape
+    if P < 1 or L % P:
+        raise ValueError(f"sequence length {L} must split into {P} equal blocks")
+    rb, re = (0, P) if rank_range is None else rank_range
+    if not 0 <= rb < re <= P:
+        raise ValueError(f"rank range [{rb}, {re}) outside the ring of {P}")
+    if q.shape[0] != B or q.shape[3] != d or q.shape[1] not in (L, (re - rb) * (L // P)):
+        raise ValueError(f"q: shape {tuple(q.shape)} does not match k {tuple(k.shape)} and the rank range")
+    if q.shape[2] % Hk:
+        raise ValueError(f"{Hk} K/V heads must divide {q.shape[2]} query heads")
+    return rb, re
+
+
 def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causal: bool = False,
                       scale=None, rank_range=None, copy_stream=None, out=None, lse=None, workspace=None,
                       split=True):
@@ -311,14 +346,20 @@ def attention_forward(q, k, v, ring_size: int, layout: str = "contiguous", causa
     whole ring runs in one unsplit launch.
     """
     torch = _torch()
+    P = ring_size
+    rb, re = _check_attention_inputs(q, k, v, P, rank_range)
     B, L, Hk, d = k.shape
     H = q.shape[2]
-    P = ring_size
     Bb = L // P
-    rb, re = (0, P) if rank_range is None else rank_range
     nr = re - rb
     code = _dtype_code(q)
     pb = make_problem(B, H, d, P, Bb, layout, causal, code, scale, kv_heads=Hk)
+    if out is not None:
+        _expect(out, "out", shape=q.shape, dtype=q.dtype, device=q.device)
+    if lse is not None:
+        _expect(lse, "lse", shape=(nr, B, H, Bb), dtype=torch.float32, device=q.device, contiguous=True)
+    if workspace is not None:
+        _expect(workspace, "workspace", device=q.device, contiguous=True)
     if out is None:
         # rows of ranks outside the range are never written: zero them
         out = torch.zeros_like(q) if (q.shape[1] == L and nr < P) else torch.empty_like(q)
@@ -368,11 +409,17 @@ def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "conti
     Hk heads); returns (dq, dk, dv). ``noalloc`` calls ra_backward_noalloc,
     which takes no workspace (the library's static scratch instead)."""
     torch = _torch()
+    P = ring_size
+    rb, re = _check_attention_inputs(q, k, v, P, rank_range)
     B, L, Hk, d = k.shape
     H = q.shape[2]
-    P = ring_size
     Bb = L // P
-    rb, re = (0, P) if rank_range is None else rank_range
+    _expect(q, "q", shape=(B, L, H, d))
+    for t, n in ((o, "o"), (do, "do")):
+        _expect(t, n, shape=q.shape, dtype=q.dtype, device=q.device)
+    _expect(lse, "lse", shape=(re - rb, B, H, Bb), dtype=torch.float32, device=q.device, contiguous=True)
+    if workspace is not None:
+        _expect(workspace, "workspace", device=q.device, contiguous=True)
     code = _dtype_code(q)
     pb = make_problem(B, H, d, P, Bb, layout, causal, code, scale, kv_heads=Hk)
     dq = torch.zeros_like(q)
@@ -400,11 +447,18 @@ def attention_backward(q, k, v, o, do, lse, ring_size: int, layout: str = "conti
 def merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse_out=None):
     """fp32 [rows, d] / [rows] partial results -> merged (o, lse)."""
     torch = _torch()
+    _expect(o_a, "o_a", dims=2, dtype=torch.float32, contiguous=True)
     rows, d = o_a.shape
+    dev = o_a.device
+    _expect(o_b, "o_b", shape=(rows, d), dtype=torch.float32, device=dev, contiguous=True)
+    for t, n in ((lse_a, "lse_a"), (lse_b, "lse_b")):
+        _expect(t, n, shape=(rows,), dtype=torch.float32, device=dev, contiguous=True)
     if out is None:
         out = torch.empty_like(o_a)
     if lse_out is None:
         lse_out = torch.empty_like(lse_a)
+    _expect(out, "out", shape=(rows, d), dtype=torch.float32, device=dev, contiguous=True)
+    _expect(lse_out, "lse_out", shape=(rows,), dtype=torch.float32, device=dev, contiguous=True)
     merge_lse_raw(rows, d, o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(),
                   out.data_ptr(), lse_out.data_ptr(), _stream_handle(None))
     return out, lse_out
@@ -413,6 +467,9 @@ def merge_lse(o_a, lse_a, o_b, lse_b, out=None, lse_out=None):
 def layout_copy(x, ring_size: int, layout: str, inverse: bool = False):
     """Original [B, L, H, d] -> blocked [P, B, Bb, H, d] (or back)."""
     torch = _torch()
+    _expect(x, "x", dims=5 if inverse else 4, contiguous=True)
+    if not inverse and (ring_size < 1 or x.shape[1] % ring_size):
+        raise ValueError(f"sequence length {x.shape[1]} must split into {ring_size} equal blocks")
     if inverse:
         P, B, Bb, H, d = x.shape
         out = torch.empty((B, P * Bb, H, d), dtype=x.dtype, device=x.device)
@@ -439,10 +496,23 @@ def linear(x, w, bias=None, residual=None, gelu=False, out_f32=False, out=None):
     """x [m, k] bf16, w [n, k] bf16 (a linear layer's [out, in] weight) ->
     x w^T (+ bias) (+ residual) (then GELU), [m, n] fp32 or bf16."""
     torch = _torch()
+    _expect(x, "x", dims=2, dtype=torch.bfloat16)
     m, k = x.shape
+    dev = x.device
+    _expect(w, "w", dims=2, dtype=torch.bfloat16, device=dev)
     n = w.shape[0]
+    if w.shape[1] != k:
+        raise ValueError(f"w: shape {tuple(w.shape)} does not match x {tuple(x.shape)}")
+    if bias is not None:
+        _expect(bias, "bias", shape=(n,), dtype=torch.float32, device=dev, contiguous=True)
+    if residual is not None:
+        _expect(residual, "residual", shape=(m, n), dtype=torch.bfloat16, device=dev)
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32 if out_f32 else torch.bfloat16, device=x.device)
+    _expect(out, "out", shape=(m, n), dtype=torch.float32 if out_f32 else torch.bfloat16, device=dev)
+    for t, nme in ((x, "x"), (w, "w"), (out, "out")) + (((residual, "residual"),) if residual is not None else ()):
+        if t.stride(1) != 1:
+            raise ValueError(f"{nme}: rows must be contiguous")
     linear_raw(m, n, k, x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), _ptr(bias), _ptr(residual),
                residual.stride(0) if residual is not None else 0, gelu, out.data_ptr(), out.stride(0), out_f32,
                _stream_handle(None))
@@ -452,9 +522,13 @@ def linear(x, w, bias=None, residual=None, gelu=False, out_f32=False, out=None):
 def layer_norm(z, gamma, beta, eps=1e-5, out=None):
     """z [rows, d] fp32 -> bf16 layer norm over d."""
     torch = _torch()
+    _expect(z, "z", dims=2, dtype=torch.float32, contiguous=True)
     rows, d = z.shape
+    for t, n in ((gamma, "gamma"), (beta, "beta")):
+        _expect(t, n, shape=(d,), dtype=torch.float32, device=z.device, contiguous=True)
     if out is None:
         out = torch.empty((rows, d), dtype=torch.bfloat16, device=z.device)
+    _expect(out, "out", shape=(rows, d), dtype=torch.bfloat16, device=z.device, contiguous=True)
     layer_norm_raw(rows, d, z.data_ptr(), gamma.data_ptr(), beta.data_ptr(), eps, out.data_ptr(),
                    _stream_handle(None))
     return out
@@ -466,8 +540,20 @@ def bpt_ffn(attn, x, weights, block_rows, eps=1e-5, out=None, workspace=None):
     block of ``block_rows`` rows at a time. ``weights``: dict of
     BPT_WEIGHT_NAMES tensors (weights bf16 [out, in], the rest fp32)."""
     torch = _torch()
+    _expect(x, "x", dims=2, dtype=torch.bfloat16, contiguous=True)
     rows, dm = x.shape
-    pb = BptProblem(rows, dm, weights["w_1"].shape[0], block_rows, eps)
+    dev = x.device
+    _expect(attn, "attn", shape=(rows, dm), dtype=torch.bfloat16, device=dev, contiguous=True)
+    dff = weights["w_1"].shape[0]
+    shapes = {"w_o": (dm, dm), "w_1": (dff, dm), "w_2": (dm, dff), "b_1": (dff,)}
+    for n in BPT_WEIGHT_NAMES:
+        _expect(weights[n], n, shape=shapes.get(n, (dm,)), dtype=torch.bfloat16 if n.startswith("w_") else torch.float32,
+                device=dev, contiguous=True)
+    if out is not None:
+        _expect(out, "out", shape=(rows, dm), dtype=torch.bfloat16, device=dev, contiguous=True)
+    if workspace is not None:
+        _expect(workspace, "workspace", device=dev, contiguous=True)
+    pb = BptProblem(rows, dm, dff, block_rows, eps)
     wts = BptWeights(*(weights[n].data_ptr() for n in BPT_WEIGHT_NAMES))
     need = bpt_workspace_bytes(pb)
     if workspace is None:

@@ -330,3 +330,55 @@ def test_binding_tells_the_library_the_size_of_the_callers_workspace(monkeypatch
     assert seen["fwd"][1] == need // 2  # too small to split: the library runs one unsplit launch
     ra.attention_forward(q3, k3, v3, 3, "striped", True, rank_range=(2, 3), split=False)
     assert seen["fwd"] == (None, 0)
+
+
+def test_binding_refuses_buffers_the_library_cannot_check():
+    """Shapes, element types and contiguity the C ABI cannot see (it takes
+    pointers and strides) are checked by the binding before any pointer is
+    handed over; each bad argument raises ValueError. CPU tensors: nothing
+    reaches the library."""
+    torch = pytest.importorskip("torch")
+    bf, f32 = torch.bfloat16, torch.float32
+    B, L, H, d, P = 1, 512, 4, 64, 4
+    Bb = L // P
+    q = torch.zeros(B, L, H, d, dtype=bf)
+    k = torch.zeros(B, L, 2, d, dtype=bf)
+    lse = torch.zeros(P, B, H, Bb)
+    z = lambda *s, dt=bf: torch.zeros(*s, dtype=dt)  # noqa: E731
+    bad = [
+        lambda: ra.attention_forward(z(B, 510, H, d), z(B, 510, 2, d), z(B, 510, 2, d), P),      # 510 % 4
+        lambda: ra.attention_forward(q, k, k, P, rank_range=(2, 5)),                             # past the ring
+        lambda: ra.attention_forward(q, k, k, P, rank_range=(2, 2)),                             # empty
+        lambda: ra.attention_forward(q, k, z(B, L, 3, d), P),                                    # v != k
+        lambda: ra.attention_forward(q, z(B, L, 3, d), z(B, L, 3, d), P),                        # 3 does not divide 4
+        lambda: ra.attention_forward(q, k.float(), k, P),                                        # mixed dtypes
+        lambda: ra.attention_forward(z(B, 200, H, d), k, k, P, rank_range=(0, 2)),              # rows of 2 ranks: 256
+        lambda: ra.attention_forward(q, k, k, P, lse=torch.zeros(P - 1, B, H, Bb)),              # lse too small
+        lambda: ra.attention_forward(q, k, k, P, lse=torch.zeros(P, B, H, Bb, dtype=torch.float64)),
+        lambda: ra.attention_forward(q, k, k, P, out=z(B, L, H, d, dt=f32)),                     # out dtype
+        lambda: ra.attention_backward(q, k, k, z(B, L, H, 32), q, lse, P),                       # o shape
+        lambda: ra.attention_backward(q, k, k, q, q, lse[:2], P),                                # lse rows
+        lambda: ra.attention_backward(q, k, k, q, q, torch.zeros(P, B, H, 2 * Bb)[..., ::2], P),   # strided lse
+        lambda: ra.attention_backward(q[:, :256], k, k, q[:, :256], q[:, :256], lse[:2], P, rank_range=(0, 2)),
+        lambda: ra.merge_lse(z(8, 64, dt=f32).t(), z(64, dt=f32), z(64, 8, dt=f32), z(64, dt=f32)),
+        lambda: ra.merge_lse(z(64, 8, dt=f32), z(63, dt=f32), z(64, 8, dt=f32), z(64, dt=f32)),
+        lambda: ra.merge_lse(z(64, 8, dt=f32), z(64, dt=f32), z(64, 8), z(64, dt=f32)),
+        lambda: ra.layout_copy(q.transpose(1, 2), P, "striped"),                                 # not contiguous
+        lambda: ra.layout_copy(z(B, 510, H, d), P, "striped"),
+        lambda: ra.linear(z(16, 64), z(32, 48)),                                                 # k mismatch
+        lambda: ra.linear(z(16, 64), z(32, 64), bias=z(32)),                                     # bias dtype
+        lambda: ra.linear(z(16, 64), z(32, 64), residual=z(16, 32, dt=f32)),                     # residual dtype
+        lambda: ra.linear(z(16, 64), z(32, 64), out=z(16, 32, dt=f32)),                          # out dtype
+        lambda: ra.layer_norm(z(16, 64, dt=f32), z(63, dt=f32), z(64, dt=f32)),
+        lambda: ra.layer_norm(z(16, 64), z(64, dt=f32), z(64, dt=f32)),                          # z dtype
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(ValueError):
+            call()
+    dm, dff = 128, 256
+    w = {n: z(dm, dt=f32) for n in ra.BPT_WEIGHT_NAMES}
+    w.update(w_o=z(dm, dm), w_1=z(dff, dm), w_2=z(dm, dff), b_1=z(dff, dt=f32))
+    for name, wrong in (("w_2", z(dff, dm)), ("b_1", z(dm, dt=f32)), ("ln1_g", z(dm)), ("w_o", z(dm, dm, dt=f32))):
+        ww = dict(w, **{name: wrong})
+        with pytest.raises(ValueError):
+            ra.bpt_ffn(z(64, dm), z(64, dm), ww, 32)
