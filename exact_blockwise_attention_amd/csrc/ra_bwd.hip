@@ -113,6 +113,19 @@ struct QTileSrc {
   int32_t rows;
 };
 
+// S / dP products with the accumulator in VGPRs and the K / V operand in
+// AGPRs: the vector work reads the scores without copying them out of
+// AGPRs first. The operands' producers are far from these products (LDS
+// reads retired by an explicit wait; K and V loaded once), and their
+// results are read in the next phase, hundreds of instructions later.
+__device__ __forceinline__ void mfma_s(f32x16& acc, const u32x4& a, const bf16x8& b, bool zero) {
+  if (zero) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(acc) : "v"(a), "a"(b));
+  } else {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+  }
+}
+
 template <int D, bool STORE_DS>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   using L = BwdLds<D>;
@@ -362,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
     bool v2 = v1 && advance();
     // the K / V registers are in (the compiler waits for them here, once)
 #pragma unroll
-    for (int ss = 0; ss < NSS; ++ss) asm volatile("" : "+v"(kreg[ss]), "+v"(vreg[ss]));
+    for (int ss = 0; ss < NSS; ++ss) asm volatile("" : "+a"(kreg[ss]), "+a"(vreg[ss]));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the zeroed stage
     wait_vm<NCOPY>();  // tile 0 has landed
     wg_barrier();
@@ -415,7 +428,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       pb2[c] = bf16x8{};
       db2[c] = bf16x8{};
     }
-    const f32x16 zacc = {};
 
     // s_waitcnt lgkmcnt(N) tied to one slot's reads
     auto slot_wait = [&](auto Nc, u32x4(&ra)[2], u32x2(&ta)[4], u32x4(&rl)[2]) __attribute__((always_inline)) {
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         const float4 d4 = __builtin_bit_cast(float4, rl[g0 & 1][1]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};  // lse in log2 units
         const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-        sx = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : sx);
+        mfma_s(sx, ra[sl][0], kreg[SS], SS == 0);
         dv[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[sl][0], tr[sl][1], 0, 1, 2, 3)), pi[c],
                         dv[dt]);
         at_slot(SSc);
@@ -497,7 +509,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
           pw[gg / 2][4 * (gg % 2) + e] = (__bf16)pv;
           dw[gg / 2][4 * (gg % 2) + e] = (__bf16)dsv;
         }
-        dx = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : dx);
+        mfma_s(dx, ra[sl][1], vreg[SS], SS == 0);
         dk[dt] = mfma32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(tr[sl][2], tr[sl][3], 0, 1, 2, 3)), di[c],
                         dk[dt]);
         // keeps the conversions of a finished chunk where they are
@@ -537,8 +549,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         } else {
           lds_wait<0>(ra[sl]);
         }
-        s0 = mfma32(__builtin_bit_cast(bf16x8, ra[sl][0]), kreg[SS], SS == 0 ? zacc : s0);
-        d0 = mfma32(__builtin_bit_cast(bf16x8, ra[sl][1]), vreg[SS], SS == 0 ? zacc : d0);
+        mfma_s(s0, ra[sl][0], kreg[SS], SS == 0);
+        mfma_s(d0, ra[sl][1], vreg[SS], SS == 0);
       });
     }
 
