@@ -251,3 +251,33 @@ def asm_marked(items):
         else:
             out.append((it[0], it[1]))
     return out
+
+
+KINFO = re.compile(r"^\s*\.set\s+(_Z\w+)\.private_seg_size,\s*(\d+)")
+
+
+def scratch_of(asm):
+    """kernel -> bytes of scratch per lane, from the listing's kernel info."""
+    out, cur = {}, None
+    for line in asm.splitlines():
+        m = KINFO.match(line)
+        if m:
+            cur = m.group(1)
+            out[cur] = int(m.group(2))
+            continue
+        if cur and line.startswith("; ScratchSize:"):
+            out[cur] = max(out[cur], int(line.split(":")[1]))
+            cur = None
+    return out
+
+
+@pytest.mark.parametrize("src", KERNEL_SOURCES)
+def test_no_kernel_spills_to_scratch(listings, src):
+    """Every kernel, the fp32 correctness kernels included, fits its
+    registers at the occupancy its launch bounds ask for: a spill would show
+    as scratch and turn the hot loops' register traffic into memory
+    traffic."""
+    scratch = scratch_of(listings[src])
+    assert scratch, f"no kernel info in {src}"
+    spilled = {k: v for k, v in scratch.items() if v}
+    assert not spilled, f"{src}: scratch bytes per lane {spilled}"
