@@ -554,6 +554,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
       });
     }
 
+    bool slow = false;  // the walk's next tile is in another run
     // one step with the current tile in stage U (the step loop runs four
     // steps per round, so that every stage is known when compiling)
     auto step = [&](auto MASKc, auto Uc) __attribute__((always_inline)) {
@@ -593,26 +594,36 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         pass1 = wpass;
         lo1 = lo_of_walk();
         if (store_ds) ds1 = ds_of_walk();
-        v2 = advance();
+        if (wqt + 1 < wq_hi) {  // the next query tile of the same (rank, head) run
+          ++wqt;
+          src_next_row_tile(src);
+        } else {
+          slow = true;  // another head or rank: the walk moves on outside the step loop
+        }
       }
     };
     // steps while cont() holds, entering the four-step round at stage st
     auto run = [&](auto MASKc, auto&& cont) __attribute__((always_inline)) {
       while (cont()) {
+        // a run change (rare) moves the walk on here, outside the steps
+        if (slow) {
+          slow = false;
+          v2 = advance();
+        }
         if (st == 0) {
           step(MASKc, ic<0>{});
           st = 1;
-          if (!cont()) break;
+          if (slow || !cont()) continue;
         }
         if (st == 1) {
           step(MASKc, ic<1>{});
           st = 2;
-          if (!cont()) break;
+          if (slow || !cont()) continue;
         }
         if (st == 2) {
           step(MASKc, ic<2>{});
           st = 3;
-          if (!cont()) break;
+          if (slow || !cont()) continue;
         }
         step(MASKc, ic<3>{});
         st = 0;
