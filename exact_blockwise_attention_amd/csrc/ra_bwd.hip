@@ -113,6 +113,23 @@ struct QTileSrc {
   int32_t rows;
 };
 
+// The position of key tile kt's first stored dS tile in its pair's run: the
+// sum over the key tiles before it of the query tiles that meet each
+// (ds_key_tile_start), with those key tiles shared out over the lanes and the
+// sum taken bit by bit from ballots. Every lane must be active; the result
+// is the same in all of them.
+__device__ __forceinline__ int32_t ds_key_tile_start_wave(const BlockRel& r, int32_t kt, int32_t block_len, int lane) {
+  const int32_t qtiles = (block_len + kDsRows - 1) / kDsRows;
+  int32_t n = 0;
+  for (int32_t k0 = 0; k0 < kt; k0 += 64) {
+    const int32_t k = k0 + lane;
+    const int32_t c = k < kt ? qtiles - ds_first_qtile(r, k, block_len) : 0;  // 0 .. qtiles
+    for (int32_t bit = 0; (1 << bit) <= qtiles; ++bit)
+      n += (int32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(((c >> bit) & 1) != 0)) << bit;
+  }
+  return n;
+}
+
 // S / dP products with the accumulator in VGPRs and the K / V operand in
 // AGPRs: the vector work reads the scores without copying them out of
 // AGPRs first. The operands' producers are far from these products (LDS
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   auto next_rank = [&]() -> bool {
     for (;;) {
       while (++wk < p.P) {
-        wi = ring_rank(j, wk, p.P);
+        wi = j + wk < p.P ? j + wk : j + wk - p.P;  // ring_rank(j, wk, P), both below P
         if (wi < p.rank_begin || wi >= p.rank_begin + p.n_ranks) continue;
         wrel = block_relation(p.layout, p.causal, wi, j, Bb);
         const int32_t a_first = first_row_seeing32(wrel, kv0, Bb);
@@ -216,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
         wfrs = first_row_seeing32(wrel, key, Bb);
         if (store_ds) {
           const int32_t run = ((wi - p.rank_begin) * p.B + b) * p.H * p.P + hk * p.G * p.P + j;
-          wds = run * (int32_t)p.ds_stride + (int32_t)ds_key_tile_start(wrel, tile, Bb) - q_first;
+          wds = run * (int32_t)p.ds_stride + ds_key_tile_start_wave(wrel, tile, Bb, lane) - q_first;
         }
         return true;
       }
