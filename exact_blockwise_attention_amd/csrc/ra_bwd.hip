@@ -113,23 +113,6 @@ struct QTileSrc {
   int32_t rows;
 };
 
-// The position of key tile kt's first stored dS tile in its pair's run: the
-// sum over the key tiles before it of the query tiles that meet each
-// (ds_key_tile_start), with those key tiles shared out over the lanes and the
-// sum taken bit by bit from ballots. Every lane must be active; the result
-// is the same in all of them.
-__device__ __forceinline__ int32_t ds_key_tile_start_wave(const BlockRel& r, int32_t kt, int32_t block_len, int lane) {
-  const int32_t qtiles = (block_len + kDsRows - 1) / kDsRows;
-  int32_t n = 0;
-  for (int32_t k0 = 0; k0 < kt; k0 += 64) {
-    const int32_t k = k0 + lane;
-    const int32_t c = k < kt ? qtiles - ds_first_qtile(r, k, block_len) : 0;  // 0 .. qtiles
-    for (int32_t bit = 0; (1 << bit) <= qtiles; ++bit)
-      n += (int32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(((c >> bit) & 1) != 0)) << bit;
-  }
-  return n;
-}
-
 // S / dP products with the accumulator in VGPRs and the K / V operand in
 // AGPRs: the vector work reads the scores without copying them out of
 // AGPRs first. The operands' producers are far from these products (LDS
@@ -202,10 +185,11 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   // tiles every row of which sees every key. Row extents grow with the row,
   // so at each rank the first kind is a run of tiles [wq_first, wq_full)
   // and the second the rest up to the last tile; each pass runs its own copy
-  // of the step, and only the first masks. (wk, wi, wgi, wqt) is the tile
-  // to copy next; per rank: its relation to block j, the pass's tile range,
-  // and (per lane) the first row that sees this lane's key.
-  int32_t wpass = 0, wk = -1, wi = 0, wgi = 0, wqt = 0, wq_lo = 0, wq_hi = 0;
+  // of the step, and only the first masks. (wc, wgi, wqt) is the tile to
+  // copy next, wc numbering the (pass, ring step) pairs pass-major; per
+  // pair: the rank, its relation to block j, the pass's tile range, and (per
+  // lane) the first row that sees this lane's key.
+  int32_t wpass = 0, wc = -1, wi = 0, wgi = 0, wqt = 0, wq_lo = 0, wq_hi = 0;
   BlockRel wrel = make_rel(kNone, 0, Bb);
   int32_t wfrs = Bb;
   // stored dS (p.ds): the walk position's tile is number wds + wqt (the
@@ -214,32 +198,55 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_bf16_kernel(BwdParams p) {
   constexpr bool store_ds = STORE_DS;
   int32_t wds = 0;
   const int32_t klast = kv0 + kKn - 1 < Bb ? kv0 + kKn - 1 : Bb - 1;
+  // The pairs' rank, tile range and first stored dS tile, 64 pairs at a
+  // time from pair cbase on, one pair per lane (cmask: the pairs that have
+  // tiles), so that moving to the next pair reads lanes instead of searching.
+  int32_t cbase = 0, c_wi = 0, c_lo = 0, c_hi = 0, c_ds = 0;
+  uint64_t cmask = 0;
+  auto fill = [&](int32_t base) {
+    cbase = base;
+    const int32_t c = base + lane;
+    const int32_t cpass = c >= p.P ? 1 : 0;
+    const int32_t ck = c - cpass * p.P;
+    const int32_t ci = j + ck < p.P ? j + ck : j + ck - p.P;  // ring_rank(j, ck, P), both below P
+    const BlockRel r = block_relation(p.layout, p.causal, ci, j, Bb);
+    const int32_t a_first = first_row_seeing32(r, kv0, Bb);
+    const int32_t q_first = a_first / kQm;
+    int32_t q_full = (first_row_seeing32(r, klast, Bb) + kQm - 1) / kQm;
+    q_full = q_full < qtiles ? q_full : qtiles;
+    c_lo = cpass == 0 ? q_first : (q_full > q_first ? q_full : q_first);
+    c_hi = cpass == 0 ? q_full : qtiles;
+    c_wi = ci;
+    const bool ok = c < 2 * p.P && ci >= p.rank_begin && ci < p.rank_begin + p.n_ranks && a_first < Bb &&
+                    c_lo < c_hi;
+    c_ds = 0;
+    if (store_ds && ok) {
+      const int32_t run = ((ci - p.rank_begin) * p.B + b) * p.H * p.P + hk * p.G * p.P + j;
+      c_ds = run * (int32_t)p.ds_stride + (int32_t)ds_key_tile_start(r, tile, Bb) - q_first;
+    }
+    cmask = __builtin_amdgcn_ballot_w64(ok);
+  };
+  fill(0);
   auto next_rank = [&]() -> bool {
     for (;;) {
-      while (++wk < p.P) {
-        wi = j + wk < p.P ? j + wk : j + wk - p.P;  // ring_rank(j, wk, P), both below P
-        if (wi < p.rank_begin || wi >= p.rank_begin + p.n_ranks) continue;
+      const int32_t nb = wc + 1 > cbase ? wc + 1 - cbase : 0;  // the next pair's lane
+      const uint64_t rest = nb < 64 ? cmask & (~0ull << nb) : 0ull;
+      if (rest != 0) {
+        const int32_t l = (int32_t)__builtin_ctzll(rest);
+        wc = cbase + l;
+        wpass = wc >= p.P ? 1 : 0;
+        wi = __builtin_amdgcn_readlane(c_wi, l);
+        wq_lo = __builtin_amdgcn_readlane(c_lo, l);
+        wq_hi = __builtin_amdgcn_readlane(c_hi, l);
+        if (store_ds) wds = __builtin_amdgcn_readlane(c_ds, l);
         wrel = block_relation(p.layout, p.causal, wi, j, Bb);
-        const int32_t a_first = first_row_seeing32(wrel, kv0, Bb);
-        if (a_first >= Bb) continue;
-        const int32_t q_first = a_first / kQm;
-        int32_t q_full = (first_row_seeing32(wrel, klast, Bb) + kQm - 1) / kQm;
-        q_full = q_full < qtiles ? q_full : qtiles;
-        wq_lo = wpass == 0 ? q_first : (q_full > q_first ? q_full : q_first);
-        wq_hi = wpass == 0 ? q_full : qtiles;
-        if (wq_lo >= wq_hi) continue;
         wqt = wq_lo;
         wgi = 0;
         wfrs = first_row_seeing32(wrel, key, Bb);
-        if (store_ds) {
-          const int32_t run = ((wi - p.rank_begin) * p.B + b) * p.H * p.P + hk * p.G * p.P + j;
-          wds = run * (int32_t)p.ds_stride + ds_key_tile_start_wave(wrel, tile, Bb, lane) - q_first;
-        }
         return true;
       }
-      if (wpass == 1) return false;
-      wpass = 1;
-      wk = -1;
+      if (cbase + 64 >= 2 * p.P) return false;
+      fill(cbase + 64);
     }
   };
   // 0: no more tiles; 1: the next tile of the same head; 2: another head or rank

@@ -276,6 +276,12 @@ SMALL_BWD = [
     # per block; and two query heads per K/V head (turns of unequal heads)
     Case(169, 1, 3, 4140, 128, 3, True, "striped", "bf16"),
     Case(170, 1, 6, 2100, 64, 3, True, "striped", "bf16", Hk=3),
+    # rings of more than 32 ranks: the key-side walk holds its (pass, rank)
+    # pairs 64 at a time, so these walks cross into a second set of pairs
+    Case(171, 1, 2, 4000, 64, 40, True, "striped", "bf16"),
+    Case(172, 1, 2, 2520, 128, 36, True, "zigzag", "bf16", Hk=1),
+    Case(173, 1, 1, 2112, 128, 33, False, "contiguous", "bf16"),
+    Case(174, 1, 1, 2176, 64, 34, True, "contiguous", "bf16"),
 ]
 
 
